@@ -1,0 +1,26 @@
+"""fp64 CPU oracle of SnapKV prefill-time KV-cache compression.
+
+Test infrastructure: imported only by the test suite, the smoke check and the
+CPU-baseline leg of the benchmark. The GPU library never imports or calls it.
+
+Every function is pinned by the CPU test suite against closed forms, library
+special cases, invariants and brute force (see tests/test_oracle_*.py); no
+function here is "parity unpinned".
+"""
+
+from .snapkv_oracle import (  # noqa: F401
+    POOL_AVG,
+    POOL_MAX,
+    OracleError,
+    OracleResult,
+    assemble_indices,
+    bf16_bits_to_f64,
+    causal_window_probs,
+    compress,
+    pool_code,
+    pool_scores,
+    prompt_scores,
+    select_prefix,
+    validate,
+    window_vote,
+)
