@@ -1,0 +1,233 @@
+"""Throughput of SnapKV prefill-time KV-cache compression on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one snapkv_compress call (vote, pooling, selection and gather) on
+one layer of synthetic, seeded input already resident in HBM. Inputs and
+outputs rotate over enough buffer sets to exceed the 256 MB Infinity Cache,
+so every step streams its K from HBM. Prints one JSON line:
+value = prompt tokens compressed per second per layer, plus the roofline of
+the scoring kernels (HIP events on the library's stream, bytes per launch
+from the algorithmic model) and the fp64 CPU oracle timed on a bounded
+sample of the same workload on this host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+METRIC = "prompt tokens compressed/sec per layer; achieved HBM GB/s vs MI355X peak"
+CACHE_BYTES = 256 << 20       # Infinity Cache
+SCORE_SOURCES = ("snapkv_score.hip",)
+
+
+def algorithmic_bytes(w, seq_lens):
+    """Bytes one call must move at minimum: Q and K read once for every
+    compressed prompt, the kept K/V rows read and written, the index list."""
+    score = gather = 0
+    for L in seq_lens:
+        n = min(L, w.budget)
+        if L > w.budget:
+            score += w.h_q * w.window * w.head_dim * 2 + w.h_kv * L * w.head_dim * 2
+        gather += 4 * w.h_kv * n * w.head_dim * 2 + 4 * w.h_kv * n
+    return score, gather
+
+
+def score_flops(w, seq_lens):
+    """One pass of Q_win . K^T over every compressed prompt's keys."""
+    return sum(2 * w.h_q * w.window * w.head_dim * L for L in seq_lens if L > w.budget)
+
+
+def _source_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "long_context_kv_snapkv_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_key, bytes_per_launch_alg):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel_key)
+    if not rec or rec.get("source_hash") != _source_hash(SCORE_SOURCES):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, x, budget_s=15.0):
+    import numpy as np  # noqa: F401
+
+    import oracle
+    threads = os.cpu_count()
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max(blas) if blas else 1
+    except Exception:
+        pass
+    lens = x.seq_lens.tolist()
+    t0 = time.perf_counter()
+    calls = 0
+    while True:
+        oracle.compress(x.q_win, x.k, x.v, lens, w.window, w.kernel, w.pool, w.budget,
+                        keep_scores=False)
+        calls += 1
+        if time.perf_counter() - t0 > budget_s or calls >= 20:
+            break
+    dt = (time.perf_counter() - t0) / calls
+    return {"value": sum(lens) / dt, "unit": "tokens/s/layer", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{w.name} layer 0, all {w.h_kv} KV heads, {calls} full oracle "
+                      f"call(s) in {dt * calls:.1f} s ({dt:.2f} s per layer)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="llama3_8b_16k")
+    ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0: auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of known size (counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the compression path runs on a single "
+              "MI355X and this build launches no multi-GPU work (--gpus must be 1).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import long_context_kv_snapkv_amd as skv
+    from synth import WORKLOADS, make_layer
+
+    w = WORKLOADS[args.workload]
+    x = make_layer(w, 0)
+    lens = x.seq_lens.tolist()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    skv.load_library()
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+            torch.bfloat16).to(dev)
+
+    q0, k0, v0 = up(x.q_win), up(x.k), up(x.v)
+    kv_bytes = 2 * k0.numel() * 2
+    nsets = args.sets or max(2, min(64, -(-4 * CACHE_BYTES // kv_bytes)))
+    batch, hkv, d, B = len(lens), w.h_kv, w.head_dim, w.budget
+    sets = []
+    for i in range(nsets):
+        sets.append(dict(q=q0.clone(), k=k0.clone(), v=v0.clone(),
+                         ok=torch.empty((batch, hkv, B, d), dtype=torch.bfloat16, device=dev),
+                         ov=torch.empty((batch, hkv, B, d), dtype=torch.bfloat16, device=dev),
+                         oi=torch.empty((batch, hkv, B), dtype=torch.int32, device=dev)))
+    del q0, k0, v0
+    ws = torch.empty(skv.snapkv_workspace_size(w.h_q, hkv, d, lens, w.window),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, events=None):
+        s = sets[i % nsets]
+        skv.snapkv_compress(s["q"], s["k"], s["v"], lens, w.window, w.kernel, w.pool, B,
+                            out_k=s["ok"], out_v=s["ov"], out_idx=s["oi"], workspace=ws,
+                            stream=stream, stage_events=events)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+
+    # per-kernel durations: the same steps again, with HIP events recorded by
+    # the library around each of its kernels on the call's stream
+    nst = skv.SNAPKV_NUM_STAGES
+    prof_steps = min(args.steps, 200)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nst)]
+           for _ in range(prof_steps)]
+    for row in evs:  # materialise the HIP events before handing them over
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for i in range(prof_steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    stage_ms = {}
+    for s in range(nst):
+        vals = [row[2 * s].elapsed_time(row[2 * s + 1]) for row in evs]
+        stage_ms[skv.snapkv_stage_name(s)] = float(np.mean(vals))
+
+    score_b, gather_b = algorithmic_bytes(w, lens)
+    total_b = score_b + gather_b
+    t_score_ms = stage_ms["snapkv_score_stats"] + stage_ms["snapkv_score_vote"]
+    achieved = score_b / (t_score_ms * 1e-3) / 1e9
+    flops = score_flops(w, lens)
+    tokens = sum(lens)
+    value = tokens / (ms_step * 1e-3)
+    roofline = {
+        "kernel": "snapkv_score (snapkv_score_stats + snapkv_score_vote)",
+        "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "traffic": _traffic("snapkv_score", score_b),
+        "bytes_per_launch": score_b, "launch_ms": round(t_score_ms, 5),
+    }
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s/layer",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": batch, "seq_len": lens if batch > 1 else lens[0],
+                   "num_q_heads": w.h_q, "num_kv_heads": hkv, "head_dim": d,
+                   "window": w.window, "kernel_size": w.kernel, "pooling": w.pool + "pool",
+                   "budget": B, "rotating_sets": nsets},
+        "hbm_gbps_whole_call": round(total_b / (ms_step * 1e-3) / 1e9, 1),
+        "hbm_frac_whole_call": round(total_b / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_call": total_b,
+        "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "mfma_util_score": {"algorithmic_1pass": round(flops / (t_score_ms * 1e-3) / 1e12 /
+                                                       BF16_PEAK_TFLOPS, 4),
+                            "issued_2pass": round(2 * flops / (t_score_ms * 1e-3) / 1e12 /
+                                                  BF16_PEAK_TFLOPS, 4)},
+        "roofline": roofline,
+    }
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = src.numel()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, x)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,175 @@
+/*
+ * snapkv.h - C ABI of the SnapKV prefill-time KV-cache compression library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (per prompt b of length L, per KV head h; P = L - W):
+ *
+ *   1. vote    s_h[j] = sum over the G = H_q/H_kv query heads of h's group and
+ *              over the W observation-window rows i of the causal attention
+ *              probability softmax_j'(q_i . k_j' / sqrt(D)), j' <= P + i,
+ *              taken at key j < P;
+ *   2. pool    c_h = s_h smoothed with a stride-1 window of kernel_size
+ *              positions (average: window sum / kernel_size, positions
+ *              outside [0, P) count as zero; max: in-range maximum);
+ *   3. select  the top B - W positions of c_h (ties to the lower position),
+ *              in ascending order, followed by the window positions P..L-1;
+ *   4. gather  those rows of K and V into a B-entry compressed cache.
+ *   A prompt with L <= B is kept whole (indices 0..L-1).
+ *
+ * Sources: glossary page "SnapKV(スナップケーブイ)", section "SnapKVの仕組み"
+ * (observation window of the last 16-64 prompt tokens; per-head attention
+ * scores aggregated; only a budget of B pairs kept; decode on the compressed
+ * cache; pooling of neighbouring scores before selection), section
+ * "実装と統合" (the four hyperparameters window_size, max_capacity_prompt,
+ * kernel_size, pooling), FAQ Q1 (MHA and GQA models); paper page "SnapKV: LLM
+ * Knows What You are Looking for Before Generation", abstract (selection of
+ * clustered important KV positions for each attention head, from an
+ * observation window at the end of the prompt) and section "기술적 접근법"
+ * (max or average pooling, kernel 5-13, window 16-64, budget 1024-4096).
+ * Where the pages are silent (softmax scale 1/sqrt(D); the causal row
+ * includes the window's own keys; aggregation is a sum; the budget B counts
+ * the W window rows; zero padding with division by kernel_size; lowest-index
+ * ties) the plainest reading is taken.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - bf16 tensors are passed as raw device pointers to bfloat16 bit patterns.
+ *   Layouts (row-major, innermost last):
+ *     q_win  [batch, H_q, W, D]  queries of positions L-W..L-1 of each prompt
+ *     k, v   [T, H_kv, D]        prompts packed back to back, T = sum(L_b)
+ *     out_k, out_v [batch, H_kv, B, D]
+ *     out_idx      [batch, H_kv, B] int32, positions relative to the prompt
+ *   Query head q belongs to KV head q / G (contiguous groups).
+ * - seq_lens is a HOST pointer to int32[batch]; it is read during the call only.
+ * - Device pointers must be 16-byte aligned.
+ * - The caller owns every buffer. The library allocates no memory and keeps no
+ *   pointer after a call returns. Inputs are read-only.
+ * - stream is a hipStream_t (NULL = the default stream). All device work is
+ *   enqueued on it and the call returns without synchronising; outputs are
+ *   valid once the stream has reached that point. Calls are re-entrant when
+ *   they use distinct workspaces; two calls in flight must not share one.
+ * - Errors are reported by status code only. Argument checks run entirely on
+ *   the host before any HIP call: on SNAPKV_ERR_INVALID_ARGUMENT,
+ *   SNAPKV_ERR_UNSUPPORTED or SNAPKV_ERR_WORKSPACE nothing is enqueued and no
+ *   output is touched. SNAPKV_ERR_HIP reports a failed launch; outputs are
+ *   then undefined. snapkv_last_error() gives the detail (per thread).
+ */
+#ifndef SNAPKV_H_
+#define SNAPKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SNAPKV_OK 0
+#define SNAPKV_ERR_INVALID_ARGUMENT 1
+#define SNAPKV_ERR_UNSUPPORTED 2
+#define SNAPKV_ERR_WORKSPACE 3
+#define SNAPKV_ERR_HIP 4
+
+#define SNAPKV_POOL_AVG 0 /* "avgpool" */
+#define SNAPKV_POOL_MAX 1 /* "maxpool" */
+
+#define SNAPKV_MAX_BATCH 256       /* prompts per call */
+#define SNAPKV_MAX_ROWS 512        /* G * W, window rows scored per KV head */
+#define SNAPKV_MAX_KERNEL 2049     /* largest pooling kernel */
+#define SNAPKV_NUM_STAGES 5        /* kernels of one snapkv_compress call */
+
+/*
+ * Bytes of device workspace that snapkv_compress and snapkv_window_scores
+ * need for this shape (the same size serves both). The workspace holds the
+ * per-chunk softmax statistics and the raw and pooled score vectors; it needs
+ * no initialisation. Returns SNAPKV_OK and writes *bytes, or an error status
+ * under the validation rules of snapkv_compress.
+ */
+int32_t snapkv_workspace_size(int32_t batch, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim,
+                              const int32_t* seq_lens, int32_t window,
+                              size_t* bytes);
+
+/*
+ * Compress one layer's prompt KV cache (steps 1-4 above).
+ *
+ *   window       W >= 1, the observation window (pages: 16-64)
+ *   kernel_size  odd, 1 <= kernel_size <= SNAPKV_MAX_KERNEL; 1 = no pooling
+ *                (pages: 5-13)
+ *   pool_mode    SNAPKV_POOL_AVG or SNAPKV_POOL_MAX
+ *   budget       B > W, entries kept per head including the W window rows
+ *                (pages: 1024-4096, and 256)
+ *
+ * Every output element is written: for prompt b and head h the first
+ * n = min(L_b, B) entries hold the kept rows and their ascending indices,
+ * the rest are zero rows with index -1. Gathered rows are bit copies of K/V.
+ *
+ * Errors: SNAPKV_ERR_INVALID_ARGUMENT for a null pointer, a misaligned
+ * device pointer, batch outside [1, SNAPKV_MAX_BATCH], heads < 1 or
+ * num_q_heads % num_kv_heads != 0, window < 1, budget <= window, an even or
+ * non-positive kernel_size, an unknown pool_mode, a seq_len < 1, or more than
+ * 2^31-1 packed tokens; SNAPKV_ERR_UNSUPPORTED for head_dim not in {64, 128},
+ * G * W > SNAPKV_MAX_ROWS or kernel_size > SNAPKV_MAX_KERNEL;
+ * SNAPKV_ERR_WORKSPACE when workspace_bytes is below snapkv_workspace_size;
+ * SNAPKV_ERR_HIP when a kernel launch fails.
+ */
+int32_t snapkv_compress(int32_t batch, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim,
+                        const void* q_win, const void* k, const void* v,
+                        const int32_t* seq_lens, int32_t window,
+                        int32_t kernel_size, int32_t pool_mode, int32_t budget,
+                        void* out_k, void* out_v, int32_t* out_idx,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Same as snapkv_compress, and in addition records hipEvent_t
+ * stage_events[2*s] before and stage_events[2*s+1] after stage s
+ * (s < SNAPKV_NUM_STAGES, named by snapkv_stage_name) on the same stream,
+ * so a caller can time each kernel. stage_events may be NULL (then this is
+ * snapkv_compress). Events are caller-owned and must exist.
+ */
+int32_t snapkv_compress_profiled(int32_t batch, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim,
+                                 const void* q_win, const void* k,
+                                 const void* v, const int32_t* seq_lens,
+                                 int32_t window, int32_t kernel_size,
+                                 int32_t pool_mode, int32_t budget,
+                                 void* out_k, void* out_v, int32_t* out_idx,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* stream, void* const* stage_events);
+
+/*
+ * The pooled scores c_h (steps 1-2) of every prompt with P = L - W >= 1,
+ * whatever its length relative to a budget; raw scores when kernel_size = 1.
+ *
+ *   out_scores  device float32 [batch, H_kv, scores_len]; entry j < P_b of
+ *               prompt b holds c_h[j], every other entry is written as 0.
+ *   scores_len  >= max_b(L_b - W) and >= 1.
+ *
+ * The values are bit-identical to the ones snapkv_compress selects from on
+ * the same inputs. Errors as for snapkv_compress; SNAPKV_ERR_INVALID_ARGUMENT
+ * also for a scores_len that is too small.
+ */
+int32_t snapkv_window_scores(int32_t batch, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim,
+                             const void* q_win, const void* k,
+                             const int32_t* seq_lens, int32_t window,
+                             int32_t kernel_size, int32_t pool_mode,
+                             float* out_scores, int32_t scores_len,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Static text of a status code ("ok", "invalid argument", ...). */
+const char* snapkv_status_string(int32_t status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* snapkv_last_error(void);
+
+/* Name of stage s of snapkv_compress, or NULL when s is out of range. */
+const char* snapkv_stage_name(int32_t stage);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SNAPKV_H_ */

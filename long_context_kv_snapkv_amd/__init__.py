@@ -1,0 +1,30 @@
+"""SnapKV prefill-time KV-cache compression for AMD Instinct MI355X (gfx950).
+
+The computation lives in libsnapkv.so (C ABI in include/snapkv.h, kernels in
+csrc/); this package is its Python binding. Build the library with
+``python -m long_context_kv_snapkv_amd.build``.
+"""
+
+from .snapkv import (  # noqa: F401
+    LIB_PATH,
+    SNAPKV_ERR_HIP,
+    SNAPKV_ERR_INVALID_ARGUMENT,
+    SNAPKV_ERR_UNSUPPORTED,
+    SNAPKV_ERR_WORKSPACE,
+    SNAPKV_NUM_STAGES,
+    SNAPKV_OK,
+    SNAPKV_POOL_AVG,
+    SNAPKV_POOL_MAX,
+    SnapKVError,
+    SnapKVLibraryMissing,
+    compress,
+    header_functions,
+    load_library,
+    pool_mode_code,
+    snapkv_compress,
+    snapkv_last_error,
+    snapkv_stage_name,
+    snapkv_status_string,
+    snapkv_window_scores,
+    snapkv_workspace_size,
+)

@@ -1,0 +1,248 @@
+"""ctypes binding of libsnapkv: the C-ABI entry points under the same names.
+
+Argument marshalling only: shapes are read from the tensors, raw device
+pointers and the current HIP stream are handed to the library, and outputs /
+workspace are allocated with torch when the caller does not pass them. Every
+step of the computation runs in the library's gfx950 kernels. If the library
+has not been built the first call raises SnapKVLibraryMissing; there is no
+fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Iterable, Optional, Sequence, Tuple
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "_lib", "libsnapkv.so")
+HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "snapkv.h")
+
+SNAPKV_OK = 0
+SNAPKV_ERR_INVALID_ARGUMENT = 1
+SNAPKV_ERR_UNSUPPORTED = 2
+SNAPKV_ERR_WORKSPACE = 3
+SNAPKV_ERR_HIP = 4
+SNAPKV_POOL_AVG = 0
+SNAPKV_POOL_MAX = 1
+SNAPKV_NUM_STAGES = 5
+
+_POOL_NAMES = {"avg": SNAPKV_POOL_AVG, "avgpool": SNAPKV_POOL_AVG,
+               "max": SNAPKV_POOL_MAX, "maxpool": SNAPKV_POOL_MAX}
+
+_lib = None
+
+_i32 = ctypes.c_int32
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+_pi32 = ctypes.POINTER(ctypes.c_int32)
+
+
+class SnapKVLibraryMissing(ImportError):
+    """libsnapkv.so has not been built."""
+
+
+class SnapKVError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        lib = load_library()
+        name = lib.snapkv_status_string(status).decode()
+        super().__init__(f"snapkv: {name} ({status}): {detail}")
+
+
+def load_library():
+    """Load libsnapkv.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise SnapKVLibraryMissing(
+            f"{LIB_PATH} is missing; build it with "
+            "`python -m long_context_kv_snapkv_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.snapkv_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _pi32, _i32,
+                                          ctypes.POINTER(_sz)]
+    lib.snapkv_workspace_size.restype = _i32
+    compress_args = [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _pi32, _i32, _i32, _i32,
+                     _i32, _vp, _vp, _vp, _vp, _sz, _vp]
+    lib.snapkv_compress.argtypes = compress_args
+    lib.snapkv_compress.restype = _i32
+    lib.snapkv_compress_profiled.argtypes = compress_args + [ctypes.POINTER(_vp)]
+    lib.snapkv_compress_profiled.restype = _i32
+    lib.snapkv_window_scores.argtypes = [_i32, _i32, _i32, _i32, _vp, _vp, _pi32, _i32,
+                                         _i32, _i32, _vp, _i32, _vp, _sz, _vp]
+    lib.snapkv_window_scores.restype = _i32
+    lib.snapkv_status_string.argtypes = [_i32]
+    lib.snapkv_status_string.restype = ctypes.c_char_p
+    lib.snapkv_last_error.argtypes = []
+    lib.snapkv_last_error.restype = ctypes.c_char_p
+    lib.snapkv_stage_name.argtypes = [_i32]
+    lib.snapkv_stage_name.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def header_functions() -> list:
+    """Names of the functions include/snapkv.h declares."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int32_t)\s*(snapkv_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def pool_mode_code(pooling) -> int:
+    if isinstance(pooling, str):
+        if pooling not in _POOL_NAMES:
+            raise ValueError(f"unknown pooling {pooling!r}")
+        return _POOL_NAMES[pooling]
+    return int(pooling)
+
+
+def _check(status: int) -> None:
+    if status != SNAPKV_OK:
+        raise SnapKVError(status, load_library().snapkv_last_error().decode())
+
+
+def _lens(seq_lens) -> Tuple[ctypes.Array, list]:
+    if isinstance(seq_lens, torch.Tensor):
+        seq_lens = seq_lens.detach().cpu().tolist()
+    vals = [int(x) for x in seq_lens]
+    return (ctypes.c_int32 * max(1, len(vals)))(*vals), vals
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream, device) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check_tensor(name: str, t: torch.Tensor, ndim: int, dtype=torch.bfloat16) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype or t.dim() != ndim or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name} must be a contiguous {ndim}-d {dtype} CUDA/HIP tensor, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def snapkv_workspace_size(num_q_heads: int, num_kv_heads: int, head_dim: int,
+                          seq_lens: Iterable[int], window: int) -> int:
+    lib = load_library()
+    arr, vals = _lens(seq_lens)
+    out = _sz(0)
+    _check(lib.snapkv_workspace_size(len(vals), num_q_heads, num_kv_heads, head_dim, arr,
+                                     window, ctypes.byref(out)))
+    return out.value
+
+
+def _shapes(q_win, k, seq_vals):
+    batch, hq, w, d = q_win.shape
+    total, hkv, dk = k.shape
+    if dk != d:
+        raise ValueError("q_win and k disagree on head_dim")
+    if batch != len(seq_vals) or total != sum(seq_vals):
+        raise ValueError("q_win batch / k rows must match seq_lens")
+    return batch, hq, hkv, d, w
+
+
+def snapkv_compress(q_win: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    seq_lens: Sequence[int], window: int, kernel_size: int, pool_mode,
+                    budget: int, *, out_k: Optional[torch.Tensor] = None,
+                    out_v: Optional[torch.Tensor] = None,
+                    out_idx: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, stream=None,
+                    stage_events: Optional[Sequence] = None):
+    """Compress one layer. Returns (out_k, out_v, out_idx); see include/snapkv.h."""
+    lib = load_library()
+    _check_tensor("q_win", q_win, 4)
+    _check_tensor("k", k, 3)
+    _check_tensor("v", v, 3)
+    arr, vals = _lens(seq_lens)
+    batch, hq, hkv, d, w = _shapes(q_win, k, vals)
+    if v.shape != k.shape:
+        raise ValueError("k and v shapes differ")
+    if w != window:
+        raise ValueError(f"q_win holds {w} window rows but window={window}")
+    dev = q_win.device
+    if out_k is None:
+        out_k = torch.empty((batch, hkv, budget, d), dtype=torch.bfloat16, device=dev)
+    if out_v is None:
+        out_v = torch.empty((batch, hkv, budget, d), dtype=torch.bfloat16, device=dev)
+    if out_idx is None:
+        out_idx = torch.empty((batch, hkv, budget), dtype=torch.int32, device=dev)
+    _check_tensor("out_k", out_k, 4)
+    _check_tensor("out_v", out_v, 4)
+    _check_tensor("out_idx", out_idx, 3, torch.int32)
+    if tuple(out_k.shape) != (batch, hkv, budget, d) or out_v.shape != out_k.shape \
+            or tuple(out_idx.shape) != (batch, hkv, budget):
+        raise ValueError("output shapes must be [batch, H_kv, budget, D] and [batch, H_kv, budget]")
+    if workspace is None:
+        workspace = torch.empty(snapkv_workspace_size(hq, hkv, d, vals, window),
+                                dtype=torch.uint8, device=dev)
+    args = (batch, hq, hkv, d, _ptr(q_win), _ptr(k), _ptr(v), arr, window, kernel_size,
+            pool_mode_code(pool_mode), budget, _ptr(out_k), _ptr(out_v), _ptr(out_idx),
+            _ptr(workspace), workspace.numel(), _stream(stream, dev))
+    if stage_events is None:
+        _check(lib.snapkv_compress(*args))
+    else:
+        evs = (_vp * len(stage_events))(*[int(e.cuda_event) for e in stage_events])
+        _check(lib.snapkv_compress_profiled(*args, evs))
+    return out_k, out_v, out_idx
+
+
+def snapkv_window_scores(q_win: torch.Tensor, k: torch.Tensor, seq_lens: Sequence[int],
+                         window: int, kernel_size: int, pool_mode, *,
+                         out_scores: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None):
+    """Pooled vote scores [batch, H_kv, scores_len] (float32); see include/snapkv.h."""
+    lib = load_library()
+    _check_tensor("q_win", q_win, 4)
+    _check_tensor("k", k, 3)
+    arr, vals = _lens(seq_lens)
+    batch, hq, hkv, d, w = _shapes(q_win, k, vals)
+    if w != window:
+        raise ValueError(f"q_win holds {w} window rows but window={window}")
+    dev = q_win.device
+    if out_scores is None:
+        p_max = max(1, max(vals) - window)
+        out_scores = torch.empty((batch, hkv, p_max), dtype=torch.float32, device=dev)
+    _check_tensor("out_scores", out_scores, 3, torch.float32)
+    if tuple(out_scores.shape[:2]) != (batch, hkv):
+        raise ValueError("out_scores must be [batch, H_kv, scores_len]")
+    if workspace is None:
+        workspace = torch.empty(snapkv_workspace_size(hq, hkv, d, vals, window),
+                                dtype=torch.uint8, device=dev)
+    _check(lib.snapkv_window_scores(batch, hq, hkv, d, _ptr(q_win), _ptr(k), arr, window,
+                                    kernel_size, pool_mode_code(pool_mode),
+                                    _ptr(out_scores), out_scores.shape[2], _ptr(workspace),
+                                    workspace.numel(), _stream(stream, dev)))
+    return out_scores
+
+
+def snapkv_status_string(status: int) -> str:
+    return load_library().snapkv_status_string(status).decode()
+
+
+def snapkv_last_error() -> str:
+    return load_library().snapkv_last_error().decode()
+
+
+def snapkv_stage_name(stage: int) -> Optional[str]:
+    name = load_library().snapkv_stage_name(stage)
+    return None if name is None else name.decode()
+
+
+def compress(q_win, k, v, seq_lens, window_size: int = 32, max_capacity_prompt: int = 4096,
+             kernel_size: int = 5, pooling: str = "avgpool", **kw):
+    """snapkv_compress under the hyperparameter names of the SnapKV cache object
+    (window_size, max_capacity_prompt, kernel_size, pooling)."""
+    return snapkv_compress(q_win, k, v, seq_lens, window_size, kernel_size, pooling,
+                           max_capacity_prompt, **kw)

@@ -1,0 +1,143 @@
+"""Shared helpers of the GPU parity tests: run the library through its C ABI
+and compare with the oracle under the acceptance rules.
+
+Acceptance (all per prompt b and KV head h):
+  scores   |g_j - o_j| <= 1e-3 * |o_j| + 1e-6 * max_j o_j        (pooled scores)
+  indices  with o sorted descending, tau = o_(m), tau' = o_(m+1),
+           tol = 1e-3 * tau + 1e-6 * max o: every j with o_j > tau' + tol is
+           kept and every j with o_j < tau - tol is not; when tau - tau' > tol
+           this makes the kept set identical to the oracle's;
+  topk     the oracle's selection rule applied to the GPU's own fp32 scores
+           reproduces the GPU's index list exactly (same precision decides);
+  gather   out_k / out_v rows are bit copies of K / V at the GPU's indices,
+           padding rows are zero with index -1.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import long_context_kv_snapkv_amd as skv
+import oracle
+
+REL_TOL = 1e-3
+ABS_FRAC = 1e-6
+
+
+def bits_to_device(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).to(device)
+
+
+def bits_from_device(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def upload(x):
+    return bits_to_device(x.q_win), bits_to_device(x.k), bits_to_device(x.v)
+
+
+def run_gpu(x, window, kernel, pool, budget, dev_inputs=None):
+    q, k, v = dev_inputs if dev_inputs is not None else upload(x)
+    lens = x.seq_lens.tolist()
+    out_k, out_v, out_idx = skv.snapkv_compress(q, k, v, lens, window, kernel, pool, budget)
+    scores = skv.snapkv_window_scores(q, k, lens, window, kernel, pool)
+    torch.cuda.synchronize()
+    return dict(out_k=bits_from_device(out_k), out_v=bits_from_device(out_v),
+                out_idx=out_idx.cpu().numpy(), scores=scores.cpu().numpy().astype(np.float64))
+
+
+def check_scores(gpu_scores, ref_pooled, seq_lens, window):
+    worst = 0.0
+    for b, length in enumerate(seq_lens):
+        p = length - window
+        if p < 1:
+            assert (gpu_scores[b] == 0).all()
+            continue
+        o = ref_pooled[b]
+        g = gpu_scores[b, :, :p]
+        bound = REL_TOL * np.abs(o) + ABS_FRAC * o.max(axis=1, keepdims=True)
+        err = np.abs(g - o)
+        worst = max(worst, float((err / np.maximum(bound, 1e-300)).max()))
+        bad = err > bound
+        assert not bad.any(), (
+            f"prompt {b}: {bad.sum()} scores out of tolerance, e.g. head/pos "
+            f"{np.argwhere(bad)[:3].tolist()} gpu={g[bad][:3]} oracle={o[bad][:3]}")
+        assert (gpu_scores[b, :, p:] == 0).all()
+    return worst
+
+
+def check_index_sets(gpu_idx, ref_pooled, seq_lens, window, budget):
+    m = budget - window
+    exact_heads = 0
+    for b, length in enumerate(seq_lens):
+        if length <= budget:
+            continue
+        for h, o in enumerate(ref_pooled[b]):
+            kept = gpu_idx[b, h, :m]
+            srt = np.sort(o)[::-1]
+            tau, tau2 = srt[m - 1], srt[m]
+            tol = REL_TOL * tau + ABS_FRAC * srt[0]
+            must = np.flatnonzero(o > tau2 + tol)
+            never = np.flatnonzero(o < tau - tol)
+            ks = set(kept.tolist())
+            assert len(ks) == m
+            missing = [j for j in must.tolist() if j not in ks]
+            assert not missing, f"prompt {b} head {h}: clearly-top positions missing {missing[:5]}"
+            wrong = [j for j in never.tolist() if j in ks]
+            assert not wrong, f"prompt {b} head {h}: clearly-low positions kept {wrong[:5]}"
+            if tau - tau2 > tol:
+                np.testing.assert_array_equal(kept, oracle.select_prefix(o, m))
+                exact_heads += 1
+    return exact_heads
+
+
+def check_structure_and_gather(res, x, window, budget):
+    gpu_idx, out_k, out_v = res["out_idx"], res["out_k"], res["out_v"]
+    offs = x.offsets
+    for b, length in enumerate(x.seq_lens.tolist()):
+        n = min(length, budget)
+        for h in range(gpu_idx.shape[1]):
+            idx = gpu_idx[b, h]
+            assert (idx[n:] == -1).all()
+            valid = idx[:n]
+            assert (np.diff(valid) > 0).all() and valid.min() >= 0 and valid.max() < length
+            if length <= budget:
+                np.testing.assert_array_equal(valid, np.arange(length))
+            else:
+                np.testing.assert_array_equal(valid[-window:], np.arange(length - window, length))
+            np.testing.assert_array_equal(out_k[b, h, :n], x.k[offs[b] + valid, h])
+            np.testing.assert_array_equal(out_v[b, h, :n], x.v[offs[b] + valid, h])
+            assert (out_k[b, h, n:] == 0).all() and (out_v[b, h, n:] == 0).all()
+
+
+def check_topk_exact(res, seq_lens, window, budget):
+    m = budget - window
+    for b, length in enumerate(seq_lens):
+        if length <= budget:
+            continue
+        p = length - window
+        for h in range(res["out_idx"].shape[1]):
+            sel = oracle.select_prefix(res["scores"][b, h, :p], m)
+            np.testing.assert_array_equal(res["out_idx"][b, h, :m], sel)
+
+
+def full_check(x, window, kernel, pool, budget, ref=None, res=None):
+    """Run GPU and oracle on the same inputs and apply every acceptance rule."""
+    lens = x.seq_lens.tolist()
+    if res is None:
+        res = run_gpu(x, window, kernel, pool, budget)
+    if ref is None:
+        ref = oracle.compress(x.q_win, x.k, x.v, lens, window, kernel, pool, budget)
+    pooled = [p for p in ref.pooled]
+    worst = check_scores(res["scores"], pooled, lens, window)
+    check_structure_and_gather(res, x, window, budget)
+    check_topk_exact(res, lens, window, budget)
+    exact = check_index_sets(res["out_idx"], pooled, lens, window, budget)
+    # where the oracle's kept set is unambiguous, the rows equal the oracle's
+    for b, length in enumerate(lens):
+        if length <= budget:
+            np.testing.assert_array_equal(res["out_idx"][b], ref.out_idx[b])
+            np.testing.assert_array_equal(res["out_k"][b], ref.out_k[b])
+    return dict(worst_score_ratio=worst, exact_heads=exact, res=res, ref=ref)

@@ -1,0 +1,111 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function the header declares, and rejects bad arguments before any HIP
+call. Fake device addresses are never dereferenced: every call here fails
+validation first (and carries an undersized workspace as a second guard)."""
+
+import ctypes
+import os
+
+import pytest
+
+import long_context_kv_snapkv_amd as skv
+from long_context_kv_snapkv_amd import snapkv as binding
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from long_context_kv_snapkv_amd.build import build
+        build()
+    return skv.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = skv.header_functions()
+    assert len(names) == 7, names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    assert skv.snapkv_status_string(0) == "ok"
+    assert skv.snapkv_status_string(1) == "invalid argument"
+    assert skv.snapkv_status_string(2) == "unsupported"
+    assert skv.snapkv_status_string(3) == "workspace too small"
+    assert skv.snapkv_status_string(4) == "HIP error"
+    assert skv.snapkv_status_string(99) == "unknown status"
+
+
+def test_stage_names(lib):
+    names = [skv.snapkv_stage_name(i) for i in range(skv.SNAPKV_NUM_STAGES)]
+    assert names == ["snapkv_score_stats", "snapkv_score_vote", "snapkv_pool",
+                     "snapkv_topk", "snapkv_gather"]
+    assert skv.snapkv_stage_name(-1) is None and skv.snapkv_stage_name(5) is None
+
+
+FAKE = 0x10000  # 16-byte aligned address that is never dereferenced
+
+
+def _compress(lib, **over):
+    a = dict(batch=1, hq=4, hkv=2, d=128, q=FAKE, k=FAKE, v=FAKE, lens=[100], window=8,
+             kernel=5, pool=0, budget=32, ok=FAKE, ov=FAKE, oi=FAKE, ws=FAKE, ws_bytes=1,
+             stream=None)
+    a.update(over)
+    lens = (ctypes.c_int32 * max(1, len(a["lens"])))(*a["lens"])
+    st = lib.snapkv_compress(a["batch"], a["hq"], a["hkv"], a["d"], a["q"], a["k"], a["v"],
+                             lens, a["window"], a["kernel"], a["pool"], a["budget"], a["ok"],
+                             a["ov"], a["oi"], a["ws"], a["ws_bytes"], a["stream"])
+    return st, skv.snapkv_last_error()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(oi=None), 1),
+    (dict(q=FAKE + 2), 1), (dict(ok=FAKE + 8), 1),
+    (dict(batch=0, lens=[]), 1), (dict(batch=257, lens=[10] * 257), 1),
+    (dict(hq=5), 1), (dict(hkv=0), 1), (dict(window=0), 1),
+    (dict(budget=8), 1), (dict(budget=3), 1),
+    (dict(kernel=4), 1), (dict(kernel=0), 1), (dict(kernel=-3), 1), (dict(pool=2), 1),
+    (dict(lens=[0]), 1), (dict(batch=2, lens=[5, -1]), 1),
+    (dict(d=96), 2), (dict(d=256), 2), (dict(hq=32, hkv=2, window=64), 2),
+    (dict(kernel=2051), 2),
+    (dict(ws_bytes=1), 3), (dict(ws=None, ws_bytes=10**9), 3), (dict(ws=FAKE + 4, ws_bytes=10**9), 3),
+])
+def test_compress_validation(lib, over, status):
+    st, msg = _compress(lib, **over)
+    assert st == status, msg
+    assert msg
+
+
+def test_window_scores_validation(lib):
+    lens = (ctypes.c_int32 * 1)(100)
+    st = lib.snapkv_window_scores(1, 4, 2, 128, FAKE, FAKE, lens, 8, 5, 0, FAKE, 91, FAKE,
+                                  1 << 30, None)
+    assert st == 1 and "scores_len" in skv.snapkv_last_error()
+    st = lib.snapkv_window_scores(1, 4, 2, 128, FAKE, FAKE, lens, 8, 6, 0, FAKE, 92, FAKE,
+                                  1, None)
+    assert st == 1
+
+
+def test_workspace_size_host_logic(lib):
+    small = skv.snapkv_workspace_size(32, 8, 128, [16384], 32)
+    big = skv.snapkv_workspace_size(32, 8, 128, [131072], 32)
+    assert 0 < small < big
+    # raw + pooled score vectors alone need 2 * 8 heads * P floats
+    assert small >= 2 * 8 * (16384 - 32) * 4
+    assert skv.snapkv_workspace_size(32, 8, 128, [16384, 100], 32) >= small
+    with pytest.raises(skv.SnapKVError) as e:
+        skv.snapkv_workspace_size(32, 8, 100, [16384], 32)
+    assert e.value.status == skv.SNAPKV_ERR_UNSUPPORTED
+
+
+def test_pooling_names_match_page_snippet():
+    import json
+    with open(os.path.join(os.path.dirname(__file__), "golden",
+                           "glossary_snippet_params.json")) as f:
+        p = json.load(f)
+    assert skv.pool_mode_code(p["pooling"]) == skv.SNAPKV_POOL_AVG
+    assert skv.pool_mode_code("maxpool") == skv.SNAPKV_POOL_MAX
+    import inspect
+    params = inspect.signature(skv.compress).parameters
+    for name in ("window_size", "max_capacity_prompt", "kernel_size", "pooling"):
+        assert name in params

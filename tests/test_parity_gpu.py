@@ -1,0 +1,163 @@
+"""GPU parity of snapkv_compress / snapkv_window_scores against the oracle.
+
+Named workloads at their full sizes (the large stacks on sampled layers), plus
+edge cases: prompts at, just over and under the budget, shorter than the
+window, a one-token prefix, no pooling, kernels wider than the prefix, MHA,
+head_dim 64, window rows that are not a multiple of 32, the 512-row maximum,
+ragged batches mixing kept-whole and compressed prompts, and prefixes longer
+than the LDS-resident selection path.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_kv_snapkv_amd as skv
+from synth import WORKLOADS, make_custom, make_layer
+
+from parity import bits_from_device, full_check, run_gpu, upload
+
+pytestmark = pytest.mark.gpu
+
+needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")
+
+
+def _named(name, layer=0):
+    w = WORKLOADS[name]
+    x = make_layer(w, layer)
+    print(f"[parity] {name} layer {layer} lens={x.seq_lens.tolist()}", flush=True)
+    return w, x
+
+
+@needs_gpu
+def test_tiny_mha_1k():
+    w, x = _named("tiny_mha_1k")
+    full_check(x, w.window, w.kernel, w.pool, w.budget)
+
+
+@needs_gpu
+def test_llama3_8b_16k():
+    w, x = _named("llama3_8b_16k")
+    full_check(x, w.window, w.kernel, w.pool, w.budget)
+
+
+@needs_gpu
+@pytest.mark.parametrize("layer", [0, 31])
+def test_llama3_8b_32k_layers(layer):
+    w, x = _named("llama3_8b_32k_x32", layer)
+    full_check(x, w.window, w.kernel, w.pool, w.budget)
+
+
+@needs_gpu
+def test_llama3_8b_ragged8():
+    w, x = _named("llama3_8b_ragged8")
+    assert (x.seq_lens < w.budget).sum() == 1
+    full_check(x, w.window, w.kernel, w.pool, w.budget)
+
+
+@needs_gpu
+def test_llama3_70b_128k_layer0():
+    w, x = _named("llama3_70b_128k_x80", 0)
+    full_check(x, w.window, w.kernel, w.pool, w.budget)
+
+
+EDGE = [
+    # lens, h_q, h_kv, d, window, kernel, pool, budget
+    ([256], 4, 2, 128, 16, 5, "avg", 256),        # L == B: kept whole
+    ([257], 4, 2, 128, 16, 5, "max", 256),        # L == B + 1
+    ([10], 4, 2, 128, 16, 5, "avg", 64),          # L < W
+    ([17], 4, 2, 128, 16, 3, "max", 16 + 1),      # P == 1 is kept whole (L <= B)
+    ([200], 4, 2, 128, 16, 1, "avg", 64),         # no pooling
+    ([150], 8, 8, 64, 32, 1, "max", 48),          # MHA, D = 64, raw scores
+    ([300], 4, 4, 64, 16, 13, "avg", 40),         # MHA, W = 16: 16 padded rows
+    ([500], 6, 2, 128, 20, 7, "avg", 100),        # R = 60 rows
+    ([700], 6, 2, 64, 24, 9, "max", 80),          # R = 72, D = 64
+    ([1200], 64, 8, 128, 64, 7, "max", 300),      # R = 512 (maximum)
+    ([97], 32, 8, 128, 32, 201, "avg", 60),       # kernel wider than the prefix
+    ([97], 32, 8, 128, 32, 2049, "max", 60),      # widest kernel
+    ([64, 300, 65, 5, 1000], 8, 2, 128, 32, 5, "avg", 96),  # ragged, mixed
+    ([1, 1, 2], 4, 4, 128, 16, 5, "max", 32),     # one-token prompts
+    ([40000], 8, 2, 128, 16, 7, "max", 2048),     # prefix > LDS-resident topk
+    ([3000, 2500], 16, 4, 128, 64, 5, "avg", 1024),
+]
+
+
+@needs_gpu
+@pytest.mark.parametrize("case", EDGE, ids=[f"edge{i}" for i in range(len(EDGE))])
+def test_edge_cases(case):
+    lens, hq, hkv, d, window, kernel, pool, budget = case
+    print(f"[parity] edge {case}", flush=True)
+    x = make_custom(lens, hq, hkv, d, window, seed=sum(lens) % 97)
+    full_check(x, window, kernel, pool, budget)
+
+
+@needs_gpu
+def test_no_planting_flat_scores():
+    # without planted structure scores are near-uniform: many near-ties, the
+    # band rule and the exact topk self-check carry the comparison
+    x = make_custom([5000], 32, 8, 128, 32, seed=3, planting="none")
+    full_check(x, 32, 5, "avg", 512)
+
+
+@needs_gpu
+def test_raw_scores_without_pooling_match_oracle_vote():
+    import oracle
+    x = make_custom([3000], 32, 8, 128, 32, seed=5)
+    q, k, _ = upload(x)
+    g = skv.snapkv_window_scores(q, k, [3000], 32, 1, "avg").cpu().numpy().astype(np.float64)
+    for h in range(8):
+        kh = oracle.bf16_bits_to_f64(x.k[:, h])
+        qg = oracle.bf16_bits_to_f64(x.q_win[0, 4 * h:4 * h + 4])
+        s = oracle.window_vote(qg, kh, 32)
+        np.testing.assert_allclose(g[0, h], s, rtol=1e-3, atol=1e-6 * s.max())
+
+
+@needs_gpu
+def test_deterministic_bitwise():
+    w = WORKLOADS["llama3_8b_16k"]
+    x = make_layer(w)
+    dev = upload(x)
+    a = run_gpu(x, w.window, w.kernel, w.pool, w.budget, dev)
+    b = run_gpu(x, w.window, w.kernel, w.pool, w.budget, dev)
+    for key in a:
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+@needs_gpu
+def test_guard_bands_untouched():
+    lens = [700, 40, 333]
+    hq, hkv, d, window, budget = 8, 2, 128, 32, 128
+    x = make_custom(lens, hq, hkv, d, window, seed=21)
+    q, k, v = upload(x)
+    batch = len(lens)
+    guard = 4096
+    nk = batch * hkv * budget * d
+    ni = batch * hkv * budget
+    kbuf = torch.full((nk + 2 * guard,), 7, dtype=torch.int16, device="cuda")
+    vbuf = torch.full((nk + 2 * guard,), 7, dtype=torch.int16, device="cuda")
+    ibuf = torch.full((ni + 2 * guard,), 12345, dtype=torch.int32, device="cuda")
+    ws_bytes = skv.snapkv_workspace_size(hq, hkv, d, lens, window)
+    wbuf = torch.full((ws_bytes + 2 * guard,), 0xA5, dtype=torch.uint8, device="cuda")
+    out_k = kbuf[guard:guard + nk].view(torch.bfloat16).view(batch, hkv, budget, d)
+    out_v = vbuf[guard:guard + nk].view(torch.bfloat16).view(batch, hkv, budget, d)
+    out_i = ibuf[guard:guard + ni].view(batch, hkv, budget)
+    ws = wbuf[guard:guard + ws_bytes]
+    skv.snapkv_compress(q, k, v, lens, window, 5, "avg", budget, out_k=out_k, out_v=out_v,
+                        out_idx=out_i, workspace=ws)
+    torch.cuda.synchronize()
+    for buf, val in ((kbuf, 7), (vbuf, 7), (ibuf, 12345), (wbuf, 0xA5)):
+        assert (buf[:guard] == val).all() and (buf[-guard:] == val).all()
+    res = dict(out_k=bits_from_device(out_k), out_v=bits_from_device(out_v),
+               out_idx=out_i.cpu().numpy())
+    from parity import check_structure_and_gather
+    check_structure_and_gather(res, x, window, budget)
+
+
+@needs_gpu
+def test_validation_error_surfaces_through_binding():
+    # an even pooling kernel is rejected on the host before anything is queued
+    x = make_custom([100], 4, 2, 128, 8, seed=1)
+    q, k, v = upload(x)
+    with pytest.raises(skv.SnapKVError) as e:
+        skv.snapkv_compress(q, k, v, [100], 8, 4, "avg", 32)
+    assert e.value.status == skv.SNAPKV_ERR_INVALID_ARGUMENT
