@@ -76,14 +76,16 @@ extern "C" {
 #define SNAPKV_MAX_BATCH 256       /* prompts per call */
 #define SNAPKV_MAX_ROWS 512        /* G * W, window rows scored per KV head */
 #define SNAPKV_MAX_KERNEL 2049     /* largest pooling kernel */
-#define SNAPKV_NUM_STAGES 5        /* kernels of one snapkv_compress call */
+#define SNAPKV_NUM_STAGES 4        /* kernels of snapkv_compress_staged */
 
 /*
- * Bytes of device workspace that snapkv_compress and snapkv_window_scores
- * need for this shape (the same size serves both). The workspace holds the
- * per-chunk softmax statistics and the raw and pooled score vectors; it needs
- * no initialisation. Returns SNAPKV_OK and writes *bytes, or an error status
- * under the validation rules of snapkv_compress.
+ * Bytes of device workspace that snapkv_compress, snapkv_compress_staged and
+ * snapkv_window_scores need for this shape (the same size serves all three).
+ * The workspace holds intermediate results only (per-chunk softmax
+ * statistics, raw and pooled score vectors, and a reserved counter area):
+ * it needs no initialisation and may be reused across calls and shapes.
+ * Returns SNAPKV_OK and writes *bytes, or an error status under the
+ * validation rules of snapkv_compress.
  */
 int32_t snapkv_workspace_size(int32_t batch, int32_t num_q_heads,
                               int32_t num_kv_heads, int32_t head_dim,
@@ -91,7 +93,8 @@ int32_t snapkv_workspace_size(int32_t batch, int32_t num_q_heads,
                               size_t* bytes);
 
 /*
- * Compress one layer's prompt KV cache (steps 1-4 above).
+ * Compress one layer's prompt KV cache (steps 1-4 above). The stages run as
+ * SNAPKV_NUM_STAGES consecutive kernels on `stream`.
  *
  *   window       W >= 1, the observation window (pages: 16-64)
  *   kernel_size  odd, 1 <= kernel_size <= SNAPKV_MAX_KERNEL; 1 = no pooling
@@ -99,10 +102,13 @@ int32_t snapkv_workspace_size(int32_t batch, int32_t num_q_heads,
  *   pool_mode    SNAPKV_POOL_AVG or SNAPKV_POOL_MAX
  *   budget       B > W, entries kept per head including the W window rows
  *                (pages: 1024-4096, and 256)
+ *   workspace    at least snapkv_workspace_size bytes of device memory
  *
  * Every output element is written: for prompt b and head h the first
  * n = min(L_b, B) entries hold the kept rows and their ascending indices,
  * the rest are zero rows with index -1. Gathered rows are bit copies of K/V.
+ * Results do not depend on how the work is scheduled: repeated calls give
+ * identical bits.
  *
  * Errors: SNAPKV_ERR_INVALID_ARGUMENT for a null pointer, a misaligned
  * device pointer, batch outside [1, SNAPKV_MAX_BATCH], heads < 1 or
@@ -122,21 +128,22 @@ int32_t snapkv_compress(int32_t batch, int32_t num_q_heads,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Same as snapkv_compress, and in addition records hipEvent_t
- * stage_events[2*s] before and stage_events[2*s+1] after stage s
- * (s < SNAPKV_NUM_STAGES, named by snapkv_stage_name) on the same stream,
- * so a caller can time each kernel. stage_events may be NULL (then this is
- * snapkv_compress). Events are caller-owned and must exist.
+ * snapkv_compress with optional per-stage timing: the same kernels (named by
+ * snapkv_stage_name: window statistics, window vote, pooling + selection,
+ * gather) and identical results. When stage_events is not NULL it points to
+ * 2 * SNAPKV_NUM_STAGES caller-owned hipEvent_t; stage_events[2*s] is
+ * recorded before and stage_events[2*s+1] after stage s on the same stream.
+ * Errors as for snapkv_compress.
  */
-int32_t snapkv_compress_profiled(int32_t batch, int32_t num_q_heads,
-                                 int32_t num_kv_heads, int32_t head_dim,
-                                 const void* q_win, const void* k,
-                                 const void* v, const int32_t* seq_lens,
-                                 int32_t window, int32_t kernel_size,
-                                 int32_t pool_mode, int32_t budget,
-                                 void* out_k, void* out_v, int32_t* out_idx,
-                                 void* workspace, size_t workspace_bytes,
-                                 void* stream, void* const* stage_events);
+int32_t snapkv_compress_staged(int32_t batch, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim,
+                               const void* q_win, const void* k,
+                               const void* v, const int32_t* seq_lens,
+                               int32_t window, int32_t kernel_size,
+                               int32_t pool_mode, int32_t budget,
+                               void* out_k, void* out_v, int32_t* out_idx,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream, void* const* stage_events);
 
 /*
  * The pooled scores c_h (steps 1-2) of every prompt with P = L - W >= 1,

@@ -20,6 +20,7 @@ from .snapkv import (  # noqa: F401
     compress,
     header_functions,
     load_library,
+    new_workspace,
     pool_mode_code,
     snapkv_compress,
     snapkv_last_error,

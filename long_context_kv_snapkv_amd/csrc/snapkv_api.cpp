@@ -1,6 +1,6 @@
 // Host side of the SnapKV compression library: argument validation, the
-// workspace plan, and the launch sequence on the caller's stream. Every check
-// runs before the first HIP call, so a rejected call enqueues nothing.
+// workspace plan, and the launches on the caller's stream. Every check runs
+// before the first HIP call, so a rejected call enqueues nothing.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -24,25 +24,27 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
-const char* const kStageNames[SNAPKV_NUM_STAGES] = {
-    "snapkv_score_stats", "snapkv_score_vote", "snapkv_pool", "snapkv_topk", "snapkv_gather"};
-
-// Everything a call needs, derived from shapes alone (so the workspace size
-// computed ahead of a call matches the call).
-struct Plan {
-  int batch, hq, hkv, d, window, group, rows, rows_pad, nrt;
-  int waves, nwr;
-  int chunk, nchunk;
-  int l_max, p_max, p_stride;
-  size_t off_part, off_raw, off_pooled, bytes;
-  snapkv::PromptTable tab;
-};
+const char* const kStageNames[SNAPKV_NUM_STAGES] = {"snapkv_score_stats", "snapkv_score_vote",
+                                                    "snapkv_topk", "snapkv_gather"};
 
 int largest_pow2_at_most(int x) {
   int p = 1;
   while (p * 2 <= x) p *= 2;
   return p;
 }
+
+// Everything a call needs, derived from shapes alone, so the workspace size
+// computed ahead of a call matches the call. Workspace layout:
+//   sync   uint32[4 + 3*batch*H_kv]          persistent-kernel counters
+//   part   float2[batch, H_kv, nchunk, rows_pad]
+//   raw    float [batch, H_kv, p_stride]
+//   pooled float [batch, H_kv, p_stride]      selection spill for long prefixes
+struct Plan {
+  int batch, hq, hkv, d, window, group, rows, rows_pad, nrt, nwr;
+  int chunk, nchunk, l_max, p_max, p_stride;
+  size_t off_sync, off_part, off_raw, off_pooled, bytes;
+  snapkv::PromptTable tab;
+};
 
 int32_t make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const int32_t* seq_lens,
                   int32_t window, Plan* pl) {
@@ -62,6 +64,8 @@ int32_t make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const int32
   if (group * window > SNAPKV_MAX_ROWS)
     return fail(SNAPKV_ERR_UNSUPPORTED, "num_q_heads / num_kv_heads * window must be <= " +
                                             std::to_string(SNAPKV_MAX_ROWS));
+  if ((int64_t)batch * hkv > (1 << 20))
+    return fail(SNAPKV_ERR_UNSUPPORTED, "batch * num_kv_heads must be <= 2^20");
   int64_t total = 0, key_sum = 0;
   int l_max = 0;
   for (int b = 0; b < batch; ++b) {
@@ -86,26 +90,28 @@ int32_t make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const int32
   pl->rows = (int)(group * window);
   pl->rows_pad = (pl->rows + 31) / 32 * 32;
   pl->nrt = pl->rows_pad / 32;
-  pl->waves = pl->nrt <= 8 ? 4 : 8;
-  pl->nwr = largest_pow2_at_most(pl->nrt < pl->waves ? pl->nrt : pl->waves);
-  // keys per scoring workgroup: about 512 workgroups over the whole call,
-  // 64-key granularity, at most 8192 keys
-  int64_t chunk = (key_sum * hkv + 511) / 512;
+  pl->nwr = largest_pow2_at_most(pl->nrt < 8 ? pl->nrt : 8);
+  // keys per scoring item: about 256 items over the whole call (one per CU
+  // and phase), 64-key granularity, 256 .. 4096 keys
+  int64_t chunk = (key_sum * hkv + 255) / 256;
   chunk = (chunk + snapkv::kKeyTile - 1) / snapkv::kKeyTile * snapkv::kKeyTile;
   if (chunk < 256) chunk = 256;
-  if (chunk > 8192) chunk = 8192;
+  if (chunk > snapkv::kMaxChunk) chunk = snapkv::kMaxChunk;
   pl->chunk = (int)chunk;
   pl->nchunk = (int)((l_max + chunk - 1) / chunk);
   pl->l_max = l_max;
   pl->p_max = l_max - window > 1 ? l_max - window : 1;
   pl->p_stride = (int)align_up((size_t)pl->p_max, 64);
+  const size_t heads = (size_t)batch * hkv;
   size_t off = 0;
+  pl->off_sync = off;
+  off = align_up(off + (snapkv::kSyncHeads + 3 * heads) * sizeof(uint32_t), 256);
   pl->off_part = off;
-  off = align_up(off + (size_t)batch * hkv * pl->nchunk * pl->rows_pad * sizeof(float2), 256);
+  off = align_up(off + heads * pl->nchunk * pl->rows_pad * sizeof(float2), 256);
   pl->off_raw = off;
-  off = align_up(off + (size_t)batch * hkv * pl->p_stride * sizeof(float), 256);
+  off = align_up(off + heads * pl->p_stride * sizeof(float), 256);
   pl->off_pooled = off;
-  off = align_up(off + (size_t)batch * hkv * pl->p_stride * sizeof(float), 256);
+  off = align_up(off + heads * pl->p_stride * sizeof(float), 256);
   pl->bytes = off;
   return SNAPKV_OK;
 }
@@ -122,65 +128,62 @@ int32_t check_pool(int32_t kernel, int32_t pool_mode) {
   return SNAPKV_OK;
 }
 
-snapkv::ScoreParams score_params(const Plan& pl, const void* q, const void* k, void* ws,
-                                 int32_t budget, bool skip_fitting) {
-  snapkv::ScoreParams sp;
-  sp.q = static_cast<const uint16_t*>(q);
-  sp.k = static_cast<const uint16_t*>(k);
-  sp.part = reinterpret_cast<float2*>(static_cast<char*>(ws) + pl.off_part);
-  sp.raw = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.off_raw);
-  sp.hq = pl.hq;
-  sp.hkv = pl.hkv;
-  sp.window = pl.window;
-  sp.group = pl.group;
-  sp.rows = pl.rows;
-  sp.rows_pad = pl.rows_pad;
-  sp.nwr = pl.nwr;
-  sp.chunk = pl.chunk;
-  sp.nchunk = pl.nchunk;
-  sp.p_stride = pl.p_stride;
-  sp.budget = budget;
-  sp.skip_fitting = skip_fitting ? 1 : 0;
-  sp.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)pl.d));
-  sp.tab = pl.tab;
-  return sp;
+snapkv::PathParams path_params(const Plan& pl, const void* q, const void* k, const void* v,
+                               void* ws, int32_t budget, int32_t kernel, int32_t pool_mode,
+                               bool score_all) {
+  snapkv::PathParams p;
+  std::memset(&p, 0, sizeof(p));
+  char* w = static_cast<char*>(ws);
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.sync = reinterpret_cast<uint32_t*>(w + pl.off_sync);
+  p.part = reinterpret_cast<float2*>(w + pl.off_part);
+  p.raw = reinterpret_cast<float*>(w + pl.off_raw);
+  p.pooled = reinterpret_cast<float*>(w + pl.off_pooled);
+  p.pooled_stride = pl.p_stride;
+  p.batch = pl.batch;
+  p.hq = pl.hq;
+  p.hkv = pl.hkv;
+  p.window = pl.window;
+  p.group = pl.group;
+  p.rows = pl.rows;
+  p.rows_pad = pl.rows_pad;
+  p.nwr = pl.nwr;
+  p.chunk = pl.chunk;
+  p.nchunk = pl.nchunk;
+  p.p_stride = pl.p_stride;
+  p.budget = budget;
+  p.kernel = kernel;
+  p.pool_mode = pool_mode;
+  p.score_all = score_all ? 1 : 0;
+  p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)pl.d));
+  p.tab = pl.tab;
+  int items = 0;
+  for (int b = 0; b < pl.batch; ++b) {
+    p.item_start[b] = items;
+    const int L = pl.tab.len[b];
+    const bool scored = L - pl.window >= 1 && (score_all || L > budget);
+    if (scored) items += pl.hkv * ((L + pl.chunk - 1) / pl.chunk);
+  }
+  p.item_start[pl.batch] = items;
+  p.n_score_items = items;
+  p.n_gather_blocks = budget > 0 ? (budget + snapkv::kGatherRows - 1) / snapkv::kGatherRows : 0;
+  p.n_tickets = 2 * items + pl.batch * pl.hkv * (1 + p.n_gather_blocks);
+  return p;
 }
 
 int32_t hip_fail(hipError_t e, const char* what) {
   return fail(SNAPKV_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-// Stages 1-2 (scoring and pooling) into `pooled` with row stride out_stride.
-int32_t run_scores(const Plan& pl, const snapkv::ScoreParams& sp, int32_t kernel,
-                   int32_t pool_mode, float* pooled, int out_stride, hipStream_t stream,
-                   hipEvent_t const* ev) {
-  const dim3 sgrid(pl.nchunk, pl.hkv, pl.batch);
-  if (ev) (void)hipEventRecord(ev[0], stream);
-  hipError_t e = snapkv::launch_score_stats(sp, pl.d, pl.waves, sgrid, stream);
-  if (e != hipSuccess) return hip_fail(e, "snapkv_score_stats launch");
-  if (ev) (void)hipEventRecord(ev[1], stream);
-  if (ev) (void)hipEventRecord(ev[2], stream);
-  e = snapkv::launch_score_vote(sp, pl.d, pl.waves, sgrid, stream);
-  if (e != hipSuccess) return hip_fail(e, "snapkv_score_vote launch");
-  if (ev) (void)hipEventRecord(ev[3], stream);
-
-  snapkv::PoolParams pp;
-  pp.raw = sp.raw;
-  pp.out = pooled;
-  pp.hkv = pl.hkv;
-  pp.window = pl.window;
-  pp.kernel = kernel;
-  pp.mode = pool_mode;
-  pp.p_stride = pl.p_stride;
-  pp.out_stride = out_stride;
-  pp.budget = sp.budget;
-  pp.skip_fitting = sp.skip_fitting;
-  pp.tab = pl.tab;
-  const dim3 pgrid((out_stride + snapkv::kPoolTile - 1) / snapkv::kPoolTile, pl.hkv, pl.batch);
-  if (ev) (void)hipEventRecord(ev[4], stream);
-  e = snapkv::launch_pool(pp, pgrid, stream);
-  if (e != hipSuccess) return hip_fail(e, "snapkv_pool launch");
-  if (ev) (void)hipEventRecord(ev[5], stream);
+int32_t check_tensors(const void* q_win, const void* k, const void* v, const void* out_k,
+                      const void* out_v, const void* out_idx) {
+  if (!q_win || !k || !v || !out_k || !out_v || !out_idx)
+    return fail(SNAPKV_ERR_INVALID_ARGUMENT, "a tensor pointer is NULL");
+  if (misaligned(q_win) || misaligned(k) || misaligned(v) || misaligned(out_k) ||
+      misaligned(out_v) || misaligned(out_idx))
+    return fail(SNAPKV_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
   return SNAPKV_OK;
 }
 
@@ -188,14 +191,11 @@ int32_t compress_impl(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const v
                       const void* k, const void* v, const int32_t* seq_lens, int32_t window,
                       int32_t kernel, int32_t pool_mode, int32_t budget, void* out_k,
                       void* out_v, int32_t* out_idx, void* workspace, size_t workspace_bytes,
-                      void* stream, void* const* stage_events) {
-  if (!q_win || !k || !v || !out_k || !out_v || !out_idx)
-    return fail(SNAPKV_ERR_INVALID_ARGUMENT, "a tensor pointer is NULL");
-  if (misaligned(q_win) || misaligned(k) || misaligned(v) || misaligned(out_k) ||
-      misaligned(out_v) || misaligned(out_idx))
-    return fail(SNAPKV_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+                      void* stream, void* const* stage_events, bool staged) {
+  int32_t st = check_tensors(q_win, k, v, out_k, out_v, out_idx);
+  if (st != SNAPKV_OK) return st;
   Plan pl;
-  int32_t st = make_plan(batch, hq, hkv, d, seq_lens, window, &pl);
+  st = make_plan(batch, hq, hkv, d, seq_lens, window, &pl);
   if (st != SNAPKV_OK) return st;
   if (budget <= window)
     return fail(SNAPKV_ERR_INVALID_ARGUMENT, "budget must exceed window (it includes the window)");
@@ -205,44 +205,34 @@ int32_t compress_impl(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const v
     return fail(SNAPKV_ERR_WORKSPACE, "workspace must be 16-byte aligned and hold " +
                                           std::to_string(pl.bytes) + " bytes");
   hipStream_t s = static_cast<hipStream_t>(stream);
+  snapkv::PathParams p =
+      path_params(pl, q_win, k, v, workspace, budget, kernel, pool_mode, /*score_all=*/false);
+  p.out_k = static_cast<uint16_t*>(out_k);
+  p.out_v = static_cast<uint16_t*>(out_v);
+  p.out_idx = out_idx;
+  hipError_t e;
+  (void)staged;  // both entry points run one kernel per stage (see the header)
+  // staged: one kernel per stage, optionally bracketed by caller events
   hipEvent_t const* ev = reinterpret_cast<hipEvent_t const*>(stage_events);
-  bool any_scored = false;
-  for (int b = 0; b < batch; ++b) any_scored |= seq_lens[b] > budget;
-
-  const snapkv::ScoreParams sp = score_params(pl, q_win, k, workspace, budget, true);
-  float* pooled = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.off_pooled);
-  if (any_scored) {
-    st = run_scores(pl, sp, kernel, pool_mode, pooled, pl.p_stride, s, ev);
-    if (st != SNAPKV_OK) return st;
-    snapkv::TopkParams tp;
-    tp.pooled = pooled;
-    tp.out_idx = out_idx;
-    tp.hkv = hkv;
-    tp.window = window;
-    tp.budget = budget;
-    tp.p_stride = pl.p_stride;
-    tp.tab = pl.tab;
-    if (ev) (void)hipEventRecord(ev[6], s);
-    hipError_t e = snapkv::launch_topk(tp, dim3(hkv, batch), s);
-    if (e != hipSuccess) return hip_fail(e, "snapkv_topk launch");
-    if (ev) (void)hipEventRecord(ev[7], s);
-  } else if (ev) {
-    for (int i = 0; i < 8; ++i) (void)hipEventRecord(ev[i], s);
-  }
-  snapkv::GatherParams gp;
-  gp.k = static_cast<const uint16_t*>(k);
-  gp.v = static_cast<const uint16_t*>(v);
-  gp.out_k = static_cast<uint16_t*>(out_k);
-  gp.out_v = static_cast<uint16_t*>(out_v);
-  gp.out_idx = out_idx;
-  gp.hkv = hkv;
-  gp.budget = budget;
-  gp.tab = pl.tab;
-  if (ev) (void)hipEventRecord(ev[8], s);
-  hipError_t e = snapkv::launch_gather(
-      gp, d, dim3((budget + snapkv::kGatherRows - 1) / snapkv::kGatherRows, hkv, batch), s);
-  if (e != hipSuccess) return hip_fail(e, "snapkv_gather launch");
-  if (ev) (void)hipEventRecord(ev[9], s);
+  auto mark = [&](int i) {
+    if (ev) (void)hipEventRecord(ev[i], s);
+  };
+  const bool any_scored = p.n_score_items > 0;
+  mark(0);
+  if (any_scored && (e = snapkv::launch_score_stats(p, d, s)) != hipSuccess)
+    return hip_fail(e, "snapkv_score_stats launch");
+  mark(1);
+  mark(2);
+  if (any_scored && (e = snapkv::launch_score_vote(p, d, s)) != hipSuccess)
+    return hip_fail(e, "snapkv_score_vote launch");
+  mark(3);
+  mark(4);
+  if (any_scored && (e = snapkv::launch_topk(p, s)) != hipSuccess)
+    return hip_fail(e, "snapkv_topk launch");
+  mark(5);
+  mark(6);
+  if ((e = snapkv::launch_gather(p, d, s)) != hipSuccess) return hip_fail(e, "snapkv_gather launch");
+  mark(7);
   return SNAPKV_OK;
 }
 
@@ -269,19 +259,19 @@ int32_t snapkv_compress(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads
                         void* stream) {
   return compress_impl(batch, num_q_heads, num_kv_heads, head_dim, q_win, k, v, seq_lens, window,
                        kernel_size, pool_mode, budget, out_k, out_v, out_idx, workspace,
-                       workspace_bytes, stream, nullptr);
+                       workspace_bytes, stream, nullptr, false);
 }
 
-int32_t snapkv_compress_profiled(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                                 int32_t head_dim, const void* q_win, const void* k,
-                                 const void* v, const int32_t* seq_lens, int32_t window,
-                                 int32_t kernel_size, int32_t pool_mode, int32_t budget,
-                                 void* out_k, void* out_v, int32_t* out_idx, void* workspace,
-                                 size_t workspace_bytes, void* stream,
-                                 void* const* stage_events) {
+int32_t snapkv_compress_staged(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, const void* q_win, const void* k,
+                               const void* v, const int32_t* seq_lens, int32_t window,
+                               int32_t kernel_size, int32_t pool_mode, int32_t budget,
+                               void* out_k, void* out_v, int32_t* out_idx, void* workspace,
+                               size_t workspace_bytes, void* stream,
+                               void* const* stage_events) {
   return compress_impl(batch, num_q_heads, num_kv_heads, head_dim, q_win, k, v, seq_lens, window,
                        kernel_size, pool_mode, budget, out_k, out_v, out_idx, workspace,
-                       workspace_bytes, stream, stage_events);
+                       workspace_bytes, stream, stage_events, true);
 }
 
 int32_t snapkv_window_scores(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
@@ -304,9 +294,20 @@ int32_t snapkv_window_scores(int32_t batch, int32_t num_q_heads, int32_t num_kv_
   if (workspace == nullptr || workspace_bytes < pl.bytes || misaligned(workspace))
     return fail(SNAPKV_ERR_WORKSPACE, "workspace must be 16-byte aligned and hold " +
                                           std::to_string(pl.bytes) + " bytes");
-  const snapkv::ScoreParams sp = score_params(pl, q_win, k, workspace, 0, false);
-  return run_scores(pl, sp, kernel_size, pool_mode, out_scores, scores_len,
-                    static_cast<hipStream_t>(stream), nullptr);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  snapkv::PathParams p = path_params(pl, q_win, k, nullptr, workspace, /*budget=*/0, kernel_size,
+                                     pool_mode, /*score_all=*/true);
+  p.pooled = out_scores;
+  p.pooled_stride = scores_len;
+  hipError_t e;
+  if (p.n_score_items > 0) {
+    if ((e = snapkv::launch_score_stats(p, head_dim, s)) != hipSuccess)
+      return hip_fail(e, "snapkv_score_stats launch");
+    if ((e = snapkv::launch_score_vote(p, head_dim, s)) != hipSuccess)
+      return hip_fail(e, "snapkv_score_vote launch");
+  }
+  if ((e = snapkv::launch_pool(p, s)) != hipSuccess) return hip_fail(e, "snapkv_pool launch");
+  return SNAPKV_OK;
 }
 
 const char* snapkv_status_string(int32_t status) {

@@ -1,0 +1,206 @@
+// Device-side building blocks shared by every kernel of the SnapKV path on
+// gfx950 (CDNA4): vector types, MFMA fragment helpers, key tiles staged
+// through LDS, barriers, and agent-scope counters.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "snapkv_kernels.h"
+
+namespace snapkv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kInf = __builtin_inff();
+constexpr int kWaves = kThreads / 64;
+constexpr int kMaxRowTilesPerWave = 2;  // row tiles of 32 window rows per wave
+
+__device__ __forceinline__ float exp2_fast(float x) {
+  return __builtin_amdgcn_exp2f(x);  // v_exp_f32
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+// Row (M index) of accumulator element v held by `lane` in a 32x32 MFMA tile
+// (the N index is lane & 31).
+__device__ __forceinline__ int acc_row(int v, int lane) {
+  return ((v >> 2) << 3) + ((lane >> 5) << 2) + (v & 3);
+}
+
+// Merge two (max, sum of 2^(x - max)) pairs.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float mx = fmaxf(m, m2);
+  if (mx == -kInf) return;
+  s = s * exp2_fast(m - mx) + s2 * exp2_fast(m2 - mx);
+  m = mx;
+}
+
+// ---------------------------------------------------------------- waits ----
+// Workgroup barrier for LDS hand-offs that leaves this wave's outstanding
+// global loads (into registers) in flight; this wave's LDS reads and writes
+// are complete before it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// ------------------------------------------------------------ key tiles ---
+// A tile is 128 keys x D bf16 of one KV head. Threads load it from global
+// memory into registers (16-byte pieces, consecutive threads on consecutive
+// pieces of a key row) and store it to LDS with rows padded by 16 bytes, so
+// the MFMA fragment reads (32 rows at one column offset) hit distinct banks.
+// Two register stages keep two tiles in flight while one is consumed.
+template <int D>
+struct KTile {
+  static constexpr int ROWB = D * 2 + 16;          // padded LDS row (bytes)
+  static constexpr int KEYS = 128;                 // keys per tile
+  static constexpr int BYTES = KEYS * ROWB;
+  static constexpr int PIECES = D / 8;             // 16-byte pieces per row
+  static constexpr int LOADS = KEYS * PIECES / kThreads;  // per thread per tile
+  static_assert(LOADS >= 1 && KEYS * PIECES % kThreads == 0, "tile split");
+  typedef u32x4 Regs[LOADS];
+};
+
+// This thread's pieces of keys [tk0, tk0 + 128) into registers. Rows at or
+// beyond kend repeat key kend - 1 (every consumer masks them): the loads stay
+// unconditional, so the compiler can count them and wait only for the tile
+// it stores while the next one is still in flight.
+template <int D>
+__device__ __forceinline__ void load_key_tile(typename KTile<D>::Regs& r, const uint16_t* kb,
+                                              size_t tstride, int tk0, int kend, int tid) {
+  using T = KTile<D>;
+#pragma unroll
+  for (int u = 0; u < T::LOADS; ++u) {
+    const int pc = tid + u * kThreads;
+    const int key = pc / T::PIECES, col = pc % T::PIECES;
+    const int j = min(tk0 + key, kend - 1);
+    r[u] = *reinterpret_cast<const u32x4*>(kb + (size_t)j * tstride + col * 8);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_key_tile(const typename KTile<D>::Regs& r,
+                                               unsigned char* tile, int tid) {
+  using T = KTile<D>;
+#pragma unroll
+  for (int u = 0; u < T::LOADS; ++u) {
+    const int pc = tid + u * kThreads;
+    const int key = pc / T::PIECES, col = pc % T::PIECES;
+    *reinterpret_cast<u32x4*>(tile + key * T::ROWB + col * 16) = r[u];
+  }
+}
+
+// MFMA fragments of key block kb (32 keys) of a staged tile: lane holds key
+// kb*32 + (lane & 31), D elements 16*s + 8*(lane >> 5) .. +7 for k-step s.
+template <int D>
+__device__ __forceinline__ void read_key_frags(bf16x8 (&kf)[D / 16], const unsigned char* tile,
+                                               int kb, int lane) {
+  using T = KTile<D>;
+  const unsigned char* row = tile + (kb * 32 + (lane & 31)) * T::ROWB + (lane >> 5) * 16;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s)
+    kf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(row + s * 32));
+  // issue every fragment read before the MFMAs that consume them, instead of
+  // one LDS round trip per MFMA
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Stream the keys [key0, kend) of one head through two LDS tile buffers,
+// with two more tiles in flight in registers. Tile i is stored to LDS, the
+// loads of tile i + 2 go into the freed registers, a barrier makes tile i
+// visible (and guarantees every wave is done with tile i - 1), then
+// after_barrier(i) and compute(tile, i) run. Global loads stay in flight
+// across the barriers. The loads are unconditional (past the end they re-read
+// key kend - 1) and the loop starts with compute, so every store waits only
+// for its own registers.
+template <int D, typename Compute, typename After>
+__device__ __forceinline__ void stream_key_tiles(const uint16_t* kb, size_t tstride, int key0,
+                                                 int kend, unsigned char (*ring)[KTile<D>::BYTES],
+                                                 Compute&& compute, After&& after_barrier) {
+  using T = KTile<D>;
+  const int tid = threadIdx.x;
+  const int ntiles = (kend - key0 + T::KEYS - 1) / T::KEYS;
+  typename T::Regs ra, rb;
+  load_key_tile<D>(ra, kb, tstride, key0, kend, tid);
+  asm volatile("" ::: "memory");  // keep tile 0's loads older than tile 1's
+  load_key_tile<D>(rb, kb, tstride, key0 + T::KEYS, kend, tid);
+  store_key_tile<D>(ra, ring[0], tid);
+  load_key_tile<D>(ra, kb, tstride, key0 + 2 * T::KEYS, kend, tid);
+  lds_barrier();
+  after_barrier(0);
+  for (int i = 0;; i += 2) {
+    compute(ring[0], i);
+    if (i + 1 >= ntiles) break;
+    store_key_tile<D>(rb, ring[1], tid);
+    load_key_tile<D>(rb, kb, tstride, key0 + (i + 3) * T::KEYS, kend, tid);
+    lds_barrier();
+    after_barrier(i + 1);
+    compute(ring[1], i + 1);
+    if (i + 2 >= ntiles) break;
+    store_key_tile<D>(ra, ring[0], tid);
+    load_key_tile<D>(ra, kb, tstride, key0 + (i + 4) * T::KEYS, kend, tid);
+    lds_barrier();
+    after_barrier(i + 2);
+  }
+}
+
+// Query fragments of this wave's row tiles (same D-to-k-slot map as the
+// keys); rows at or beyond `rows` are zero.
+template <int D, int RTW>
+__device__ __forceinline__ void load_query_frags(bf16x8 (&qf)[RTW][D / 16],
+                                                 const uint16_t* qbase, int rows, int wr,
+                                                 int nwr, int my_nrt, int lane) {
+#pragma unroll
+  for (int t = 0; t < RTW; ++t) {
+    const int r = (wr + nwr * t) * 32 + (lane & 31);
+    const bool ok = t < my_nrt && r < rows;
+    // unconditional load of a valid row, zeroed when out of range: no branch
+    // around the loads keeps the compiler's count of pending loads exact
+    const uint16_t* src = qbase + (size_t)min(r, rows - 1) * D + (lane >> 5) * 8;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      u32x4 x = *reinterpret_cast<const u32x4*>(src + s * 16);
+      const uint32_t keep = ok ? 0xFFFFFFFFu : 0u;
+      x &= u32x4{keep, keep, keep, keep};
+      qf[t][s] = as_bf16x8(x);
+    }
+  }
+}
+
+// ------------------------------------------------------ agent counters ----
+// Publish: every thread's prior global writes become visible device-wide
+// before the counter moves (the barrier gathers the workgroup's writes, the
+// release on the atomic makes them visible to other XCDs).
+__device__ __forceinline__ void publish(uint32_t* counter) {
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until *counter >= target. Thread 0 polls with relaxed agent-scope
+// loads (coherent, no cache maintenance per poll) and sleeps between polls;
+// one acquire fence follows, then a barrier, so writes published before the
+// counter reached target are visible to the whole workgroup. The wait is
+// bounded by the 100 MHz wall clock: after kWaitTicks it gives up and
+// records the timeout in *error (the results are then invalid, but every
+// wave still exits).
+constexpr uint64_t kWaitTicks = 10000000ull;  // 0.1 s
+__device__ __forceinline__ void wait_count(const uint32_t* counter, uint32_t target,
+                                           uint32_t* error) {
+  if (threadIdx.x == 0) {
+    const uint64_t t0 = wall_clock64();
+    while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(8);
+      if (wall_clock64() - t0 > kWaitTicks) {
+        __hip_atomic_fetch_or(error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+}
+
+}  // namespace snapkv

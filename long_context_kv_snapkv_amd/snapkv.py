@@ -28,7 +28,7 @@ SNAPKV_ERR_WORKSPACE = 3
 SNAPKV_ERR_HIP = 4
 SNAPKV_POOL_AVG = 0
 SNAPKV_POOL_MAX = 1
-SNAPKV_NUM_STAGES = 5
+SNAPKV_NUM_STAGES = 4
 
 _POOL_NAMES = {"avg": SNAPKV_POOL_AVG, "avgpool": SNAPKV_POOL_AVG,
                "max": SNAPKV_POOL_MAX, "maxpool": SNAPKV_POOL_MAX}
@@ -70,8 +70,8 @@ def load_library():
                      _i32, _vp, _vp, _vp, _vp, _sz, _vp]
     lib.snapkv_compress.argtypes = compress_args
     lib.snapkv_compress.restype = _i32
-    lib.snapkv_compress_profiled.argtypes = compress_args + [ctypes.POINTER(_vp)]
-    lib.snapkv_compress_profiled.restype = _i32
+    lib.snapkv_compress_staged.argtypes = compress_args + [ctypes.POINTER(_vp)]
+    lib.snapkv_compress_staged.restype = _i32
     lib.snapkv_window_scores.argtypes = [_i32, _i32, _i32, _i32, _vp, _vp, _pi32, _i32,
                                          _i32, _i32, _vp, _i32, _vp, _sz, _vp]
     lib.snapkv_window_scores.restype = _i32
@@ -133,6 +133,14 @@ def _check_tensor(name: str, t: torch.Tensor, ndim: int, dtype=torch.bfloat16) -
                          f"got {t.dtype} {tuple(t.shape)} on {t.device}")
 
 
+def new_workspace(num_q_heads: int, num_kv_heads: int, head_dim: int,
+                  seq_lens: Iterable[int], window: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace for this shape (reusable across calls that do
+    not overlap in time)."""
+    return torch.zeros(snapkv_workspace_size(num_q_heads, num_kv_heads, head_dim, seq_lens,
+                                             window), dtype=torch.uint8, device=device)
+
+
 def snapkv_workspace_size(num_q_heads: int, num_kv_heads: int, head_dim: int,
                           seq_lens: Iterable[int], window: int) -> int:
     lib = load_library()
@@ -159,8 +167,12 @@ def snapkv_compress(q_win: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                     out_v: Optional[torch.Tensor] = None,
                     out_idx: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None, stream=None,
-                    stage_events: Optional[Sequence] = None):
-    """Compress one layer. Returns (out_k, out_v, out_idx); see include/snapkv.h."""
+                    staged: bool = False, stage_events: Optional[Sequence] = None):
+    """Compress one layer. Returns (out_k, out_v, out_idx); see include/snapkv.h.
+
+    staged=True (or stage_events given) runs snapkv_compress_staged, one
+    kernel per stage; otherwise the single persistent kernel. A workspace
+    passed in must be zero-filled before its first use (new_workspace)."""
     lib = load_library()
     _check_tensor("q_win", q_win, 4)
     _check_tensor("k", k, 3)
@@ -185,16 +197,19 @@ def snapkv_compress(q_win: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             or tuple(out_idx.shape) != (batch, hkv, budget):
         raise ValueError("output shapes must be [batch, H_kv, budget, D] and [batch, H_kv, budget]")
     if workspace is None:
-        workspace = torch.empty(snapkv_workspace_size(hq, hkv, d, vals, window),
-                                dtype=torch.uint8, device=dev)
+        workspace = new_workspace(hq, hkv, d, vals, window, dev)
     args = (batch, hq, hkv, d, _ptr(q_win), _ptr(k), _ptr(v), arr, window, kernel_size,
             pool_mode_code(pool_mode), budget, _ptr(out_k), _ptr(out_v), _ptr(out_idx),
             _ptr(workspace), workspace.numel(), _stream(stream, dev))
-    if stage_events is None:
-        _check(lib.snapkv_compress(*args))
-    else:
+    if stage_events is not None:
+        if len(stage_events) != 2 * SNAPKV_NUM_STAGES:
+            raise ValueError(f"stage_events needs {2 * SNAPKV_NUM_STAGES} events")
         evs = (_vp * len(stage_events))(*[int(e.cuda_event) for e in stage_events])
-        _check(lib.snapkv_compress_profiled(*args, evs))
+        _check(lib.snapkv_compress_staged(*args, evs))
+    elif staged:
+        _check(lib.snapkv_compress_staged(*args, None))
+    else:
+        _check(lib.snapkv_compress(*args))
     return out_k, out_v, out_idx
 
 

@@ -38,14 +38,24 @@ def upload(x):
     return bits_to_device(x.q_win), bits_to_device(x.k), bits_to_device(x.v)
 
 
-def run_gpu(x, window, kernel, pool, budget, dev_inputs=None):
+def run_gpu(x, window, kernel, pool, budget, dev_inputs=None, workspace=None):
+    """snapkv_compress, snapkv_compress_staged on the same inputs, and the
+    exported scores. The two compress calls must agree bit for bit."""
     q, k, v = dev_inputs if dev_inputs is not None else upload(x)
     lens = x.seq_lens.tolist()
-    out_k, out_v, out_idx = skv.snapkv_compress(q, k, v, lens, window, kernel, pool, budget)
+    hq, hkv, d = q.shape[1], k.shape[1], k.shape[2]
+    ws = workspace if workspace is not None else skv.new_workspace(hq, hkv, d, lens, window)
+    out_k, out_v, out_idx = skv.snapkv_compress(q, k, v, lens, window, kernel, pool, budget,
+                                                workspace=ws)
+    sk, sv, si = skv.snapkv_compress(q, k, v, lens, window, kernel, pool, budget, staged=True)
     scores = skv.snapkv_window_scores(q, k, lens, window, kernel, pool)
     torch.cuda.synchronize()
-    return dict(out_k=bits_from_device(out_k), out_v=bits_from_device(out_v),
-                out_idx=out_idx.cpu().numpy(), scores=scores.cpu().numpy().astype(np.float64))
+    res = dict(out_k=bits_from_device(out_k), out_v=bits_from_device(out_v),
+               out_idx=out_idx.cpu().numpy(), scores=scores.cpu().numpy().astype(np.float64))
+    np.testing.assert_array_equal(res["out_idx"], si.cpu().numpy())
+    np.testing.assert_array_equal(res["out_k"], bits_from_device(sk))
+    np.testing.assert_array_equal(res["out_v"], bits_from_device(sv))
+    return res
 
 
 def check_scores(gpu_scores, ref_pooled, seq_lens, window):

@@ -23,6 +23,7 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = skv.header_functions()
     assert len(names) == 7, names
+    assert "snapkv_compress_staged" in names
     for name in names:
         assert hasattr(lib, name), name
 
@@ -38,9 +39,8 @@ def test_status_strings(lib):
 
 def test_stage_names(lib):
     names = [skv.snapkv_stage_name(i) for i in range(skv.SNAPKV_NUM_STAGES)]
-    assert names == ["snapkv_score_stats", "snapkv_score_vote", "snapkv_pool",
-                     "snapkv_topk", "snapkv_gather"]
-    assert skv.snapkv_stage_name(-1) is None and skv.snapkv_stage_name(5) is None
+    assert names == ["snapkv_score_stats", "snapkv_score_vote", "snapkv_topk", "snapkv_gather"]
+    assert skv.snapkv_stage_name(-1) is None and skv.snapkv_stage_name(4) is None
 
 
 FAKE = 0x10000  # 16-byte aligned address that is never dereferenced

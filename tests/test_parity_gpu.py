@@ -138,6 +138,7 @@ def test_guard_bands_untouched():
     ibuf = torch.full((ni + 2 * guard,), 12345, dtype=torch.int32, device="cuda")
     ws_bytes = skv.snapkv_workspace_size(hq, hkv, d, lens, window)
     wbuf = torch.full((ws_bytes + 2 * guard,), 0xA5, dtype=torch.uint8, device="cuda")
+    wbuf[guard:guard + ws_bytes] = 0  # the workspace itself starts zero-filled
     out_k = kbuf[guard:guard + nk].view(torch.bfloat16).view(batch, hkv, budget, d)
     out_v = vbuf[guard:guard + nk].view(torch.bfloat16).view(batch, hkv, budget, d)
     out_i = ibuf[guard:guard + ni].view(batch, hkv, budget)
@@ -151,6 +152,33 @@ def test_guard_bands_untouched():
                out_idx=out_i.cpu().numpy())
     from parity import check_structure_and_gather
     check_structure_and_gather(res, x, window, budget)
+
+
+@needs_gpu
+def test_workspace_reused_across_calls_and_shapes():
+    # one buffer, sized for the largest shape and never cleared, serves a
+    # sequence of calls of different shapes: intermediates from one call
+    # must not leak into the next
+    from parity import run_gpu
+    shapes = [([3000, 500], 16, 4, 128, 32, 7, "max", 256),
+              ([900], 8, 8, 64, 16, 5, "avg", 128),
+              ([3000, 500], 16, 4, 128, 32, 7, "max", 256),
+              ([70, 2000, 40], 32, 8, 128, 64, 13, "avg", 512)]
+    size = max(skv.snapkv_workspace_size(hq, hkv, d, lens, w)
+               for lens, hq, hkv, d, w, *_ in shapes)
+    ws = torch.full((size,), 0x5A, dtype=torch.uint8, device="cuda")
+    for i, (lens, hq, hkv, d, w, kern, pool, budget) in enumerate(shapes):
+        print(f"[parity] reuse call {i} {lens}", flush=True)
+        x = make_custom(lens, hq, hkv, d, w, seed=40 + i)
+        res = run_gpu(x, w, kern, pool, budget, workspace=ws)
+        full_check(x, w, kern, pool, budget, res=res)
+
+
+@pytest.mark.skip(reason="the single-launch persistent kernel did not finish on its first "
+                         "two hardware runs (tiny MHA workload); it is not launched by the "
+                         "library until the cause is established")
+def test_persistent_single_launch_path():
+    raise AssertionError("not enabled")
 
 
 @needs_gpu
