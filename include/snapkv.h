@@ -76,14 +76,16 @@ extern "C" {
 #define SNAPKV_MAX_BATCH 256       /* prompts per call */
 #define SNAPKV_MAX_ROWS 512        /* G * W, window rows scored per KV head */
 #define SNAPKV_MAX_KERNEL 2049     /* largest pooling kernel */
-#define SNAPKV_NUM_STAGES 4        /* kernels of snapkv_compress_staged */
+#define SNAPKV_NUM_STAGES 4        /* stages: vote statistics, vote + pool,
+                                      select, gather */
 
 /*
  * Bytes of device workspace that snapkv_compress, snapkv_compress_staged and
  * snapkv_window_scores need for this shape (the same size serves all three).
  * The workspace holds intermediate results only (per-chunk softmax
- * statistics, raw and pooled score vectors, and a reserved counter area):
- * it needs no initialisation and may be reused across calls and shapes.
+ * statistics and pooled score vectors, each written before it is read): it
+ * needs no initialisation and may be reused across calls and shapes, but not
+ * by two calls in flight at once.
  * Returns SNAPKV_OK and writes *bytes, or an error status under the
  * validation rules of snapkv_compress.
  */
@@ -93,8 +95,9 @@ int32_t snapkv_workspace_size(int32_t batch, int32_t num_q_heads,
                               size_t* bytes);
 
 /*
- * Compress one layer's prompt KV cache (steps 1-4 above). The stages run as
- * SNAPKV_NUM_STAGES consecutive kernels on `stream`.
+ * Compress one layer's prompt KV cache (steps 1-4 above) with
+ * SNAPKV_NUM_STAGES consecutive kernels on `stream`: vote statistics, vote
+ * with pooling, selection, gather.
  *
  *   window       W >= 1, the observation window (pages: 16-64)
  *   kernel_size  odd, 1 <= kernel_size <= SNAPKV_MAX_KERNEL; 1 = no pooling
@@ -129,8 +132,8 @@ int32_t snapkv_compress(int32_t batch, int32_t num_q_heads,
 
 /*
  * snapkv_compress with optional per-stage timing: the same kernels (named by
- * snapkv_stage_name: window statistics, window vote, pooling + selection,
- * gather) and identical results. When stage_events is not NULL it points to
+ * snapkv_stage_name) and identical results. When stage_events is not NULL it
+ * points to
  * 2 * SNAPKV_NUM_STAGES caller-owned hipEvent_t; stage_events[2*s] is
  * recorded before and stage_events[2*s+1] after stage s on the same stream.
  * Errors as for snapkv_compress.
@@ -172,7 +175,8 @@ const char* snapkv_status_string(int32_t status);
 /* Detail of the last failure on the calling thread ("" if none). */
 const char* snapkv_last_error(void);
 
-/* Name of stage s of snapkv_compress, or NULL when s is out of range. */
+/* Name of stage s of snapkv_compress_staged (its kernel's name), or NULL
+ * when s is out of range. */
 const char* snapkv_stage_name(int32_t stage);
 
 #ifdef __cplusplus

@@ -25,7 +25,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
 const char* const kStageNames[SNAPKV_NUM_STAGES] = {"snapkv_score_stats", "snapkv_score_vote",
-                                                    "snapkv_topk", "snapkv_gather"};
+                                                    "snapkv_select", "snapkv_gather"};
 
 int largest_pow2_at_most(int x) {
   int p = 1;
@@ -35,14 +35,14 @@ int largest_pow2_at_most(int x) {
 
 // Everything a call needs, derived from shapes alone, so the workspace size
 // computed ahead of a call matches the call. Workspace layout:
-//   sync   uint32[4 + 3*batch*H_kv]          persistent-kernel counters
-//   part   float2[batch, H_kv, nchunk, rows_pad]
-//   raw    float [batch, H_kv, p_stride]
-//   pooled float [batch, H_kv, p_stride]      selection spill for long prefixes
+//   part      float2[batch, H_kv, nchunk, rows_pad]  per-chunk row statistics
+//   pooled    float [batch, H_kv, p_stride]      pooled scores, p_stride =
+//                                                max P rounded up to 64
+// Every word is written by a call before that call reads it.
 struct Plan {
   int batch, hq, hkv, d, window, group, rows, rows_pad, nrt, nwr;
   int chunk, nchunk, l_max, p_max, p_stride;
-  size_t off_sync, off_part, off_raw, off_pooled, bytes;
+  size_t off_part, off_pooled, bytes;
   snapkv::PromptTable tab;
 };
 
@@ -104,12 +104,8 @@ int32_t make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const int32
   pl->p_stride = (int)align_up((size_t)pl->p_max, 64);
   const size_t heads = (size_t)batch * hkv;
   size_t off = 0;
-  pl->off_sync = off;
-  off = align_up(off + (snapkv::kSyncHeads + 3 * heads) * sizeof(uint32_t), 256);
   pl->off_part = off;
   off = align_up(off + heads * pl->nchunk * pl->rows_pad * sizeof(float2), 256);
-  pl->off_raw = off;
-  off = align_up(off + heads * pl->p_stride * sizeof(float), 256);
   pl->off_pooled = off;
   off = align_up(off + heads * pl->p_stride * sizeof(float), 256);
   pl->bytes = off;
@@ -137,9 +133,7 @@ snapkv::PathParams path_params(const Plan& pl, const void* q, const void* k, con
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
   p.v = static_cast<const uint16_t*>(v);
-  p.sync = reinterpret_cast<uint32_t*>(w + pl.off_sync);
   p.part = reinterpret_cast<float2*>(w + pl.off_part);
-  p.raw = reinterpret_cast<float*>(w + pl.off_raw);
   p.pooled = reinterpret_cast<float*>(w + pl.off_pooled);
   p.pooled_stride = pl.p_stride;
   p.batch = pl.batch;
@@ -152,25 +146,22 @@ snapkv::PathParams path_params(const Plan& pl, const void* q, const void* k, con
   p.nwr = pl.nwr;
   p.chunk = pl.chunk;
   p.nchunk = pl.nchunk;
-  p.p_stride = pl.p_stride;
   p.budget = budget;
   p.kernel = kernel;
   p.pool_mode = pool_mode;
   p.score_all = score_all ? 1 : 0;
   p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)pl.d));
   p.tab = pl.tab;
-  int items = 0;
-  for (int b = 0; b < pl.batch; ++b) {
-    p.item_start[b] = items;
-    const int L = pl.tab.len[b];
-    const bool scored = L - pl.window >= 1 && (score_all || L > budget);
-    if (scored) items += pl.hkv * ((L + pl.chunk - 1) / pl.chunk);
-  }
-  p.item_start[pl.batch] = items;
-  p.n_score_items = items;
   p.n_gather_blocks = budget > 0 ? (budget + snapkv::kGatherRows - 1) / snapkv::kGatherRows : 0;
-  p.n_tickets = 2 * items + pl.batch * pl.hkv * (1 + p.n_gather_blocks);
   return p;
+}
+
+bool any_scored(const Plan& pl, int32_t budget, bool score_all) {
+  for (int b = 0; b < pl.batch; ++b) {
+    const int L = pl.tab.len[b];
+    if (L - pl.window >= 1 && (score_all || L > budget)) return true;
+  }
+  return false;
 }
 
 int32_t hip_fail(hipError_t e, const char* what) {
@@ -191,7 +182,7 @@ int32_t compress_impl(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const v
                       const void* k, const void* v, const int32_t* seq_lens, int32_t window,
                       int32_t kernel, int32_t pool_mode, int32_t budget, void* out_k,
                       void* out_v, int32_t* out_idx, void* workspace, size_t workspace_bytes,
-                      void* stream, void* const* stage_events, bool staged) {
+                      void* stream, void* const* stage_events) {
   int32_t st = check_tensors(q_win, k, v, out_k, out_v, out_idx);
   if (st != SNAPKV_OK) return st;
   Plan pl;
@@ -211,24 +202,23 @@ int32_t compress_impl(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const v
   p.out_v = static_cast<uint16_t*>(out_v);
   p.out_idx = out_idx;
   hipError_t e;
-  (void)staged;  // both entry points run one kernel per stage (see the header)
-  // staged: one kernel per stage, optionally bracketed by caller events
+  // optional caller events bracket every stage (snapkv_compress_staged)
   hipEvent_t const* ev = reinterpret_cast<hipEvent_t const*>(stage_events);
   auto mark = [&](int i) {
     if (ev) (void)hipEventRecord(ev[i], s);
   };
-  const bool any_scored = p.n_score_items > 0;
+  const bool scored = any_scored(pl, budget, false);
   mark(0);
-  if (any_scored && (e = snapkv::launch_score_stats(p, d, s)) != hipSuccess)
+  if (scored && (e = snapkv::launch_score_stats(p, d, s)) != hipSuccess)
     return hip_fail(e, "snapkv_score_stats launch");
   mark(1);
   mark(2);
-  if (any_scored && (e = snapkv::launch_score_vote(p, d, s)) != hipSuccess)
+  if (scored && (e = snapkv::launch_score_vote(p, d, s)) != hipSuccess)
     return hip_fail(e, "snapkv_score_vote launch");
   mark(3);
   mark(4);
-  if (any_scored && (e = snapkv::launch_topk(p, s)) != hipSuccess)
-    return hip_fail(e, "snapkv_topk launch");
+  if (scored && (e = snapkv::launch_select(p, s)) != hipSuccess)
+    return hip_fail(e, "snapkv_select launch");
   mark(5);
   mark(6);
   if ((e = snapkv::launch_gather(p, d, s)) != hipSuccess) return hip_fail(e, "snapkv_gather launch");
@@ -259,7 +249,7 @@ int32_t snapkv_compress(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads
                         void* stream) {
   return compress_impl(batch, num_q_heads, num_kv_heads, head_dim, q_win, k, v, seq_lens, window,
                        kernel_size, pool_mode, budget, out_k, out_v, out_idx, workspace,
-                       workspace_bytes, stream, nullptr, false);
+                       workspace_bytes, stream, nullptr);
 }
 
 int32_t snapkv_compress_staged(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
@@ -271,7 +261,7 @@ int32_t snapkv_compress_staged(int32_t batch, int32_t num_q_heads, int32_t num_k
                                void* const* stage_events) {
   return compress_impl(batch, num_q_heads, num_kv_heads, head_dim, q_win, k, v, seq_lens, window,
                        kernel_size, pool_mode, budget, out_k, out_v, out_idx, workspace,
-                       workspace_bytes, stream, stage_events, true);
+                       workspace_bytes, stream, stage_events);
 }
 
 int32_t snapkv_window_scores(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
@@ -299,14 +289,14 @@ int32_t snapkv_window_scores(int32_t batch, int32_t num_q_heads, int32_t num_kv_
                                      pool_mode, /*score_all=*/true);
   p.pooled = out_scores;
   p.pooled_stride = scores_len;
+  p.export_scores = 1;
   hipError_t e;
-  if (p.n_score_items > 0) {
-    if ((e = snapkv::launch_score_stats(p, head_dim, s)) != hipSuccess)
-      return hip_fail(e, "snapkv_score_stats launch");
-    if ((e = snapkv::launch_score_vote(p, head_dim, s)) != hipSuccess)
-      return hip_fail(e, "snapkv_score_vote launch");
-  }
-  if ((e = snapkv::launch_pool(p, s)) != hipSuccess) return hip_fail(e, "snapkv_pool launch");
+  // stats only where something is scored; the vote grid always runs, as it
+  // also zeroes the exported rows past P
+  if (any_scored(pl, 0, true) && (e = snapkv::launch_score_stats(p, head_dim, s)) != hipSuccess)
+    return hip_fail(e, "snapkv_score_stats launch");
+  if ((e = snapkv::launch_score_vote(p, head_dim, s)) != hipSuccess)
+    return hip_fail(e, "snapkv_score_vote launch");
   return SNAPKV_OK;
 }
 

@@ -1,6 +1,6 @@
 // Device-side building blocks shared by every kernel of the SnapKV path on
 // gfx950 (CDNA4): vector types, MFMA fragment helpers, key tiles staged
-// through LDS, barriers, and agent-scope counters.
+// through LDS, and barriers.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -167,40 +167,6 @@ __device__ __forceinline__ void load_query_frags(bf16x8 (&qf)[RTW][D / 16],
       qf[t][s] = as_bf16x8(x);
     }
   }
-}
-
-// ------------------------------------------------------ agent counters ----
-// Publish: every thread's prior global writes become visible device-wide
-// before the counter moves (the barrier gathers the workgroup's writes, the
-// release on the atomic makes them visible to other XCDs).
-__device__ __forceinline__ void publish(uint32_t* counter) {
-  __syncthreads();
-  if (threadIdx.x == 0)
-    __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Wait until *counter >= target. Thread 0 polls with relaxed agent-scope
-// loads (coherent, no cache maintenance per poll) and sleeps between polls;
-// one acquire fence follows, then a barrier, so writes published before the
-// counter reached target are visible to the whole workgroup. The wait is
-// bounded by the 100 MHz wall clock: after kWaitTicks it gives up and
-// records the timeout in *error (the results are then invalid, but every
-// wave still exits).
-constexpr uint64_t kWaitTicks = 10000000ull;  // 0.1 s
-__device__ __forceinline__ void wait_count(const uint32_t* counter, uint32_t target,
-                                           uint32_t* error) {
-  if (threadIdx.x == 0) {
-    const uint64_t t0 = wall_clock64();
-    while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(8);
-      if (wall_clock64() - t0 > kWaitTicks) {
-        __hip_atomic_fetch_or(error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  }
-  __syncthreads();
 }
 
 }  // namespace snapkv

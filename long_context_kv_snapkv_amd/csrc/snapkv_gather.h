@@ -19,7 +19,7 @@
 namespace snapkv {
 
 template <int D>
-__device__ void snapkv_gather_item(const PathParams& p, int b, int h, int rb) {
+__device__ __forceinline__ void snapkv_gather_item(const PathParams& p, int b, int h, int rb) {
   constexpr int PIECES = D / 8;
   constexpr int ROWS_PER_PASS = kThreads / PIECES;
   constexpr int PASSES = kGatherRows / ROWS_PER_PASS;

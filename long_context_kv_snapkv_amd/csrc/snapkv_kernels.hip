@@ -1,28 +1,14 @@
-// Kernels of the SnapKV compression path on gfx950.
+// Kernels of the SnapKV compression path on gfx950, as grids of work items:
 //
-// The library runs the stages as separate kernels (snapkv_score_stats,
-// snapkv_score_vote, snapkv_topk with pooling, snapkv_gather; snapkv_pool for
-// the score export). snapkv_compress_persistent is compiled but NOT launched:
-// its first hardware runs did not finish (see the design notes), and it stays
-// disabled until the cause is established.
+//   snapkv_score_stats  (chunk, head, prompt)   per-row softmax statistics
+//   snapkv_score_vote   (chunk, head, prompt)   window vote + pooling
+//   snapkv_select       (head, prompt)          top-(B - W) positions
+//   snapkv_gather       (row block, head, prompt)
 //
-// snapkv_compress_persistent runs a whole call in one launch: one workgroup
-// per CU takes tickets from an atomic counter, in this order:
-//   [0, S)             stats items   (prompt, head, key chunk)
-//   [S, 2S)            vote items    (same enumeration)
-//   [2S, 2S + H)       select items  (prompt, head): pooling + top-(B-W)
-//   [2S + H, ...)      gather items  (prompt, head, 64 output rows)
-// An item waits only for items with lower tickets (vote: all stats items of
-// its head; select: all vote items of its head; gather: its head's select),
-// so the workgroups that hold those tickets are running and never wait on a
-// higher ticket: the schedule cannot deadlock, whatever the number of
-// resident workgroups. Completion is published with release atomics on
-// per-head counters; waits are acquire polls, bounded (a timeout raises the
-// error word and lets every wave exit). The last workgroup to leave zeroes
-// the counters for the next call.
-//
-// The standalone kernels run the same item bodies over plain grids; they
-// serve the score export and the per-stage timing path.
+// A compress call runs the four in stream order; the kernel boundaries carry
+// every hand-off between stages (no inter-workgroup waiting or flags). The
+// score export runs stats and vote only, with the caller's buffer as the
+// pooled rows.
 #include <type_traits>
 
 #include "snapkv_gather.h"
@@ -41,7 +27,6 @@ __device__ __forceinline__ int num_chunks(const PathParams& p, int b) {
   return (p.tab.len[b] + p.chunk - 1) / p.chunk;
 }
 
-// ------------------------------------------------------ standalone grids --
 template <int D, int RTW>
 __global__ void __launch_bounds__(kThreads) snapkv_score_stats(const PathParams p) {
   __shared__ StatsSmem<D> sm;
@@ -54,125 +39,27 @@ template <int D, int RTW>
 __global__ void __launch_bounds__(kThreads) snapkv_score_vote(const PathParams p) {
   __shared__ VoteSmem<D> sm;
   const int b = blockIdx.z, h = blockIdx.y, c = blockIdx.x;
-  if (!is_scored(p, b) || c * p.chunk >= p.tab.len[b] - p.window) return;
+  const int P = p.tab.len[b] - p.window;
+  const int nvote = P >= 1 ? (P + p.chunk - 1) / p.chunk : 0;
+  if (p.export_scores && c == (nvote > 0 ? nvote - 1 : 0)) {
+    // exported rows are zero past P (the whole row when nothing is scored)
+    float* row = p.pooled + (size_t)(b * p.hkv + h) * p.pooled_stride;
+    for (int j = max(P, 0) + (int)threadIdx.x; j < p.pooled_stride; j += kThreads) row[j] = 0.f;
+  }
+  if (!is_scored(p, b) || c >= nvote) return;
   snapkv_score_vote_item<D, RTW>(p, sm, b, h, c);
 }
 
-// Export of the pooled scores (entries past P are 0): a tile and its halo
-// are staged in LDS, then pooled with the same operation order as selection.
-__global__ void __launch_bounds__(kThreads) snapkv_pool(const PathParams p) {
-  __shared__ __attribute__((aligned(16))) float tile[kPoolTile + kMaxKernel];
-  const int b = blockIdx.z, h = blockIdx.y;
-  const int j0 = blockIdx.x * kPoolTile;
-  const int P = p.tab.len[b] - p.window;
-  float* out = p.pooled + (size_t)(b * p.hkv + h) * p.pooled_stride;
-  const int jend = min(j0 + kPoolTile, p.pooled_stride);
-  const int tid = threadIdx.x;
-  if (P < 1) {
-    for (int j = j0 + tid; j < jend; j += kThreads) out[j] = 0.f;
-    return;
-  }
-  const int r = p.kernel >> 1;
-  const float* src = p.raw + (size_t)(b * p.hkv + h) * p.p_stride;
-  for (int u = tid; u < kPoolTile + 2 * r; u += kThreads) {
-    const int j = j0 - r + u;
-    tile[u] = (j >= 0 && j < P) ? src[j] : 0.f;
-  }
-  __syncthreads();
-  for (int j = j0 + tid; j < jend; j += kThreads) {
-    out[j] = j < P ? pool_value([&](int u) { return tile[u - (j0 - r)]; }, j, P, p.kernel,
-                                p.pool_mode)
-                   : 0.f;
-  }
-}
-
-__global__ void __launch_bounds__(kThreads) snapkv_topk(const PathParams p) {
+__global__ void __launch_bounds__(kThreads) snapkv_select(const PathParams p) {
   __shared__ SelectSmem sm;
   const int h = blockIdx.x, b = blockIdx.y;
   if (p.tab.len[b] <= p.budget) return;  // kept whole by the gather
-  snapkv_topk_item(p, sm, b, h);
+  snapkv_select_item(p, sm, b, h);
 }
 
 template <int D>
 __global__ void __launch_bounds__(kThreads) snapkv_gather(const PathParams p) {
   snapkv_gather_item<D>(p, blockIdx.z, blockIdx.y, blockIdx.x);
-}
-
-// ------------------------------------------------------------ persistent --
-template <int D>
-union alignas(16) PersistentSmem {
-  StatsSmem<D> stats;
-  VoteSmem<D> vote;
-  SelectSmem select;
-};
-
-template <int D, int RTW>
-__global__ void __launch_bounds__(kThreads) snapkv_compress_persistent(const PathParams p) {
-  __shared__ PersistentSmem<D> sm;
-  __shared__ uint32_t s_ticket, s_last;
-  const int heads = p.batch * p.hkv;
-  uint32_t* done_stats = p.sync + kSyncHeads;
-  uint32_t* done_vote = done_stats + heads;
-  uint32_t* done_select = done_vote + heads;
-  uint32_t* err = p.sync + kSyncError;
-  const int ns = p.n_score_items;
-
-  for (;;) {
-    if (threadIdx.x == 0)
-      s_ticket = __hip_atomic_fetch_add(p.sync + kSyncTicket, 1u, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const uint32_t t = s_ticket;
-    __syncthreads();
-    if (t >= (uint32_t)p.n_tickets) break;
-    if (t < (uint32_t)(2 * ns)) {
-      const bool vote = t >= (uint32_t)ns;
-      const int x = vote ? (int)t - ns : (int)t;
-      int lo = 0, hi = p.batch;  // prompt: largest b with item_start[b] <= x
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (p.item_start[mid] <= x) lo = mid; else hi = mid;
-      }
-      const int b = lo;
-      const int nch = num_chunks(p, b);
-      const int y = x - p.item_start[b];
-      const int h = y / nch, c = y % nch;
-      const int g = b * p.hkv + h;
-      if (!vote) {
-        snapkv_score_stats_item<D, RTW>(p, sm.stats, b, h, c);
-        publish(&done_stats[g]);
-      } else {
-        wait_count(&done_stats[g], (uint32_t)nch, err);
-        if (c * p.chunk < p.tab.len[b] - p.window) snapkv_score_vote_item<D, RTW>(p, sm.vote, b, h, c);
-        publish(&done_vote[g]);
-      }
-    } else if (t < (uint32_t)(2 * ns + heads)) {
-      const int g = (int)t - 2 * ns;
-      const int b = g / p.hkv, h = g % p.hkv;
-      if (p.tab.len[b] > p.budget) {
-        wait_count(&done_vote[g], (uint32_t)num_chunks(p, b), err);
-        snapkv_topk_item(p, sm.select, b, h);
-        publish(&done_select[g]);
-      }
-    } else {
-      const int x = (int)t - 2 * ns - heads;
-      const int g = x / p.n_gather_blocks, rb = x % p.n_gather_blocks;
-      const int b = g / p.hkv, h = g % p.hkv;
-      if (p.tab.len[b] > p.budget) wait_count(&done_select[g], 1u, err);
-      snapkv_gather_item<D>(p, b, h, rb);
-    }
-  }
-
-  // the last workgroup out zeroes the counters (not the error word)
-  if (threadIdx.x == 0)
-    s_last = __hip_atomic_fetch_add(p.sync + kSyncExit, 1u, __ATOMIC_ACQ_REL,
-                                    __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
-  __syncthreads();
-  if (s_last) {
-    const int words = kSyncHeads + 3 * heads;
-    for (int i = threadIdx.x; i < words; i += kThreads)
-      if (i != kSyncError) __hip_atomic_store(p.sync + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
 }
 
 template <typename F>
@@ -204,8 +91,7 @@ int row_tiles_per_wave(const PathParams& p) {
 hipError_t launch_score_stats(const PathParams& p, int head_dim, hipStream_t stream) {
   return dispatch_dim_rtw(head_dim, row_tiles_per_wave(p), [&](auto d, auto rtw) {
     hipLaunchKernelGGL((snapkv_score_stats<decltype(d)::value, decltype(rtw)::value>),
-                       dim3(p.nchunk, p.hkv, p.batch),
-                       dim3(kThreads), 0, stream, p);
+                       dim3(p.nchunk, p.hkv, p.batch), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
   });
 }
@@ -213,43 +99,19 @@ hipError_t launch_score_stats(const PathParams& p, int head_dim, hipStream_t str
 hipError_t launch_score_vote(const PathParams& p, int head_dim, hipStream_t stream) {
   return dispatch_dim_rtw(head_dim, row_tiles_per_wave(p), [&](auto d, auto rtw) {
     hipLaunchKernelGGL((snapkv_score_vote<decltype(d)::value, decltype(rtw)::value>),
-                       dim3(p.nchunk, p.hkv, p.batch),
-                       dim3(kThreads), 0, stream, p);
+                       dim3(p.nchunk, p.hkv, p.batch), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
   });
 }
 
-hipError_t launch_pool(const PathParams& p, hipStream_t stream) {
-  const dim3 grid((p.pooled_stride + kPoolTile - 1) / kPoolTile, p.hkv, p.batch);
-  hipLaunchKernelGGL(snapkv_pool, grid, dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_topk(const PathParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(snapkv_topk, dim3(p.hkv, p.batch), dim3(kThreads), 0, stream, p);
+hipError_t launch_select(const PathParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(snapkv_select, dim3(p.hkv, p.batch), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_gather(const PathParams& p, int head_dim, hipStream_t stream) {
   return dispatch_dim(head_dim, [&](auto d) {
     hipLaunchKernelGGL(snapkv_gather<decltype(d)::value>, dim3(p.n_gather_blocks, p.hkv, p.batch),
-                       dim3(kThreads), 0, stream, p);
-    return hipGetLastError();
-  });
-}
-
-hipError_t persistent_blocks_per_cu(int head_dim, int rtw, int* blocks) {
-  return dispatch_dim_rtw(head_dim, rtw, [&](auto d, auto r) {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        blocks, snapkv_compress_persistent<decltype(d)::value, decltype(r)::value>, kThreads, 0);
-  });
-}
-
-hipError_t launch_persistent(const PathParams& p, int head_dim, int workgroups,
-                             hipStream_t stream) {
-  return dispatch_dim_rtw(head_dim, row_tiles_per_wave(p), [&](auto d, auto rtw) {
-    hipLaunchKernelGGL((snapkv_compress_persistent<decltype(d)::value, decltype(rtw)::value>),
-                       dim3(workgroups),
                        dim3(kThreads), 0, stream, p);
     return hipGetLastError();
   });

@@ -21,6 +21,11 @@
 //        across the two lane halves and the row-tile waves through LDS).
 // Keys stream through two 128-key LDS tiles with two more tiles in flight in
 // registers; the group's query rows stay in VGPRs as MFMA operands.
+//
+// snapkv_pool is fused into the vote item: the item also computes the votes
+// of the r = k/2 keys beyond each end of its chunk (the same values the
+// neighbouring items compute: same keys, same operation order), pools its
+// own positions from LDS and writes only pooled scores.
 // All reductions run in a fixed order, so results are bitwise reproducible
 // and independent of which workgroup runs an item.
 #pragma once
@@ -40,7 +45,7 @@ struct alignas(16) VoteSmem {
   unsigned char ring[2][KTile<D>::BYTES];
   float lse[kMaxRows];
   float vred[2][kWaves][KTile<D>::KEYS];
-  float s_chunk[kMaxChunk];
+  float s_chunk[kMaxChunk + kMaxKernel];  // the chunk plus its pooling halo
 };
 
 // Which row tiles and key blocks a wave owns: waves split the row tiles
@@ -61,9 +66,37 @@ __device__ __forceinline__ WaveRole wave_role(const PathParams& p, int wave) {
   return r;
 }
 
+// Pooled value at position j from an accessor get(u), 0 <= u < P:
+//   avg: (1/k) * sum_{|u-j| <= r} s[u]   (u outside [0, P) adds 0)
+//   max: max_{|u-j| <= r, 0 <= u < P} s[u]
+// with r = k / 2 (glossary page "SnapKV(スナップケーブイ)", section
+// "SnapKVの仕組み", paragraph "Pooling for Robustness"; paper page "SnapKV:
+// LLM Knows What You are Looking for Before Generation", section
+// "기술적 접근법": max or average pooling, kernel 5-13; kernel 1 leaves the
+// scores as they are). The operation order is fixed here, so every kernel
+// that pools produces identical bits.
+template <typename Get>
+__device__ __forceinline__ float pool_value(Get get, int j, int P, int kernel, int mode) {
+  const int r = kernel >> 1;
+  if (mode == 1) {
+    float v = -kInf;
+    for (int e = 0; e < kernel; ++e) {
+      const int u = j - r + e;
+      if (u >= 0 && u < P) v = fmaxf(v, get(u));
+    }
+    return v;
+  }
+  float acc = 0.f;
+  for (int e = 0; e < kernel; ++e) {
+    const int u = j - r + e;
+    if (u >= 0 && u < P) acc += get(u);
+  }
+  return kernel == 1 ? acc : acc * (1.0f / (float)kernel);
+}
+
 // ---------------------------------------------------------------- stats ---
 template <int D, int RTW>
-__device__ void snapkv_score_stats_item(const PathParams& p, StatsSmem<D>& sm, int b, int h,
+__device__ __forceinline__ void snapkv_score_stats_item(const PathParams& p, StatsSmem<D>& sm, int b, int h,
                                         int c) {
   const int L = p.tab.len[b];
   const int P = L - p.window;
@@ -154,12 +187,16 @@ __device__ void snapkv_score_stats_item(const PathParams& p, StatsSmem<D>& sm, i
 
 // ----------------------------------------------------------------- vote ---
 template <int D, int RTW>
-__device__ void snapkv_score_vote_item(const PathParams& p, VoteSmem<D>& sm, int b, int h,
+__device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, VoteSmem<D>& sm, int b, int h,
                                        int c) {
   const int L = p.tab.len[b];
   const int P = L - p.window;
   const int key0 = c * p.chunk;
   const int kend = min(key0 + p.chunk, P);
+  // the votes of r keys on each side are recomputed so this item can pool
+  // its own positions (identical values: same keys, same operation order)
+  const int r = p.kernel >> 1;
+  const int kv0 = max(0, key0 - r), kv1 = min(P, kend + r);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const WaveRole role = wave_role(p, wave);
 
@@ -215,7 +252,7 @@ __device__ void snapkv_score_vote_item(const PathParams& p, VoteSmem<D>& sm, int
   constexpr int KEYS = KTile<D>::KEYS;
   const size_t tstride = (size_t)p.hkv * D;
   const uint16_t* kbase = p.k + ((size_t)p.tab.off[b] * p.hkv + h) * D;
-  const int ntiles = (kend - key0 + KEYS - 1) / KEYS;
+  const int ntiles = (kv1 - kv0 + KEYS - 1) / KEYS;
   // fold tile i's row-tile partials (written before the barrier that
   // precedes tile i + 1) in a fixed order
   auto fold = [&](int i) {
@@ -226,9 +263,9 @@ __device__ void snapkv_score_vote_item(const PathParams& p, VoteSmem<D>& sm, int
     }
   };
   auto compute = [&](const unsigned char* tile, int i) {
-    const int tk0 = key0 + i * KEYS;
+    const int tk0 = kv0 + i * KEYS;
     for (int kb = role.wk; kb < KEYS / 32; kb += role.nwk) {
-      if (tk0 + kb * 32 >= kend) break;
+      if (tk0 + kb * 32 >= kv1) break;
       bf16x8 kf[D / 16];
       read_key_frags<D>(kf, tile, kb, lane);
       float cs = 0.f;
@@ -247,15 +284,18 @@ __device__ void snapkv_score_vote_item(const PathParams& p, VoteSmem<D>& sm, int
       if (lane < 32) sm.vred[i & 1][role.wr][kb * 32 + lane] = cs;
     }
   };
-  stream_key_tiles<D>(kbase, tstride, key0, kend, sm.ring, compute, [&](int i) {
+  stream_key_tiles<D>(kbase, tstride, kv0, kv1, sm.ring, compute, [&](int i) {
     if (i > 0) fold(i - 1);
   });
   __syncthreads();
   fold(ntiles - 1);
   __syncthreads();
-  float* out = p.raw + (size_t)(b * p.hkv + h) * p.p_stride;
-  for (int j = tid; j < kend - key0; j += kThreads) out[key0 + j] = sm.s_chunk[j];
-  __syncthreads();  // LDS is reused by the next item
+  // snapkv_pool, staged in LDS: pooled scores of this item's positions
+  float* pooled = p.pooled + (size_t)(b * p.hkv + h) * p.pooled_stride;
+  for (int j = key0 + tid; j < kend; j += kThreads)
+    pooled[j] = pool_value([&](int u) { return sm.s_chunk[u - kv0]; }, j, P, p.kernel,
+                           p.pool_mode);
+  __syncthreads();  // LDS is reused next
 }
 
 }  // namespace snapkv

@@ -1,106 +1,52 @@
-// snapkv_pool and snapkv_topk: smoothing of a head's vote vector and the
-// per-head selection of the m = B - W best prefix positions, as work items.
+// snapkv_select: per-head selection of the m = B - W best prefix positions
+// (glossary page "SnapKV(スナップケーブイ)", section "SnapKVの仕組み", step 3:
+// the top-budget positions by pooled score are kept; paper page "SnapKV: LLM
+// Knows What You are Looking for Before Generation", abstract: selection is
+// per attention head). Output: the m positions with the largest pooled
+// scores, ties going to the lower position, in ascending order, followed by
+// the window positions P .. L-1.
 //
-// Pooling (glossary page "SnapKV(スナップケーブイ)", section "SnapKVの仕組み",
-// paragraph "Pooling for Robustness"; paper page "SnapKV: LLM Knows What You
-// are Looking for Before Generation", section "기술적 접근법": max or average
-// pooling, kernel 5-13; kernel 1 leaves the scores as they are):
-//   avg: c[j] = (1/k) * sum_{|u-j| <= r} s[u]      (u outside [0, P) adds 0)
-//   max: c[j] = max_{|u-j| <= r, 0 <= u < P} s[u]
-// with r = k / 2. pool_value() fixes the operation order, so every kernel
-// that pools produces identical bits.
-//
-// Selection (glossary page, same section, step 3: keep the top-budget pairs;
-// paper page, abstract: per attention head): the m largest pooled scores,
-// ties going to the lower position, in ascending order, followed by the
-// window positions P .. L-1. One workgroup per (prompt, head):
-//   * the raw votes are staged in LDS and pooled in place; the pooled values
-//     become order-preserving 32-bit keys (sign flipped for non-negatives,
-//     all bits flipped for negatives); prefixes longer than the LDS cache
-//     spill to global memory;
-//   * a radix select over three digits (11, 11 and 10 bits) finds the m-th
-//     largest key tau and how many keys equal to tau are taken: the first
-//     digit over all keys (LDS atomics merged per wave: lanes sharing a bin
-//     add once), the last two on the keys of the threshold bin only;
-//   * each wave then owns a contiguous segment of positions: per-wave counts
-//     of keys above and equal to tau decide which ties are kept (lowest
-//     positions first) and where each wave writes; within a wave, ballots
-//     and mbcnt prefixes place the kept positions in ascending order.
-// Integer-only decisions on the fp32 bits: exact given the scores.
+// One workgroup per (prompt, head), integer decisions only (exact given the
+// fp32 pooled scores):
+//   * pooled scores become order-preserving 32-bit keys (sign bit set for
+//     non-negatives, all bits flipped for negatives);
+//   * positions are read in slabs of 4 * kThreads: thread t holds positions
+//     4t .. 4t+3 of every slab (one coalesced 16-byte load per slab). Up to
+//     kMaxSlabsHeld slabs (64 keys per thread) stay in registers for the
+//     whole selection; longer prefixes are re-read in batches of that size;
+//   * a radix select over digits of 11, 11 and 10 bits finds tau, the m-th
+//     largest key, and `need`, how many keys equal to tau are kept (the
+//     lowest-positioned ones). Histograms are LDS atomics into kReplicas
+//     copies (lane l adds to copy l % kReplicas, copies 4 banks apart):
+//     scores concentrate in few bins, and lanes that hit the same address
+//     serialise, so the copies bound that to 64 / kReplicas lanes. One wave
+//     sums the copies and finds the bin holding the threshold (row totals,
+//     then a suffix scan over lanes) while the others clear the second
+//     histogram buffer for the next digit;
+//   * ordered compaction: per (slab, wave) counts of keys above and equal to
+//     tau, one exclusive scan of those counts in position order, then within
+//     a wave ballots and mbcnt give every kept position its output slot.
 #pragma once
+
+#include <type_traits>
 
 #include "snapkv_device.h"
 
 namespace snapkv {
 
-constexpr int kBins = 2048;
-constexpr int kCandCap = 4096;
+constexpr int kSlab = 4 * kThreads;  // positions per slab
+constexpr int kMaxSlabsHeld = 16;    // slabs per thread batch: 64 keys in VGPRs
+constexpr int kBins = 2048;          // digits: key bits 31..21, 20..10, 9..0
+constexpr int kReplicas = 8;         // histogram copies
+constexpr int kRepStride = kBins + 4;  // words between copies: 16-byte aligned, 4 banks apart
+constexpr int kHistWords = kReplicas * kRepStride;
 
 struct alignas(16) SelectSmem {
-  uint32_t keys[kSelectLdsKeys];
-  uint32_t hist[kBins];
-  uint32_t cand[kCandCap];
-  uint32_t wsum[2][kWaves];
-  uint32_t sh_bin, sh_need, sh_ncand;
+  uint32_t rep[2][kHistWords];  // two replicated histograms, used by alternate digits
+  uint32_t cnt[kMaxSlabsHeld * kWaves][2];   // per (slab, wave): keys > tau, keys == tau
+  uint32_t base[kMaxSlabsHeld * kWaves][2];  // exclusive prefix of cnt in position order
+  uint32_t sh_bin, sh_need, sh_gt_carry, sh_eq_carry;
 };
-
-// Pooled value at position j from an accessor get(u) for 0 <= u < P.
-template <typename Get>
-__device__ __forceinline__ float pool_value(Get get, int j, int P, int kernel, int mode) {
-  const int r = kernel >> 1;
-  if (mode == 1) {
-    float v = -kInf;
-    for (int e = 0; e < kernel; ++e) {
-      const int u = j - r + e;
-      if (u >= 0 && u < P) v = fmaxf(v, get(u));
-    }
-    return v;
-  }
-  float acc = 0.f;
-  for (int e = 0; e < kernel; ++e) {
-    const int u = j - r + e;
-    if (u >= 0 && u < P) acc += get(u);
-  }
-  return kernel == 1 ? acc : acc * (1.0f / (float)kernel);
-}
-
-// dst[i] = src[i] for i < n (dst in LDS): each thread issues 16 independent
-// global loads before storing any, so the copy costs few memory round trips.
-__device__ __forceinline__ void load_floats(float* dst, const float* src, int n) {
-  constexpr int kBatch = 16;
-  for (int base = 0; base < n; base += kThreads * kBatch) {
-    float v[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int i = base + threadIdx.x + u * kThreads;
-      v[u] = src[min(i, n - 1)];
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int i = base + threadIdx.x + u * kThreads;
-      if (i < n) dst[i] = v[u];
-    }
-  }
-}
-
-// Visit keys j = 0 .. n-1, thread tid taking j = base + tid + u * kThreads:
-// kKeyBatch keys are fetched (from LDS, or from the global spill) before any
-// is processed. f(j, valid, key) runs on every thread for every slot, so it
-// may use wave-wide primitives.
-constexpr int kKeyBatch = 8;
-template <typename Get, typename F>
-__device__ __forceinline__ void for_each_key(int n, Get&& get, F&& f) {
-  for (int base = 0; base < n; base += kThreads * kKeyBatch) {
-    uint32_t key[kKeyBatch];
-#pragma unroll
-    for (int u = 0; u < kKeyBatch; ++u) key[u] = get(min(base + (int)threadIdx.x + u * kThreads, n - 1));
-#pragma unroll
-    for (int u = 0; u < kKeyBatch; ++u) {
-      const int j = base + (int)threadIdx.x + u * kThreads;
-      f(j, j < n, key[u]);
-    }
-  }
-}
 
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
@@ -112,224 +58,294 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Add 1 to hist[bin] for every active lane; lanes sharing a bin are merged
-// into one atomic by their lowest lane (up to 4 rounds, then plain atomics).
-__device__ __forceinline__ void hist_add(uint32_t* hist, bool active, uint32_t bin) {
-  uint64_t pending = __ballot(active);
-  const int lane = threadIdx.x & 63;
-#pragma unroll 1
-  for (int round = 0; round < 4 && pending; ++round) {
-    const int leader = __builtin_ctzll(pending);
-    const uint32_t lbin = __shfl(bin, leader);
-    const uint64_t same = __ballot(active && bin == lbin) & pending;
-    if (lane == leader) atomicAdd(&hist[lbin], (uint32_t)__popcll(same));
-    pending &= ~same;
+// Keys of slabs slab0 .. slab0+NS-1 for this thread. Loads are unconditional
+// (clamped to the float4 group holding position P-1, inside the row since
+// rows are padded to 64 floats) so they all issue before the first use.
+template <int NS>
+__device__ __forceinline__ void load_keys(uint32_t (&key)[NS][4], const float* src, int P,
+                                          int slab0) {
+  const int last = (P - 1) & ~3;
+  float4 v[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int j = (slab0 + s) * kSlab + 4 * (int)threadIdx.x;
+    v[s] = *reinterpret_cast<const float4*>(src + min(j, last));
   }
-  if ((pending >> lane) & 1ull) atomicAdd(&hist[bin], 1u);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    key[s][0] = order_key(v[s].x);
+    key[s][1] = order_key(v[s].y);
+    key[s][2] = order_key(v[s].z);
+    key[s][3] = order_key(v[s].w);
+  }
 }
 
-// Wave 0: the bin holding the need-th largest key among 64*PER bins (bins
-// ordered by value), and the count still needed inside it. Each lane holds
-// PER contiguous bins in registers.
-template <int PER>
-__device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t need, uint32_t* sh_bin,
-                                         uint32_t* sh_need) {
+// Zero histogram buffer h with 16-byte stores, threads first .. kThreads-1.
+__device__ __forceinline__ void clear_hist(uint32_t* h, int first) {
+  u32x4* h4 = reinterpret_cast<u32x4*>(h);
+  for (int i = (int)threadIdx.x - first; i < kHistWords / 4; i += kThreads - first)
+    h4[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+// Wave 0 only: the bin of replicated histogram h holding the need-th largest
+// key (bins ordered by value, the largest last) -> *sh_bin, and how many keys
+// of that bin are still needed -> *sh_need. Requires 1 <= need <= total.
+// Lane l sums the copies of bins 256 i + 4 l .. +3 for rows i = 0..7 (reads
+// of consecutive 16-byte words, conflict-free); the row holding the
+// threshold comes from the wave-wide row totals, then a suffix scan over
+// the lanes of that row finds the bin.
+__device__ __forceinline__ void find_bin_wave(const uint32_t* h, uint32_t need, uint32_t* sh_bin,
+                                              uint32_t* sh_need) {
   const int lane = threadIdx.x & 63;
-  uint32_t c[PER];
-  const uint4* h4 = reinterpret_cast<const uint4*>(hist + lane * PER);
+  uint32_t c[8][4];
 #pragma unroll
-  for (int i = 0; i < PER / 4; ++i) {
-    const uint4 q = h4[i];
-    c[4 * i] = q.x;
-    c[4 * i + 1] = q.y;
-    c[4 * i + 2] = q.z;
-    c[4 * i + 3] = q.w;
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c[i][e] = 0u;
+#pragma unroll
+  for (int r = 0; r < kReplicas; ++r) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(h + r * kRepStride + 256 * i + 4 * lane);
+      c[i][0] += x[0];
+      c[i][1] += x[1];
+      c[i][2] += x[2];
+      c[i][3] += x[3];
+    }
   }
-  uint32_t local = 0;
+  uint32_t rs[8];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) local += c[i];
-  uint32_t incl = local;  // sum over lanes >= this lane
+  for (int i = 0; i < 8; ++i) rs[i] = wave_sum(c[i][0] + c[i][1] + c[i][2] + c[i][3]);
+  // the row from the top whose keys reach `need` (uniform over the wave)
+  uint32_t above = 0, cr[4] = {0u, 0u, 0u, 0u};
+  int row = 0;
+  bool found = false;
+#pragma unroll
+  for (int i = 7; i >= 0; --i) {
+    if (!found && (above + rs[i] >= need || i == 0)) {
+      found = true;
+      row = i;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cr[e] = c[i][e];
+    } else if (!found) {
+      above += rs[i];
+    }
+  }
+  const uint32_t local = cr[0] + cr[1] + cr[2] + cr[3];
+  uint32_t incl = local;  // sum over lanes >= lane
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const uint32_t y = __shfl_down(incl, off);
     if (lane + off < 64) incl += y;
   }
-  const uint32_t above = incl - local;
-  if (above < need && need <= incl) {
-    uint32_t a = above;
-    int bin = 0;
-    bool found = false;
+  const uint32_t ex = above + incl - local;  // keys in bins above this lane's four
+  if (ex < need && need <= ex + local) {
+    uint32_t a = ex;
+    int e_hit = 0;
+    bool hit = false;
 #pragma unroll
-    for (int i = PER - 1; i >= 0; --i) {
-      if (!found && (a + c[i] >= need || i == 0)) {
-        bin = i;
-        found = true;
-      } else if (!found) {
-        a += c[i];
+    for (int e = 3; e >= 0; --e) {
+      if (!hit && (a + cr[e] >= need || e == 0)) {
+        hit = true;
+        e_hit = e;
+      } else if (!hit) {
+        a += cr[e];
       }
     }
-    *sh_bin = (uint32_t)(lane * PER + bin);
+    *sh_bin = (uint32_t)(256 * row + 4 * lane + e_hit);
     *sh_need = need - a;
   }
 }
 
-// Pool, select and write out_idx for one (prompt, head) with L > budget.
-__device__ void snapkv_topk_item(const PathParams& p, SelectSmem& sm, int b, int h) {
+// Select for one (prompt, head) with L > budget. NS slabs per batch; with
+// RESIDENT the prefix fits in one batch and is loaded once.
+template <int NS, bool RESIDENT>
+__device__ __forceinline__ void select_head(const PathParams& p, SelectSmem& sm, int b, int h) {
   const int L = p.tab.len[b];
   const int P = L - p.window;
   const uint32_t m = (uint32_t)(p.budget - p.window);  // 1 <= m < P
-  const float* raw = p.raw + (size_t)(b * p.hkv + h) * p.p_stride;
-  float* spill = p.pooled + (size_t)(b * p.hkv + h) * p.pooled_stride;
-  int32_t* out = p.out_idx + (size_t)(b * p.hkv + h) * p.budget;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const bool in_lds = P <= kSelectLdsKeys;
+  const size_t head = (size_t)(b * p.hkv + h);
+  const float* src = p.pooled + head * p.pooled_stride;
+  int32_t* out = p.out_idx + head * p.budget;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nbatch = RESIDENT ? 1 : (P + NS * kSlab - 1) / (NS * kSlab);
 
-  // ---- pooled keys. Cached prefixes are pooled in place, kCandCap
-  // positions at a time: a chunk's pooled values are staged in `cand`, the
-  // raw values of its last r positions (the next chunk's left halo) are saved
-  // in `hist`, then the chunk is overwritten with its keys.
-  if (in_lds) {
-    float* vals = reinterpret_cast<float*>(sm.keys);
-    float* staged = reinterpret_cast<float*>(sm.cand);
-    float* halo = reinterpret_cast<float*>(sm.hist);  // r <= kBins raw values
-    const int r = p.kernel >> 1;
-    load_floats(vals, raw, P);
-    __syncthreads();
-    for (int a = 0; a < P; a += kCandCap) {
-      const int e = min(P, a + kCandCap);
-      for (int j = a + tid; j < e; j += kThreads)
-        staged[j - a] = pool_value([&](int u) { return u >= a ? vals[u] : halo[u - (a - r)]; },
-                                   j, P, p.kernel, p.pool_mode);
-      __syncthreads();
-      for (int i = tid; i < r; i += kThreads)
-        if (e - r + i >= 0) halo[i] = vals[e - r + i];
-      __syncthreads();
-      for (int j = a + tid; j < e; j += kThreads) sm.keys[j] = order_key(staged[j - a]);
-      __syncthreads();
-    }
-  } else {
-    // long prefix: pool tile by tile through LDS, keys spill to global
-    float* vals = reinterpret_cast<float*>(sm.keys);
-    const int r = p.kernel >> 1;
-    const int span = kSelectLdsKeys - 2 * r;  // positions pooled per tile
-    for (int a = 0; a < P; a += span) {
-      const int lo = max(0, a - r), hi = min(P, a + span + r);
-      load_floats(vals, raw + lo, hi - lo);
-      __syncthreads();
-      for (int j = a + tid; j < min(P, a + span); j += kThreads)
-        spill[j] = pool_value([&](int u) { return vals[u - lo]; }, j, P, p.kernel, p.pool_mode);
-      __syncthreads();
-    }
+  uint32_t key[NS][4];
+  if (RESIDENT) load_keys<NS>(key, src, P, 0);
+  clear_hist(sm.rep[0], 0);
+  clear_hist(sm.rep[1], 0);
+  if (tid == 0) {
+    sm.sh_gt_carry = 0u;
+    sm.sh_eq_carry = 0u;
   }
-  for (int i = tid; i < kBins; i += kThreads) sm.hist[i] = 0u;
-  if (tid == 0) sm.sh_ncand = 0u;
-  __syncthreads();
-  auto key_at = [&](int j) -> uint32_t { return in_lds ? sm.keys[j] : order_key(spill[j]); };
-
-  // ---- digit 1: bits 31..21 over all keys
-  for_each_key(P, key_at, [&](int, bool valid, uint32_t u) { hist_add(sm.hist, valid, u >> 21); });
-  __syncthreads();
-  if (tid < 64) find_bin<kBins / 64>(sm.hist, m, &sm.sh_bin, &sm.sh_need);
-  __syncthreads();
-  uint32_t prefix = sm.sh_bin << 21;
-  uint32_t need = sm.sh_need;
-  const uint32_t in_bin = sm.hist[sm.sh_bin];
-  const bool use_cand = in_bin <= (uint32_t)kCandCap;
   __syncthreads();
 
-  // ---- the threshold bin's keys (their order is irrelevant for tau)
-  if (use_cand) {
-    for_each_key(P, key_at, [&](int, bool valid, uint32_t u) {
-      const bool hit = valid && (u >> 21) == (prefix >> 21);
-      const uint64_t bal = __ballot(hit);
-      uint32_t base = 0;
-      if (lane == 0 && bal) base = atomicAdd(&sm.sh_ncand, (uint32_t)__popcll(bal));
-      base = __shfl(base, 0);
-      if (hit) sm.cand[base + lanes_below(bal)] = u;
+  // f(jb, keys) over every float4 group of every batch, in batch order:
+  // keys[e] is position jb + e
+  auto visit_groups = [&](auto&& f) {
+    for (int bt = 0; bt < nbatch; ++bt) {
+      if (!RESIDENT) load_keys<NS>(key, src, P, bt * NS);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) f((bt * NS + s) * kSlab + 4 * tid, key[s]);
+    }
+  };
+  // One digit: keys matching the known prefix are counted into histogram
+  // buffer `buf` (copy tid % kReplicas; equal bins within a float4 group add
+  // once), then wave 0 finds the threshold bin while the other waves clear
+  // the other buffer for the next digit.
+  uint32_t prefix = 0u, need = m;
+  auto digit = [&](int buf, int shift, uint32_t dmask, uint32_t pmask, bool clear_other) {
+    uint32_t* h = sm.rep[buf] + (tid % kReplicas) * kRepStride;
+    visit_groups([&](int jb, const uint32_t(&k4)[4]) {
+      uint32_t bin[4];
+      bool ok[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ok[e] = jb + e < P && (k4[e] & pmask) == prefix;
+        bin[e] = (k4[e] >> shift) & dmask;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bool first = ok[e];
+        uint32_t c = 0;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          const bool same = ok[f] && bin[f] == bin[e];
+          if (f < e && same) first = false;
+          if (f >= e && same) ++c;
+        }
+        if (first) atomicAdd(&h[bin[e]], c);
+      }
     });
-  }
-
-  // ---- digits 2 (bits 20..10) and 3 (bits 9..0)
-#pragma unroll 1
-  for (int pass = 0; pass < 2; ++pass) {
-    const int shift = pass == 0 ? 10 : 0;
-    const uint32_t dmask = pass == 0 ? 0x7FFu : 0x3FFu;
-    const uint32_t pmask = pass == 0 ? 0xFFE00000u : 0xFFFFFC00u;
-    for (int i = tid; i < kBins; i += kThreads) sm.hist[i] = 0u;
     __syncthreads();
-    auto visit = [&](int, bool valid, uint32_t u) {
-      hist_add(sm.hist, valid && (u & pmask) == prefix, (u >> shift) & dmask);
-    };
-    if (use_cand)
-      for_each_key((int)in_bin, [&](int j) { return sm.cand[j]; }, visit);
-    else
-      for_each_key(P, key_at, visit);
-    __syncthreads();
-    if (tid < 64) {
-      if (pass == 0)
-        find_bin<2048 / 64>(sm.hist, need, &sm.sh_bin, &sm.sh_need);
-      else
-        find_bin<1024 / 64>(sm.hist, need, &sm.sh_bin, &sm.sh_need);
-    }
+    if (wave == 0)
+      find_bin_wave(sm.rep[buf], need, &sm.sh_bin, &sm.sh_need);
+    else if (clear_other)
+      clear_hist(sm.rep[buf ^ 1], 64);
     __syncthreads();
     prefix |= sm.sh_bin << shift;
     need = sm.sh_need;
-    __syncthreads();  // sh_* and hist are rewritten next pass
-  }
-  const uint32_t tau = prefix;  // the m-th largest key; `need` keys equal to it are kept
+  };
 
-  // ---- compaction: wave w owns one contiguous segment of positions and
-  // walks it 64 at a time (coalesced, conflict-free); ballots count in order
-  const int wave = tid >> 6;
-  const int seg = (P + kWaves * 64 - 1) / (kWaves * 64) * 64;
-  const int s0 = min(P, wave * seg), s1 = min(P, s0 + seg);
-  // each wave visits its segment 64 keys at a time, kKeyBatch steps per fetch
-  auto for_segment = [&](auto&& f) {
-    for (int base = s0; base < s1; base += 64 * kKeyBatch) {
-      uint32_t key[kKeyBatch];
+  // ---- radix select: digits of 11, 11 and 10 bits
+  digit(0, 21, 0x7FFu, 0x00000000u, false);
+  digit(1, 10, 0x7FFu, 0xFFE00000u, true);
+  digit(0, 0, 0x3FFu, 0xFFFFFC00u, false);
+  const uint32_t tau = prefix;  // the m-th largest key
+  // `need`: keys equal to tau that are kept
+
+  // ---- ordered compaction, one batch at a time
+  const int nent = NS * kWaves;
+  for (int bt = 0; bt < nbatch; ++bt) {
+    if (!RESIDENT) load_keys<NS>(key, src, P, bt * NS);
 #pragma unroll
-      for (int u = 0; u < kKeyBatch; ++u) key[u] = key_at(min(base + u * 64 + lane, s1 - 1));
+    for (int s = 0; s < NS; ++s) {
+      const int jb = (bt * NS + s) * kSlab + 4 * tid;
+      uint32_t gt = 0, eq = 0;
 #pragma unroll
-      for (int u = 0; u < kKeyBatch; ++u) {
-        const int j = base + u * 64 + lane;
-        f(j, j < s1, key[u]);
+      for (int e = 0; e < 4; ++e) {
+        const bool valid = jb + e < P;
+        gt += (uint32_t)__popcll(__ballot(valid && key[s][e] > tau));
+        eq += (uint32_t)__popcll(__ballot(valid && key[s][e] == tau));
+      }
+      if (lane == 0) {
+        sm.cnt[s * kWaves + wave][0] = gt;
+        sm.cnt[s * kWaves + wave][1] = eq;
       }
     }
-  };
-  uint32_t w_gt = 0, w_eq = 0;
-  if (s0 < s1) {
-    for_segment([&](int, bool valid, uint32_t u) {
-      w_gt += (uint32_t)__popcll(__ballot(valid && u > tau));
-      w_eq += (uint32_t)__popcll(__ballot(valid && u == tau));
-    });
+    __syncthreads();
+    if (wave == 0) {  // exclusive scan of (gt, eq) over entries (slab-major)
+      const uint32_t cg = sm.sh_gt_carry, cq = sm.sh_eq_carry;
+      const int e0 = 2 * lane, e1 = 2 * lane + 1;
+      const uint32_t g0 = e0 < nent ? sm.cnt[e0][0] : 0u, q0 = e0 < nent ? sm.cnt[e0][1] : 0u;
+      const uint32_t g1 = e1 < nent ? sm.cnt[e1][0] : 0u, q1 = e1 < nent ? sm.cnt[e1][1] : 0u;
+      uint32_t gi = g0 + g1, qi = q0 + q1;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t yg = __shfl_up(gi, off), yq = __shfl_up(qi, off);
+        if (lane >= off) {
+          gi += yg;
+          qi += yq;
+        }
+      }
+      const uint32_t gx = cg + gi - (g0 + g1), qx = cq + qi - (q0 + q1);
+      if (e0 < nent) {
+        sm.base[e0][0] = gx;
+        sm.base[e0][1] = qx;
+      }
+      if (e1 < nent) {
+        sm.base[e1][0] = gx + g0;
+        sm.base[e1][1] = qx + q0;
+      }
+      if (lane == 63) {
+        sm.sh_gt_carry = cg + gi;
+        sm.sh_eq_carry = cq + qi;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int jb = (bt * NS + s) * kSlab + 4 * tid;
+      const uint32_t gt_before = sm.base[s * kWaves + wave][0];
+      const uint32_t eq_before = sm.base[s * kWaves + wave][1];
+      bool gt[4], eq[4];
+      uint64_t beq[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool valid = jb + e < P;
+        gt[e] = valid && key[s][e] > tau;
+        eq[e] = valid && key[s][e] == tau;
+        beq[e] = __ballot(eq[e]);
+      }
+      uint32_t eq_rank = eq_before;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) eq_rank += lanes_below(beq[e]);
+      bool sel[4];
+      uint64_t bsel[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sel[e] = gt[e] || (eq[e] && eq_rank < need);
+        eq_rank += eq[e] ? 1u : 0u;
+        bsel[e] = __ballot(sel[e]);
+      }
+      uint32_t pos = gt_before + min(eq_before, need);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pos += lanes_below(bsel[e]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (sel[e] && pos < m) out[pos] = jb + e;
+        pos += sel[e] ? 1u : 0u;
+      }
+    }
+    __syncthreads();  // cnt / base are rewritten by the next batch
   }
-  if (lane == 0) {
-    sm.wsum[0][wave] = w_gt;
-    sm.wsum[1][wave] = w_eq;
-  }
-  __syncthreads();
-  uint32_t eq_before = 0, pos_base = 0;
-  for (int w = 0; w < wave; ++w) {
-    const uint32_t gt_w = sm.wsum[0][w], eq_w = sm.wsum[1][w];
-    const uint32_t take_w = eq_before >= need ? 0u : min(eq_w, need - eq_before);
-    pos_base += gt_w + take_w;
-    eq_before += eq_w;
-  }
-  uint32_t eq_seen = 0, sel_seen = 0;
-  if (s0 < s1) for_segment([&](int j, bool valid, uint32_t u) {
-    const bool gt = valid && u > tau;
-    const bool eq = valid && u == tau;
-    const uint64_t beq = __ballot(eq);
-    const uint32_t eq_rank = eq_before + eq_seen + lanes_below(beq);
-    const bool sel = gt || (eq && eq_rank < need);
-    const uint64_t bsel = __ballot(sel);
-    const uint32_t pos = pos_base + sel_seen + lanes_below(bsel);
-    if (sel && pos < m) out[pos] = j;
-    eq_seen += (uint32_t)__popcll(beq);
-    sel_seen += (uint32_t)__popcll(bsel);
-  });
   for (int i = tid; i < p.window; i += kThreads) out[m + i] = P + i;
-  __syncthreads();  // LDS is reused by the next item
+}
+
+// Selection of one (prompt, head): the smallest register batch that holds
+// the prefix, or batches of kMaxSlabsHeld slabs re-read for longer prefixes.
+__device__ __forceinline__ void snapkv_select_item(const PathParams& p, SelectSmem& sm, int b,
+                                                   int h) {
+  const int P = p.tab.len[b] - p.window;
+  const int slabs = (P + kSlab - 1) / kSlab;
+  if (slabs <= 1)
+    select_head<1, true>(p, sm, b, h);
+  else if (slabs <= 2)
+    select_head<2, true>(p, sm, b, h);
+  else if (slabs <= 4)
+    select_head<4, true>(p, sm, b, h);
+  else if (slabs <= 8)
+    select_head<8, true>(p, sm, b, h);
+  else if (slabs <= kMaxSlabsHeld)
+    select_head<kMaxSlabsHeld, true>(p, sm, b, h);
+  else
+    select_head<kMaxSlabsHeld, false>(p, sm, b, h);
 }
 
 }  // namespace snapkv

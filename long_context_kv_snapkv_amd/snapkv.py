@@ -170,9 +170,9 @@ def snapkv_compress(q_win: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                     staged: bool = False, stage_events: Optional[Sequence] = None):
     """Compress one layer. Returns (out_k, out_v, out_idx); see include/snapkv.h.
 
-    staged=True (or stage_events given) runs snapkv_compress_staged, one
-    kernel per stage; otherwise the single persistent kernel. A workspace
-    passed in must be zero-filled before its first use (new_workspace)."""
+    staged=True (or stage_events given) runs snapkv_compress_staged, the same
+    kernels with caller events around each stage; otherwise snapkv_compress.
+    A workspace needs no initialisation."""
     lib = load_library()
     _check_tensor("q_win", q_win, 4)
     _check_tensor("k", k, 3)

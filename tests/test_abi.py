@@ -39,7 +39,7 @@ def test_status_strings(lib):
 
 def test_stage_names(lib):
     names = [skv.snapkv_stage_name(i) for i in range(skv.SNAPKV_NUM_STAGES)]
-    assert names == ["snapkv_score_stats", "snapkv_score_vote", "snapkv_topk", "snapkv_gather"]
+    assert names == ["snapkv_score_stats", "snapkv_score_vote", "snapkv_select", "snapkv_gather"]
     assert skv.snapkv_stage_name(-1) is None and skv.snapkv_stage_name(4) is None
 
 
@@ -90,8 +90,8 @@ def test_workspace_size_host_logic(lib):
     small = skv.snapkv_workspace_size(32, 8, 128, [16384], 32)
     big = skv.snapkv_workspace_size(32, 8, 128, [131072], 32)
     assert 0 < small < big
-    # raw + pooled score vectors alone need 2 * 8 heads * P floats
-    assert small >= 2 * 8 * (16384 - 32) * 4
+    # the pooled score vectors alone need 8 heads * P floats
+    assert small >= 8 * (16384 - 32) * 4
     assert skv.snapkv_workspace_size(32, 8, 128, [16384, 100], 32) >= small
     with pytest.raises(skv.SnapKVError) as e:
         skv.snapkv_workspace_size(32, 8, 100, [16384], 32)
