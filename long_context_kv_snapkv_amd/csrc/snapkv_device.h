@@ -38,6 +38,43 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
   m = mx;
 }
 
+// ------------------------------------------------------- selection keys ---
+// Order-preserving 32-bit key of an fp32 score: unsigned comparison of keys
+// orders the scores (sign bit set for non-negatives, all bits flipped for
+// negatives). The top 11 bits are the first radix digit of the selection.
+__device__ __forceinline__ uint32_t order_key(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+constexpr int kTopShift = 21;
+constexpr int kTopBins = kTopHistBins;
+static_assert(kTopBins == 1 << (32 - kTopShift), "top digit");
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Inclusive prefix sum over the lanes of a wave64: DPP row shifts within each
+// 16-lane row, then the row totals (read from lanes 15, 31, 47) are added to
+// the rows above them.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
+  const int row = (int)(threadIdx.x & 63) >> 4;
+  x += (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+  return x;
+}
+
+__device__ __forceinline__ uint32_t wave_total(uint32_t incl_scan) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)incl_scan, 63);
+}
+
 // ---------------------------------------------------------------- waits ----
 // Workgroup barrier for LDS hand-offs that leaves this wave's outstanding
 // global loads (into registers) in flight; this wave's LDS reads and writes

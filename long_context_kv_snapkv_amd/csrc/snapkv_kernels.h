@@ -14,6 +14,7 @@ constexpr int kThreads = 512;      // workgroup size of every kernel
 constexpr int kKeyTile = 64;       // keys per LDS tile
 constexpr int kMaxChunk = 4096;    // keys per scoring work item
 constexpr int kGatherRows = 64;    // compressed rows per gather work item
+constexpr int kTopHistBins = 2048; // bins of the selection's first radix digit
 
 // Per-prompt table passed by value in the kernel arguments.
 struct PromptTable {
@@ -31,6 +32,7 @@ struct PathParams {
   int32_t* out_idx;   // [batch, Hkv, budget]
   float2* part;       // [batch, Hkv, nchunk, rows_pad] per-chunk (max, sum) in log2 units
   float* pooled;      // [batch, Hkv, pooled_stride] pooled scores c_h[j], j < P
+  uint32_t* top_hist;   // [batch * Hkv, kTopHistBins] histogram of the pooled keys' top 11 bits
   int32_t batch, hq, hkv, window, group;
   int32_t rows, rows_pad;  // G*W and its round-up to 32
   int32_t nwr;             // waves that split the row tiles (power of two)

@@ -25,7 +25,9 @@
 // snapkv_pool is fused into the vote item: the item also computes the votes
 // of the r = k/2 keys beyond each end of its chunk (the same values the
 // neighbouring items compute: same keys, same operation order), pools its
-// own positions from LDS and writes only pooled scores.
+// own positions from LDS and writes only pooled scores. It also counts its
+// pooled keys' top 11 bits (the selection's first radix digit) into the
+// head's histogram.
 // All reductions run in a fixed order, so results are bitwise reproducible
 // and independent of which workgroup runs an item.
 #pragma once
@@ -46,6 +48,7 @@ struct alignas(16) VoteSmem {
   float lse[kMaxRows];
   float vred[2][kWaves][KTile<D>::KEYS];
   float s_chunk[kMaxChunk + kMaxKernel];  // the chunk plus its pooling halo
+  uint32_t top[kTopBins];                 // top-digit histogram of this chunk's pooled keys
 };
 
 // Which row tiles and key blocks a wave owns: waves split the row tiles
@@ -173,6 +176,10 @@ __device__ __forceinline__ void snapkv_score_stats_item(const PathParams& p, Sta
   }
   __syncthreads();
   float2* dst = p.part + ((size_t)(b * p.hkv + h) * p.nchunk + c) * p.rows_pad;
+  if (c == 0) {  // the vote items of this head accumulate into it next
+    uint32_t* top = p.top_hist + (size_t)(b * p.hkv + h) * kTopBins;
+    for (int i = tid; i < kTopBins; i += kThreads) top[i] = 0u;
+  }
   for (int r = tid; r < p.rows; r += kThreads) {
     const int rt = r >> 5, owner = rt % role.nwr, t = rt / role.nwr;
     float m = -kInf, s = 0.f;
@@ -199,6 +206,8 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
   const int kv0 = max(0, key0 - r), kv1 = min(P, kend + r);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const WaveRole role = wave_role(p, wave);
+
+  for (int i = tid; i < kTopBins; i += kThreads) sm.top[i] = 0u;
 
   // lse of every row from the per-chunk statistics: `tpr` threads share a
   // row, each merging every tpr-th chunk, then a fixed-order fold in LDS
@@ -291,10 +300,24 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
   fold(ntiles - 1);
   __syncthreads();
   // snapkv_pool, staged in LDS: pooled scores of this item's positions
-  float* pooled = p.pooled + (size_t)(b * p.hkv + h) * p.pooled_stride;
-  for (int j = key0 + tid; j < kend; j += kThreads)
-    pooled[j] = pool_value([&](int u) { return sm.s_chunk[u - kv0]; }, j, P, p.kernel,
-                           p.pool_mode);
+  const size_t head = (size_t)(b * p.hkv + h);
+  float* pooled = p.pooled + head * p.pooled_stride;
+  for (int j = key0 + tid; j < kend; j += kThreads) {
+    const float c_j = pool_value([&](int u) { return sm.s_chunk[u - kv0]; }, j, P, p.kernel,
+                                 p.pool_mode);
+    pooled[j] = c_j;
+    if (!p.export_scores) atomicAdd(&sm.top[order_key(c_j) >> kTopShift], 1u);
+  }
+  if (!p.export_scores) {
+    // the selection's first radix digit: this chunk's counts join the head's
+    // histogram (few distinct bins per chunk, so few global atomics)
+    __syncthreads();
+    uint32_t* top = p.top_hist + head * kTopBins;
+    for (int i = tid; i < kTopBins; i += kThreads) {
+      const uint32_t n = sm.top[i];
+      if (n != 0u) atomicAdd(&top[i], n);
+    }
+  }
   __syncthreads();  // LDS is reused next
 }
 
