@@ -145,64 +145,106 @@ __device__ __forceinline__ void read_key_frags(bf16x8 (&kf)[D / 16], const unsig
 }
 
 // Stream the keys [key0, kend) of one head through two LDS tile buffers,
-// with two more tiles in flight in registers. Tile i is stored to LDS, the
-// loads of tile i + 2 go into the freed registers, a barrier makes tile i
-// visible (and guarantees every wave is done with tile i - 1), then
-// after_barrier(i) and compute(tile, i) run. Global loads stay in flight
-// across the barriers. The loads are unconditional (past the end they re-read
-// key kend - 1) and the loop starts with compute, so every store waits only
-// for its own registers.
-template <int D, typename Compute, typename After>
-__device__ __forceinline__ void stream_key_tiles(const uint16_t* kb, size_t tstride, int key0,
-                                                 int kend, unsigned char (*ring)[KTile<D>::BYTES],
-                                                 Compute&& compute, After&& after_barrier) {
+// with two more tiles in flight in registers. KeyStream::prefetch issues the
+// loads of tile 0 (the caller may do other work while they fly, as long as
+// it does not wait on global loads issued after them); run() then stores
+// tile i to LDS, loads tile i + 2 into the freed registers, and after
+// a barrier that makes tile i visible (and guarantees every wave is done with
+// tile i - 1) calls after_barrier(i) and compute(tile, i). Global loads stay
+// in flight across the barriers. The loads are unconditional (past the end
+// they re-read key kend - 1) and the loop starts with compute, so every store
+// waits only for its own registers.
+template <int D>
+struct KeyStream {
   using T = KTile<D>;
-  const int tid = threadIdx.x;
-  const int ntiles = (kend - key0 + T::KEYS - 1) / T::KEYS;
   typename T::Regs ra, rb;
-  load_key_tile<D>(ra, kb, tstride, key0, kend, tid);
-  asm volatile("" ::: "memory");  // keep tile 0's loads older than tile 1's
-  load_key_tile<D>(rb, kb, tstride, key0 + T::KEYS, kend, tid);
-  store_key_tile<D>(ra, ring[0], tid);
-  load_key_tile<D>(ra, kb, tstride, key0 + 2 * T::KEYS, kend, tid);
-  lds_barrier();
-  after_barrier(0);
-  for (int i = 0;; i += 2) {
-    compute(ring[0], i);
-    if (i + 1 >= ntiles) break;
-    store_key_tile<D>(rb, ring[1], tid);
-    load_key_tile<D>(rb, kb, tstride, key0 + (i + 3) * T::KEYS, kend, tid);
-    lds_barrier();
-    after_barrier(i + 1);
-    compute(ring[1], i + 1);
-    if (i + 2 >= ntiles) break;
-    store_key_tile<D>(ra, ring[0], tid);
-    load_key_tile<D>(ra, kb, tstride, key0 + (i + 4) * T::KEYS, kend, tid);
-    lds_barrier();
-    after_barrier(i + 2);
+  const uint16_t* kb;
+  size_t tstride;
+  int key0, kend;
+
+  // Only tile 0 is requested up front: when every CU starts at once, the
+  // first tile arrives sooner if it does not compete with deeper prefetch.
+  __device__ __forceinline__ void prefetch() {
+    load_key_tile<D>(ra, kb, tstride, key0, kend, threadIdx.x);
   }
-}
+
+  template <typename Compute, typename After>
+  __device__ __forceinline__ void run(unsigned char (*ring)[T::BYTES], Compute&& compute,
+                                      After&& after_barrier) {
+    const int tid = threadIdx.x;
+    const int ntiles = (kend - key0 + T::KEYS - 1) / T::KEYS;
+    store_key_tile<D>(ra, ring[0], tid);
+    load_key_tile<D>(rb, kb, tstride, key0 + T::KEYS, kend, tid);
+    asm volatile("" ::: "memory");  // keep tile 1's loads older than tile 2's
+    load_key_tile<D>(ra, kb, tstride, key0 + 2 * T::KEYS, kend, tid);
+    lds_barrier();
+    after_barrier(0);
+    for (int i = 0;; i += 2) {
+      compute(ring[0], i);
+      if (i + 1 >= ntiles) break;
+      store_key_tile<D>(rb, ring[1], tid);
+      load_key_tile<D>(rb, kb, tstride, key0 + (i + 3) * T::KEYS, kend, tid);
+      lds_barrier();
+      after_barrier(i + 1);
+      compute(ring[1], i + 1);
+      if (i + 2 >= ntiles) break;
+      store_key_tile<D>(ra, ring[0], tid);
+      load_key_tile<D>(ra, kb, tstride, key0 + (i + 4) * T::KEYS, kend, tid);
+      lds_barrier();
+      after_barrier(i + 2);
+    }
+  }
+};
 
 // Query fragments of this wave's row tiles (same D-to-k-slot map as the
-// keys); rows at or beyond `rows` are zero.
-template <int D, int RTW>
-__device__ __forceinline__ void load_query_frags(bf16x8 (&qf)[RTW][D / 16],
-                                                 const uint16_t* qbase, int rows, int wr,
-                                                 int nwr, int my_nrt, int lane) {
+// keys), staged through LDS: the group's rows (contiguous in q_win) are read
+// with whole-row coalesced loads, 128 rows per round, into `buf` laid out
+// like a key tile, and each wave reads its row tiles' fragments from there.
+// Rows at or beyond `rows` are zero. issue_next() runs right after the first
+// round's loads are issued (the caller starts its key prefetch there: those
+// loads are younger, so waiting for the query rows does not wait for them).
+// Ends with a barrier after which `buf` may be reused.
+template <int D, int RTW, typename Next>
+__device__ __forceinline__ void stage_query_frags(bf16x8 (&qf)[RTW][D / 16], const uint16_t* qbase,
+                                                  int rows, int rows_pad, int wr, int nwr,
+                                                  int my_nrt, unsigned char* buf, Next&& issue_next) {
+  using T = KTile<D>;
+  constexpr int PIECES = T::PIECES;                 // 16-byte pieces per row
+  constexpr int PER = T::KEYS * PIECES / kThreads;  // pieces per thread per round
+  const int tid = threadIdx.x, lane = tid & 63;
 #pragma unroll
-  for (int t = 0; t < RTW; ++t) {
-    const int r = (wr + nwr * t) * 32 + (lane & 31);
-    const bool ok = t < my_nrt && r < rows;
-    // unconditional load of a valid row, zeroed when out of range: no branch
-    // around the loads keeps the compiler's count of pending loads exact
-    const uint16_t* src = qbase + (size_t)min(r, rows - 1) * D + (lane >> 5) * 8;
+  for (int t = 0; t < RTW; ++t)
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      u32x4 x = *reinterpret_cast<const u32x4*>(src + s * 16);
-      const uint32_t keep = ok ? 0xFFFFFFFFu : 0u;
-      x &= u32x4{keep, keep, keep, keep};
-      qf[t][s] = as_bf16x8(x);
+    for (int s = 0; s < D / 16; ++s) qf[t][s] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  for (int r0 = 0; r0 < rows_pad; r0 += T::KEYS) {
+    u32x4 x[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int piece = tid + u * kThreads;
+      const int row = r0 + piece / PIECES;
+      x[u] = *reinterpret_cast<const u32x4*>(qbase + (size_t)min(row, rows - 1) * D +
+                                             (piece % PIECES) * 8);
     }
+    if (r0 == 0) {
+      asm volatile("" ::: "memory");  // the query loads stay older than the caller's
+      issue_next();
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int piece = tid + u * kThreads;
+      const int row = piece / PIECES;
+      const uint32_t keep = r0 + row < rows ? 0xFFFFFFFFu : 0u;
+      *reinterpret_cast<u32x4*>(buf + row * T::ROWB + (piece % PIECES) * 16) =
+          x[u] & u32x4{keep, keep, keep, keep};
+    }
+    lds_barrier();
+#pragma unroll
+    for (int t = 0; t < RTW; ++t) {
+      const int rt = wr + nwr * t;  // row tile of this wave
+      const int local = rt - r0 / 32;
+      if (t < my_nrt && local >= 0 && local < T::KEYS / 32) read_key_frags<D>(qf[t], buf, local, lane);
+    }
+    lds_barrier();
   }
 }
 

@@ -46,7 +46,7 @@ template <int D>
 struct alignas(16) VoteSmem {
   unsigned char ring[2][KTile<D>::BYTES];
   float lse[kMaxRows];
-  float vred[2][kWaves][KTile<D>::KEYS];
+  float vred[2][2 * kWaves][KTile<D>::KEYS];  // per (row-tile wave, lane half)
   float s_chunk[kMaxChunk + kMaxKernel];  // the chunk plus its pooling halo
   uint32_t top[kTopBins];                 // top-digit histogram of this chunk's pooled keys
 };
@@ -97,10 +97,29 @@ __device__ __forceinline__ float pool_value(Get get, int j, int P, int kernel, i
   return kernel == 1 ? acc : acc * (1.0f / (float)kernel);
 }
 
+// The MFMA chains of a group are all issued before the softmax arithmetic
+// that consumes them, so the matrix core works on the later chains while
+// the VALU works on the first: with one row tile per wave a group is two of
+// the wave's key blocks, with two row tiles it is one key block (two chains
+// either way, within the register budget).
+template <int RTW>
+struct KeyGroup {
+  static constexpr int G = RTW == 1 ? 2 : 1;  // key blocks per group
+  int kb[G];
+  bool has[G];
+  __device__ __forceinline__ KeyGroup(int kb0, int nwk, int tk0, int kend, int keys) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      kb[g] = kb0 + g * nwk;
+      has[g] = g == 0 || (kb[g] < keys / 32 && tk0 + kb[g] * 32 < kend);
+    }
+  }
+};
+
 // ---------------------------------------------------------------- stats ---
 template <int D, int RTW>
-__device__ __forceinline__ void snapkv_score_stats_item(const PathParams& p, StatsSmem<D>& sm, int b, int h,
-                                        int c) {
+__device__ __forceinline__ void snapkv_score_stats_item(const PathParams& p, StatsSmem<D>& sm,
+                                                        int b, int h, int c) {
   const int L = p.tab.len[b];
   const int P = L - p.window;
   const int key0 = c * p.chunk;
@@ -109,9 +128,11 @@ __device__ __forceinline__ void snapkv_score_stats_item(const PathParams& p, Sta
   const WaveRole role = wave_role(p, wave);
 
   bf16x8 qf[RTW][D / 16];
-  const uint16_t* qbase = p.q + (size_t)(b * p.hq + h * p.group) * p.window * D;
-  load_query_frags<D, RTW>(qf, qbase, p.rows, role.wr, role.nwr, role.my_nrt, lane);
-  asm volatile("" ::: "memory");  // query loads stay older than the key-tile loads
+  KeyStream<D> ks{{}, {}, p.k + ((size_t)p.tab.off[b] * p.hkv + h) * D, (size_t)p.hkv * D,
+                  key0, kend};
+  stage_query_frags<D, RTW>(qf, p.q + (size_t)(b * p.hq + h * p.group) * p.window * D, p.rows,
+                            p.rows_pad, role.wr, role.nwr, role.my_nrt, sm.ring[1],
+                            [&] { ks.prefetch(); });
 
   int lim[RTW];  // last key visible to this lane's row
   float mrun[RTW], srun[RTW];
@@ -125,46 +146,103 @@ __device__ __forceinline__ void snapkv_score_stats_item(const PathParams& p, Sta
   const float scale = p.scale_log2;
   const int full_end = min(P, kend);  // keys below this are visible to every row
 
-  const size_t tstride = (size_t)p.hkv * D;
-  const uint16_t* kbase = p.k + ((size_t)p.tab.off[b] * p.hkv + h) * D;
+  // online (max, sum) update of row tile t with block logits acc (keys bk0 + m)
+  auto update = [&](f32x16 acc, int t, int bk0) {
+    if (bk0 + 32 > full_end) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int j = bk0 + acc_row(v, lane);
+        if (j > lim[t] || j >= kend) acc[v] = -kInf;
+      }
+    }
+    float mx = -kInf;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, acc[v]);
+    const float mnew = fmaxf(mrun[t], mx * scale);
+    if (mnew != -kInf) {
+      float sum = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sum += exp2_fast(fmaf(acc[v], scale, -mnew));
+      srun[t] = srun[t] * exp2_fast(mrun[t] - mnew) + sum;
+      mrun[t] = mnew;
+    }
+  };
+  // the same update for a block every row sees in full, without branches
+  // (an all -inf block leaves the state unchanged), so it can be interleaved
+  // with the MFMA chain of the next block
+  auto update_full = [&](const f32x16& acc, int t) {
+    float mx0 = fmaxf(acc[0], acc[1]), mx1 = fmaxf(acc[2], acc[3]);
+#pragma unroll
+    for (int v = 4; v < 16; v += 4) {
+      mx0 = fmaxf(mx0, fmaxf(acc[v], acc[v + 1]));
+      mx1 = fmaxf(mx1, fmaxf(acc[v + 2], acc[v + 3]));
+    }
+    const float mnew = fmaxf(mrun[t], fmaxf(mx0, mx1) * scale);
+    const float mref = mnew == -kInf ? 0.f : mnew;
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; v += 2) {
+      s0 += exp2_fast(fmaf(acc[v], scale, -mref));
+      s1 += exp2_fast(fmaf(acc[v + 1], scale, -mref));
+    }
+    srun[t] = fmaf(srun[t], exp2_fast(mrun[t] - mref), s0 + s1);
+    mrun[t] = mnew;
+  };
+  // Software pipeline over this wave's key blocks: the MFMA chains of block
+  // n are issued, then the softmax update of block n - 1 runs while they
+  // execute. Tiles whose keys are all visible to every row take this path;
+  // the tile that reaches the window or the chunk end flushes the pending
+  // block and is processed with masking.
+  f32x16 pacc[RTW];
+#pragma unroll
+  for (int t = 0; t < RTW; ++t)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) pacc[t][v] = -kInf;
   auto compute = [&](const unsigned char* tile, int i) {
     const int tk0 = key0 + i * KTile<D>::KEYS;
-    for (int kb = role.wk; kb < KTile<D>::KEYS / 32; kb += role.nwk) {
-      const int bk0 = tk0 + kb * 32;
-      if (bk0 >= kend) break;
-      bf16x8 kf[D / 16];
-      read_key_frags<D>(kf, tile, kb, lane);
-      const bool full = bk0 + 32 <= full_end;
+    if (tk0 + KTile<D>::KEYS <= full_end) {
+      for (int kb = role.wk; kb < KTile<D>::KEYS / 32; kb += role.nwk) {
+        bf16x8 kf[D / 16];
+        read_key_frags<D>(kf, tile, kb, lane);
+        f32x16 acc[RTW];
+#pragma unroll
+        for (int t = 0; t < RTW; ++t) {
+          acc[t] = f32x16{};
+#pragma unroll
+          for (int s = 0; s < D / 16; ++s)
+            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[t][s], acc[t], 0, 0, 0);
+        }
+#pragma unroll
+        for (int t = 0; t < RTW; ++t) update_full(pacc[t], t);
+#pragma unroll
+        for (int t = 0; t < RTW; ++t) pacc[t] = acc[t];
+      }
+    } else {
 #pragma unroll
       for (int t = 0; t < RTW; ++t) {
-        if (t >= role.my_nrt) break;
-        f32x16 acc = {};
+        update_full(pacc[t], t);
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[t][s], acc, 0, 0, 0);
-        // acc[v]: logit of key bk0 + acc_row(v, lane) for this lane's row
-        if (!full) {
+        for (int v = 0; v < 16; ++v) pacc[t][v] = -kInf;
+      }
+      for (int kb = role.wk; kb < KTile<D>::KEYS / 32; kb += role.nwk) {
+        const int bk0 = tk0 + kb * 32;
+        if (bk0 >= kend) break;
+        bf16x8 kf[D / 16];
+        read_key_frags<D>(kf, tile, kb, lane);
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int j = bk0 + acc_row(v, lane);
-            if (j > lim[t] || j >= kend) acc[v] = -kInf;
-          }
-        }
-        float mx = -kInf;
+        for (int t = 0; t < RTW; ++t) {
+          f32x16 acc = {};
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, acc[v]);
-        const float mnew = fmaxf(mrun[t], mx * scale);
-        if (mnew != -kInf) {
-          float sum = 0.f;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) sum += exp2_fast(fmaf(acc[v], scale, -mnew));
-          srun[t] = srun[t] * exp2_fast(mrun[t] - mnew) + sum;
-          mrun[t] = mnew;
+          for (int s = 0; s < D / 16; ++s)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[t][s], acc, 0, 0, 0);
+          update(acc, t, bk0);
         }
       }
     }
   };
-  stream_key_tiles<D>(kbase, tstride, key0, kend, sm.ring, compute, [](int) {});
+  ks.run(sm.ring, compute, [](int) {});
+#pragma unroll
+  for (int t = 0; t < RTW; ++t) update_full(pacc[t], t);
 
   // lanes l and l^32 hold the same row over different keys
 #pragma unroll
@@ -189,13 +267,18 @@ __device__ __forceinline__ void snapkv_score_stats_item(const PathParams& p, Sta
     }
     dst[r] = make_float2(m, s);
   }
-  __syncthreads();  // LDS is reused by the next item
 }
 
 // ----------------------------------------------------------------- vote ---
+// Loads are issued in the order the item needs them to be complete: first
+// the per-chunk statistics (the first kPartBatch per thread), then the
+// query rows and the first key tile. The lse merge then waits only for the
+// statistics while the rest is still in flight.
+constexpr int kPartBatch = 8;
+
 template <int D, int RTW>
-__device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, VoteSmem<D>& sm, int b, int h,
-                                       int c) {
+__device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, VoteSmem<D>& sm,
+                                                       int b, int h, int c) {
   const int L = p.tab.len[b];
   const int P = L - p.window;
   const int key0 = c * p.chunk;
@@ -207,32 +290,48 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const WaveRole role = wave_role(p, wave);
 
-  for (int i = tid; i < kTopBins; i += kThreads) sm.top[i] = 0u;
+  // statistics of row `row`, chunks sub, sub + tpr, ...: the first batch
+  const int nch = (L + p.chunk - 1) / p.chunk;
+  const float2* part = p.part + (size_t)(b * p.hkv + h) * p.nchunk * p.rows_pad;
+  int tpr = 1;
+  while (tpr * 2 * p.rows_pad <= kThreads) tpr *= 2;
+  const int span = kThreads / tpr;  // rows per round (>= rows_pad)
+  const int row = tid % span, sub = tid / span;
+  const bool row_ok = row < p.rows;
+  const int row_c = min(row, p.rows - 1);
+  float2 pe[kPartBatch];
+#pragma unroll
+  for (int u = 0; u < kPartBatch; ++u)
+    pe[u] = part[(size_t)min(sub + u * tpr, nch - 1) * p.rows_pad + row_c];
+  asm volatile("" ::: "memory");  // statistics loads stay older than the rest
 
-  // lse of every row from the per-chunk statistics: `tpr` threads share a
-  // row, each merging every tpr-th chunk, then a fixed-order fold in LDS
+  bf16x8 qf[RTW][D / 16];
+  KeyStream<D> ks{{}, {}, p.k + ((size_t)p.tab.off[b] * p.hkv + h) * D, (size_t)p.hkv * D,
+                  kv0, kv1};
+  stage_query_frags<D, RTW>(qf, p.q + (size_t)(b * p.hq + h * p.group) * p.window * D, p.rows,
+                            p.rows_pad, role.wr, role.nwr, role.my_nrt, sm.ring[1],
+                            [&] { ks.prefetch(); });
+
+  for (int i = tid; i < kTopBins; i += kThreads) sm.top[i] = 0u;
+  // lse of every row: `tpr` threads share a row, each merging every tpr-th
+  // chunk (max first, then the rescaled sum), then a fixed-order fold in LDS
   {
-    const int nch = (L + p.chunk - 1) / p.chunk;
-    const float2* part = p.part + (size_t)(b * p.hkv + h) * p.nchunk * p.rows_pad;
-    float2* scratch = reinterpret_cast<float2*>(&sm.vred[0][0][0]);  // kThreads float2
-    int tpr = 1;
-    while (tpr * 2 * p.rows_pad <= kThreads) tpr *= 2;
-    const int span = kThreads / tpr;  // rows per round (>= rows_pad)
-    const int r = tid % span, sub = tid / span;
     float m = -kInf, s = 0.f;
-    if (r < p.rows) {
-#pragma unroll 4
-      for (int cc = sub; cc < nch; cc += tpr) m = fmaxf(m, part[(size_t)cc * p.rows_pad + r].x);
-      if (m != -kInf) {  // a chunk subset may see none of this row's keys
-#pragma unroll 4
-        for (int cc = sub; cc < nch; cc += tpr) {
-          const float2 e = part[(size_t)cc * p.rows_pad + r];
-          s += e.y * exp2_fast(e.x - m);
-        }
-      }
+#pragma unroll
+    for (int u = 0; u < kPartBatch; ++u)
+      if (sub + u * tpr < nch) m = fmaxf(m, pe[u].x);
+    if (m != -kInf) {  // a chunk subset may see none of this row's keys
+#pragma unroll
+      for (int u = 0; u < kPartBatch; ++u)
+        if (sub + u * tpr < nch) s += pe[u].y * exp2_fast(pe[u].x - m);
     }
-    scratch[tid] = make_float2(m, s);
-    __syncthreads();
+    for (int cc = sub + kPartBatch * tpr; cc < nch; cc += tpr) {  // long prompts only
+      const float2 e = part[(size_t)cc * p.rows_pad + row_c];
+      lse_merge(m, s, e.x, e.y);
+    }
+    float2* scratch = reinterpret_cast<float2*>(&sm.vred[0][0][0]);  // kThreads float2
+    scratch[tid] = row_ok ? make_float2(m, s) : make_float2(-kInf, 0.f);
+    lds_barrier();
     if (tid < p.rows_pad) {
       float mm = -kInf, ss = 0.f;
       for (int q = 0; q < tpr; ++q) {
@@ -241,13 +340,8 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
       }
       sm.lse[tid] = tid < p.rows ? mm + log2f(ss) : kInf;  // padded rows add 0
     }
-    __syncthreads();
+    lds_barrier();
   }
-
-  bf16x8 qf[RTW][D / 16];
-  const uint16_t* qbase = p.q + (size_t)(b * p.hq + h * p.group) * p.window * D;
-  load_query_frags<D, RTW>(qf, qbase, p.rows, role.wr, role.nwr, role.my_nrt, lane);
-  asm volatile("" ::: "memory");  // query loads stay older than the key-tile loads
   float lr[RTW][16];
 #pragma unroll
   for (int t = 0; t < RTW; ++t) {
@@ -259,41 +353,60 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
   const float scale = p.scale_log2;
 
   constexpr int KEYS = KTile<D>::KEYS;
-  const size_t tstride = (size_t)p.hkv * D;
-  const uint16_t* kbase = p.k + ((size_t)p.tab.off[b] * p.hkv + h) * D;
   const int ntiles = (kv1 - kv0 + KEYS - 1) / KEYS;
-  // fold tile i's row-tile partials (written before the barrier that
-  // precedes tile i + 1) in a fixed order
+  const int nparts = 2 * role.nwr;  // (row-tile wave, lane half) partial sums per key
+  // fold tile i's partials (written before the barrier that precedes tile
+  // i + 1) in a fixed order
   auto fold = [&](int i) {
     for (int kk = tid; kk < KEYS; kk += kThreads) {
       float s = 0.f;
-      for (int q = 0; q < role.nwr; ++q) s += sm.vred[i & 1][q][kk];
+      for (int q = 0; q < nparts; ++q) s += sm.vred[i & 1][q][kk];
       sm.s_chunk[i * KEYS + kk] = s;
     }
   };
+  // column sums over this wave's rows of block kb (keys tk0 + kb*32 + lane%32):
+  // lanes l and l + 32 hold different rows of the same key, so each half
+  // writes its own partial
+  auto colsum = [&](const f32x16(&acc)[RTW]) {
+    float cs = 0.f;
+#pragma unroll
+    for (int t = 0; t < RTW; ++t) {
+      if (t >= role.my_nrt) break;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) cs += exp2_fast(fmaf(acc[t][v], scale, -lr[t][v]));
+    }
+    return cs;
+  };
   auto compute = [&](const unsigned char* tile, int i) {
     const int tk0 = kv0 + i * KEYS;
-    for (int kb = role.wk; kb < KEYS / 32; kb += role.nwk) {
+    float* vr = &sm.vred[i & 1][2 * role.wr + (lane >> 5)][lane & 31];
+    for (int kb = role.wk; kb < KEYS / 32; kb += KeyGroup<RTW>::G * role.nwk) {
       if (tk0 + kb * 32 >= kv1) break;
-      bf16x8 kf[D / 16];
-      read_key_frags<D>(kf, tile, kb, lane);
-      float cs = 0.f;
+      KeyGroup<RTW> grp(kb, role.nwk, tk0, kv1, KEYS);
+      bf16x8 kf[KeyGroup<RTW>::G][D / 16];
+      f32x16 acc[KeyGroup<RTW>::G][RTW];
 #pragma unroll
-      for (int t = 0; t < RTW; ++t) {
-        if (t >= role.my_nrt) break;
-        f32x16 acc = {};
+      for (int g = 0; g < KeyGroup<RTW>::G; ++g)
+        if (grp.has[g]) read_key_frags<D>(kf[g], tile, grp.kb[g], lane);
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[t][s], kf[s], acc, 0, 0, 0);
-        // acc[v]: logit of row acc_row(v, lane) for key tk0 + kb*32 + (lane & 31)
+      for (int g = 0; g < KeyGroup<RTW>::G; ++g) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) cs += exp2_fast(fmaf(acc[v], scale, -lr[t][v]));
+        for (int t = 0; t < RTW; ++t) {
+          acc[g][t] = f32x16{};
+          if (grp.has[g] && t < role.my_nrt) {
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s)
+              acc[g][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[t][s], kf[g][s], acc[g][t], 0, 0, 0);
+          }
+        }
       }
-      cs += __shfl_xor(cs, 32);
-      if (lane < 32) sm.vred[i & 1][role.wr][kb * 32 + lane] = cs;
+      // acc[g][t][v]: logit of row acc_row(v, lane) of row tile t for this lane's key
+#pragma unroll
+      for (int g = 0; g < KeyGroup<RTW>::G; ++g)
+        if (grp.has[g]) vr[grp.kb[g] * 32] = colsum(acc[g]);
     }
   };
-  stream_key_tiles<D>(kbase, tstride, kv0, kv1, sm.ring, compute, [&](int i) {
+  ks.run(sm.ring, compute, [&](int i) {
     if (i > 0) fold(i - 1);
   });
   __syncthreads();
@@ -310,15 +423,15 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
   }
   if (!p.export_scores) {
     // the selection's first radix digit: this chunk's counts join the head's
-    // histogram (few distinct bins per chunk, so few global atomics)
-    __syncthreads();
+    // histogram (few distinct bins per chunk, so few global atomics); the
+    // barrier covers LDS only, the pooled stores need not have landed
+    lds_barrier();
     uint32_t* top = p.top_hist + head * kTopBins;
     for (int i = tid; i < kTopBins; i += kThreads) {
       const uint32_t n = sm.top[i];
       if (n != 0u) atomicAdd(&top[i], n);
     }
   }
-  __syncthreads();  // LDS is reused next
 }
 
 }  // namespace snapkv

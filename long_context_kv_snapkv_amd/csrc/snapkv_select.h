@@ -20,15 +20,16 @@
 //     later digit counts the keys that match the known prefix into kReplicas
 //     LDS copies (lane l adds to copy l % kReplicas, copies 4 banks apart):
 //     scores concentrate in few bins and lanes that hit one address
-//     serialise, so the copies bound that to 64 / kReplicas lanes. One wave
-//     sums the copies and finds the bin holding the m-th largest key. When
-//     every key of that bin is needed the threshold is settled at that
-//     digit: the kept keys are exactly those >= the bin's lowest key;
-//   * ordered compaction: per (slab, wave) counts of kept keys, one
-//     exclusive scan of those counts in position order, then within a wave
-//     ballots and mbcnt give every kept position its output slot. Only if
-//     the last digit leaves a bin of equal keys of which some are kept are
-//     the lowest-positioned ones of them taken (tie path).
+//     serialise, so the copies bound that to 64 / kReplicas lanes. Each wave
+//     sums the copies of one histogram row and the bin holding the m-th
+//     largest key is found from the row totals. When every key of that bin
+//     is needed the threshold is settled at that digit: the kept keys are
+//     exactly those >= the bin's lowest key;
+//   * ordered compaction: per-slab wave scans of packed (above, equal)
+//     counts and one exclusive scan of the per-(slab, wave) totals give
+//     every kept position its output slot. Only if the last digit leaves a
+//     bin of equal keys of which some are kept are the lowest-positioned
+//     ones of them taken.
 #pragma once
 
 #include "snapkv_device.h"
@@ -44,8 +45,9 @@ constexpr int kHistWords = kReplicas * kRepStride;
 
 struct alignas(16) SelectSmem {
   uint32_t rep[2][kHistWords];  // replicated histograms of digits 2 and 3
-  uint32_t cnt[kMaxSlabsHeld * kWaves][2];   // per (slab, wave): kept (or > tau), == tau
+  uint32_t cnt[kMaxSlabsHeld * kWaves];      // per (slab, wave): above | equal << 16
   uint32_t base[kMaxSlabsHeld * kWaves][2];  // exclusive prefix of cnt in position order
+  uint32_t rowtot[kWaves];                   // histogram row totals (find)
   uint32_t sh_bin, sh_need, sh_count, sh_carry0, sh_carry1;
 };
 
@@ -80,56 +82,46 @@ __device__ __forceinline__ void clear_hist(uint32_t* h, int first) {
     h4[i] = u32x4{0u, 0u, 0u, 0u};
 }
 
-// Wave 0 only. Given counts(i) = this lane's four bins 256 i + 4 lane .. +3
-// (rows i = 0..7), find the bin holding the need-th largest key (bins
-// ordered by value, the largest last): -> sm.sh_bin, the keys of that bin
-// still needed -> sm.sh_need, and the bin's count -> sm.sh_count. Requires
-// 1 <= need <= total. The row comes from the wave-wide row totals, then a
-// suffix scan over the lanes of that row finds the bin.
+// All waves: the bin holding the need-th largest key (bins ordered by value,
+// the largest last) -> sm.sh_bin, the keys of that bin still needed ->
+// sm.sh_need, and the bin's count -> sm.sh_count. Wave w takes row w (bins
+// 256 w .. 256 w + 255); counts() gives this lane's four bins 256 w + 4 lane
+// .. +3. Row totals are exchanged through LDS; the wave holding the
+// threshold then finds it with its lane scan. Requires 1 <= need <= total.
+// Contains two barriers; the result is valid after the second.
 template <typename Counts>
-__device__ __forceinline__ void find_bin_wave(Counts&& counts, uint32_t need, SelectSmem& sm) {
-  const int lane = threadIdx.x & 63;
-  u32x4 c[8];
+__device__ __forceinline__ void find_bin(Counts&& counts, uint32_t need, SelectSmem& sm) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  static_assert(kWaves * 256 == kBins, "one histogram row per wave");
+  const u32x4 c = counts();
+  const uint32_t local = c[0] + c[1] + c[2] + c[3];
+  const uint32_t incl = wave_incl_scan(local);  // lanes <= lane of this row
+  const uint32_t total = wave_total(incl);
+  if (lane == 0) sm.rowtot[wave] = total;
+  __syncthreads();
+  uint32_t above = 0;  // keys in the rows above this one
+  for (int w = kWaves - 1; w > wave; --w) above += sm.rowtot[w];
+  if (above < need && need <= above + total) {  // the threshold is in this row
+    const uint32_t ex = above + total - incl;   // keys in the lanes above this one
+    if (ex < need && need <= ex + local) {
+      uint32_t a = ex;
+      int e_hit = 0;
+      bool hit = false;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = counts(i);
-  uint32_t rs[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    rs[i] = wave_total(wave_incl_scan(c[i][0] + c[i][1] + c[i][2] + c[i][3]));
-  uint32_t above = 0;  // keys in rows above the threshold row (uniform)
-  u32x4 cr = c[0];
-  int row = 0;
-  bool found = false;
-#pragma unroll
-  for (int i = 7; i >= 0; --i) {
-    if (!found && (above + rs[i] >= need || i == 0)) {
-      found = true;
-      row = i;
-      cr = c[i];
-    } else if (!found) {
-      above += rs[i];
-    }
-  }
-  const uint32_t local = cr[0] + cr[1] + cr[2] + cr[3];
-  const uint32_t incl = wave_incl_scan(local);          // lanes <= lane
-  const uint32_t ex = above + wave_total(incl) - incl;  // keys in the lanes above this one
-  if (ex < need && need <= ex + local) {
-    uint32_t a = ex;
-    int e_hit = 0;
-    bool hit = false;
-#pragma unroll
-    for (int e = 3; e >= 0; --e) {
-      if (!hit && (a + cr[e] >= need || e == 0)) {
-        hit = true;
-        e_hit = e;
-      } else if (!hit) {
-        a += cr[e];
+      for (int e = 3; e >= 0; --e) {
+        if (!hit && (a + c[e] >= need || e == 0)) {
+          hit = true;
+          e_hit = e;
+        } else if (!hit) {
+          a += c[e];
+        }
       }
+      sm.sh_bin = (uint32_t)(256 * wave + 4 * lane + e_hit);
+      sm.sh_need = need - a;
+      sm.sh_count = c[e_hit];
     }
-    sm.sh_bin = (uint32_t)(256 * row + 4 * lane + e_hit);
-    sm.sh_need = need - a;
-    sm.sh_count = cr[e_hit];
   }
+  __syncthreads();
 }
 
 // Select for one (prompt, head) with L > budget. NS slabs per batch; with
@@ -148,17 +140,13 @@ __device__ __forceinline__ void select_head(const PathParams& p, SelectSmem& sm,
 
   uint32_t key[NS][4];
   if (RESIDENT) load_keys<NS>(key, src, P, 0);
-  // digit 1: the histogram the vote kernel accumulated
-  if (wave == 0)
-    find_bin_wave([&](int i) { return *reinterpret_cast<const u32x4*>(top + 256 * i + 4 * lane); },
-                  m, sm);
-  else
-    clear_hist(sm.rep[0], 64);
+  clear_hist(sm.rep[0], 0);
   if (tid == 0) {
     sm.sh_carry0 = 0u;
     sm.sh_carry1 = 0u;
   }
-  __syncthreads();
+  // digit 1: the histogram the vote kernel accumulated
+  find_bin([&] { return *reinterpret_cast<const u32x4*>(top + 256 * wave + 4 * lane); }, m, sm);
   uint32_t prefix = sm.sh_bin << kTopShift;  // resolved high bits of tau
   uint32_t need = sm.sh_need;
   bool settled = need == sm.sh_count;  // the whole threshold bin is kept
@@ -174,8 +162,8 @@ __device__ __forceinline__ void select_head(const PathParams& p, SelectSmem& sm,
     }
   };
   // one more digit of `bits` bits below the resolved prefix, counted into
-  // histogram buffer `buf`; wave 0 finds the threshold bin while the other
-  // waves clear the other buffer
+  // histogram buffer `buf`; the threshold bin is found, then the other
+  // buffer is cleared for the next digit
   auto digit = [&](int buf, int bits) {
     const int shift = low - bits;
     const uint32_t dmask = (1u << bits) - 1u;
@@ -186,21 +174,18 @@ __device__ __forceinline__ void select_head(const PathParams& p, SelectSmem& sm,
         if ((k4[e] >> low) == (prefix >> low)) atomicAdd(&hrep[(k4[e] >> shift) & dmask], 1u);
     });
     __syncthreads();
-    if (wave == 0) {
-      const uint32_t* hb = sm.rep[buf];
-      find_bin_wave(
-          [&](int i) {
-            u32x4 acc = {0u, 0u, 0u, 0u};
+    const uint32_t* hb = sm.rep[buf];
+    find_bin(
+        [&] {
+          u32x4 acc = {0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int r = 0; r < kReplicas; ++r)
-              acc += *reinterpret_cast<const u32x4*>(hb + r * kRepStride + 256 * i + 4 * lane);
-            return acc;
-          },
-          need, sm);
-    } else {
-      clear_hist(sm.rep[buf ^ 1], 64);
-    }
-    __syncthreads();
+          for (int r = 0; r < kReplicas; ++r)
+            acc += *reinterpret_cast<const u32x4*>(hb + r * kRepStride + 256 * wave + 4 * lane);
+          return acc;
+        },
+        need, sm);
+    clear_hist(sm.rep[buf ^ 1], 0);  // the other buffer, for the next digit
+    lds_barrier();
     prefix |= sm.sh_bin << shift;
     need = sm.sh_need;
     settled = need == sm.sh_count;
@@ -212,28 +197,36 @@ __device__ __forceinline__ void select_head(const PathParams& p, SelectSmem& sm,
   // tau = prefix exactly, and `need` of the keys equal to tau are kept.
   const uint32_t tau = prefix;
 
-  // ---- ordered compaction, one batch at a time
+  // ---- ordered compaction, one batch at a time. Per slab, each thread
+  // counts its keys above the threshold (settled: >= prefix; otherwise
+  // > tau) and equal to tau, packed as above | equal << 16; a wave scan
+  // gives every lane the counts of the lanes before it, the wave totals go
+  // through LDS, and wave 0 turns them into per-(slab, wave) bases in
+  // position order. A key above the threshold lands at (above before it) +
+  // min(equal before it, need); a key equal to tau is kept while (equal
+  // before it) < need and lands at (above before it) + (equal before it).
   const int nent = NS * kWaves;
   for (int bt = 0; bt < nbatch; ++bt) {
     if (!RESIDENT) load_keys<NS>(key, src, P, bt * NS);
+    uint32_t lane_ex[NS];  // packed counts of the lanes before this one, per slab
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      uint32_t c0 = 0, c1 = 0;
+      uint32_t c = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        c0 += (uint32_t)__popcll(__ballot(settled ? key[s][e] >= tau : key[s][e] > tau));
-        if (!settled) c1 += (uint32_t)__popcll(__ballot(key[s][e] == tau));
+        const uint32_t u = key[s][e];
+        c += (settled ? u >= tau : u > tau) ? 1u : 0u;
+        c += (!settled && u == tau) ? 0x10000u : 0u;
       }
-      if (lane == 0) {
-        sm.cnt[s * kWaves + wave][0] = c0;
-        sm.cnt[s * kWaves + wave][1] = c1;
-      }
+      const uint32_t incl = wave_incl_scan(c);
+      lane_ex[s] = incl - c;
+      if (lane == 63) sm.cnt[s * kWaves + wave] = incl;
     }
     __syncthreads();
-    if (wave == 0) {  // exclusive scan of (c0, c1) over the entries (slab-major)
+    if (wave == 0) {  // exclusive prefix of the (above, equal) totals, slab-major
       const int e0 = 2 * lane, e1 = 2 * lane + 1;
-      const uint32_t a0 = e0 < nent ? sm.cnt[e0][0] : 0u, b0 = e0 < nent ? sm.cnt[e0][1] : 0u;
-      const uint32_t a1 = e1 < nent ? sm.cnt[e1][0] : 0u, b1 = e1 < nent ? sm.cnt[e1][1] : 0u;
+      const uint32_t c0 = e0 < nent ? sm.cnt[e0] : 0u, c1 = e1 < nent ? sm.cnt[e1] : 0u;
+      const uint32_t a0 = c0 & 0xFFFFu, b0 = c0 >> 16, a1 = c1 & 0xFFFFu, b1 = c1 >> 16;
       const uint32_t ia = wave_incl_scan(a0 + a1), ib = wave_incl_scan(b0 + b1);
       const uint32_t ca = sm.sh_carry0, cb = sm.sh_carry1;
       const uint32_t xa = ca + ia - (a0 + a1), xb = cb + ib - (b0 + b1);
@@ -254,39 +247,20 @@ __device__ __forceinline__ void select_head(const PathParams& p, SelectSmem& sm,
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int ent = s * kWaves + wave;
-      if (sm.cnt[ent][0] + sm.cnt[ent][1] == 0u) continue;  // nothing kept here (uniform)
+      uint32_t above = sm.base[ent][0] + (lane_ex[s] & 0xFFFFu);
+      uint32_t equal = sm.base[ent][1] + (lane_ex[s] >> 16);
       const int jb = (bt * NS + s) * kSlab + 4 * tid;
-      bool sel[4];
-      uint32_t pos;
-      if (settled) {
-        pos = sm.base[ent][0];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sel[e] = key[s][e] >= tau;
-          pos += lanes_below(__ballot(sel[e]));
-        }
-      } else {
-        const uint32_t eq_before = sm.base[ent][1];
-        bool gt[4], eq[4];
-        uint32_t eq_rank = eq_before;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          gt[e] = key[s][e] > tau;
-          eq[e] = key[s][e] == tau;
-          eq_rank += lanes_below(__ballot(eq[e]));
-        }
-        pos = sm.base[ent][0] + min(eq_before, need);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sel[e] = gt[e] || (eq[e] && eq_rank < need);
-          eq_rank += eq[e] ? 1u : 0u;
-          pos += lanes_below(__ballot(sel[e]));
-        }
-      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if (sel[e] && pos < m) out[pos] = jb + e;
-        pos += sel[e] ? 1u : 0u;
+        const uint32_t u = key[s][e];
+        if (settled ? u >= tau : u > tau) {
+          const uint32_t pos = above + min(equal, need);
+          if (pos < m) out[pos] = jb + e;
+          ++above;
+        } else if (!settled && u == tau) {
+          if (equal < need && above + equal < m) out[above + equal] = jb + e;
+          ++equal;
+        }
       }
     }
     __syncthreads();  // cnt / base are rewritten by the next batch
