@@ -36,6 +36,8 @@ int largest_pow2_at_most(int x) {
 // Everything a call needs, derived from shapes alone, so the workspace size
 // computed ahead of a call matches the call. Workspace layout:
 //   top_hist  uint32[batch * H_kv, 2048]            top-digit histogram per head
+//   sel_table uint32[batch * H_kv, t_stride, 2]     per-segment counts before it
+//   sel_meta  uint32[batch * H_kv, 4]               threshold of each head
 //   part      float2[batch, H_kv, nchunk, rows_pad]  per-chunk row statistics
 //   pooled    float [batch, H_kv, p_stride]      pooled scores, p_stride =
 //                                                max P rounded up to 64
@@ -43,7 +45,8 @@ int largest_pow2_at_most(int x) {
 struct Plan {
   int batch, hq, hkv, d, window, group, rows, rows_pad, nrt, nwr;
   int chunk, nchunk, l_max, p_max, p_stride;
-  size_t off_top, off_part, off_pooled, bytes;
+  size_t off_top, off_table, off_meta, off_part, off_pooled, bytes;
+  int t_stride;
   snapkv::PromptTable tab;
 };
 
@@ -107,6 +110,11 @@ int32_t make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const int32
   size_t off = 0;
   pl->off_top = off;
   off = align_up(off + heads * snapkv::kTopHistBins * sizeof(uint32_t), 256);
+  pl->t_stride = (pl->p_stride + snapkv::kSegment - 1) / snapkv::kSegment;
+  pl->off_table = off;
+  off = align_up(off + heads * pl->t_stride * 2 * sizeof(uint32_t), 256);
+  pl->off_meta = off;
+  off = align_up(off + heads * 4 * sizeof(uint32_t), 256);
   pl->off_part = off;
   off = align_up(off + heads * pl->nchunk * pl->rows_pad * sizeof(float2), 256);
   pl->off_pooled = off;
@@ -137,6 +145,9 @@ snapkv::PathParams path_params(const Plan& pl, const void* q, const void* k, con
   p.k = static_cast<const uint16_t*>(k);
   p.v = static_cast<const uint16_t*>(v);
   p.top_hist = reinterpret_cast<uint32_t*>(w + pl.off_top);
+  p.sel_table = reinterpret_cast<uint32_t*>(w + pl.off_table);
+  p.sel_meta = reinterpret_cast<uint32_t*>(w + pl.off_meta);
+  p.table_stride = pl.t_stride;
   p.part = reinterpret_cast<float2*>(w + pl.off_part);
   p.pooled = reinterpret_cast<float*>(w + pl.off_pooled);
   p.pooled_stride = pl.p_stride;

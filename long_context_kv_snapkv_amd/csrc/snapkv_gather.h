@@ -1,25 +1,98 @@
-// snapkv_gather: assemble the compressed cache from the kept indices, as work
-// items of 64 output rows.
+// snapkv_gather: assemble the compressed cache, as work items of 64 output
+// slots.
 //
 // out_k[b,h,t,:] = k[off_b + idx[t], h, :] and likewise for V, for the first
-// n = min(L, B) entries; the remaining entries are zero rows with index -1
+// n = min(L, B) slots; the remaining slots are zero rows with index -1
 // (glossary page "SnapKV(スナップケーブイ)", section "SnapKVの仕組み", steps
 // 3-4: the kept pairs form the cache that decode then reads). A prompt with
-// L <= B is copied whole (indices 0 .. L-1) and its index list is written
-// here; for longer prompts the list comes from the selection.
+// L <= B is copied whole (indices 0 .. L-1). For longer prompts slots
+// 0 .. m-1 (m = B - W) hold the kept prefix positions in ascending order and
+// slots m .. B-1 the window positions P .. L-1; the item finds the kept
+// positions of its slots from the selection's count table: only the
+// segments whose kept keys fall into its slots are rescanned (at most one
+// per slot), and each kept key's slot follows from the counts before it.
 //
 // Each lane moves one 16-byte piece of a row, so a wave moves whole rows:
 // reads are row-granular gathers from the packed [T, H_kv, D] cache, writes
 // are contiguous. All of a thread's loads are issued before its stores.
-// Rows are bit copies.
+// Rows are bit copies; out_idx is written here for every slot.
 #pragma once
 
 #include "snapkv_device.h"
 
 namespace snapkv {
 
+struct GatherSmem {
+  int32_t pos[kGatherRows];  // kept position of each of the item's slots
+  int32_t seg[kGatherRows];  // segments holding them
+  uint32_t nseg;
+};
+
+// s.pos[t - lo] = the kept prefix position in slot t, for lo <= t < hi <= m,
+// of prompt b / head h with L > B.
+__device__ __forceinline__ void locate_kept(const PathParams& p, GatherSmem& s, int b, int h,
+                                            int lo, int hi) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int P = p.tab.len[b] - p.window;
+  const uint32_t m = (uint32_t)(p.budget - p.window);
+  const size_t head = (size_t)(b * p.hkv + h);
+  const uint32_t* tab = p.sel_table + head * (size_t)p.table_stride * 2;
+  const uint32_t* meta = p.sel_meta + head * 4;
+  const uint32_t tau = meta[0], need = meta[1];
+  const bool settled = meta[2] != 0u;
+  const int nseg = (P + kSegment - 1) / kSegment;
+  if (tid < kGatherRows) s.pos[tid] = -1;
+  if (tid == 0) s.nseg = 0u;
+  __syncthreads();
+  // segments whose kept slots [before, before next) meet [lo, hi): each
+  // holds at least one of the item's slots, so there are at most
+  // kGatherRows of them (empty segments are skipped)
+  for (int e = tid; e < nseg; e += kThreads) {
+    const uint32_t kb = tab[2 * e] + min(tab[2 * e + 1], need);
+    const uint32_t ka = e + 1 < nseg ? tab[2 * e + 2] + min(tab[2 * e + 3], need) : m;
+    if (kb < ka && kb < (uint32_t)hi && ka > (uint32_t)lo) {
+      const uint32_t q = atomicAdd(&s.nseg, 1u);
+      if (q < (uint32_t)kGatherRows) s.seg[q] = e;
+    }
+  }
+  __syncthreads();
+  const int nneed = min((int)s.nseg, kGatherRows);
+  const float* src = p.pooled + head * p.pooled_stride;
+  const int last = (P - 1) & ~3;
+  for (int q = wave; q < nneed; q += kWaves) {
+    const int e = s.seg[q];
+    const int j0 = e * kSegment + 4 * lane;
+    const float4 v = *reinterpret_cast<const float4*>(src + min(j0, last));
+    uint32_t key[4] = {j0 < P ? order_key(v.x) : 0u, j0 + 1 < P ? order_key(v.y) : 0u,
+                       j0 + 2 < P ? order_key(v.z) : 0u, j0 + 3 < P ? order_key(v.w) : 0u};
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      c += (settled ? key[k] >= tau : key[k] > tau) ? 1u : 0u;
+      c += (!settled && key[k] == tau) ? 0x10000u : 0u;
+    }
+    const uint32_t ex = wave_incl_scan(c) - c;
+    uint32_t above = tab[2 * e] + (ex & 0xFFFFu);
+    uint32_t equal = tab[2 * e + 1] + (ex >> 16);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t slot = 0xFFFFFFFFu;
+      if (settled ? key[k] >= tau : key[k] > tau) {
+        slot = above + min(equal, need);
+        ++above;
+      } else if (!settled && key[k] == tau) {
+        if (equal < need) slot = above + equal;
+        ++equal;
+      }
+      if (slot >= (uint32_t)lo && slot < (uint32_t)hi) s.pos[slot - lo] = j0 + k;
+    }
+  }
+  __syncthreads();
+}
+
 template <int D>
-__device__ __forceinline__ void snapkv_gather_item(const PathParams& p, int b, int h, int rb) {
+__device__ __forceinline__ void snapkv_gather_item(const PathParams& p, GatherSmem& gs, int b,
+                                                   int h, int rb) {
   constexpr int PIECES = D / 8;
   constexpr int ROWS_PER_PASS = kThreads / PIECES;
   constexpr int PASSES = kGatherRows / ROWS_PER_PASS;
@@ -28,6 +101,8 @@ __device__ __forceinline__ void snapkv_gather_item(const PathParams& p, int b, i
   const int L = p.tab.len[b];
   const int B = p.budget;
   const bool whole = L <= B;
+  const int P = L - p.window, m = B - p.window;
+  if (!whole && t0 < m) locate_kept(p, gs, b, h, t0, min(t0 + kGatherRows, m));
   const int tid = threadIdx.x;
   int32_t* idx = p.out_idx + (size_t)(b * p.hkv + h) * B;
   const size_t tstride = (size_t)p.hkv * D;
@@ -36,15 +111,16 @@ __device__ __forceinline__ void snapkv_gather_item(const PathParams& p, int b, i
   const size_t obase = (size_t)(b * p.hkv + h) * B * D;
   const int piece = tid % PIECES;
   u32x4 kx[PASSES], vx[PASSES];
-  int tt[PASSES];
+  int tt[PASSES], jj[PASSES];
 #pragma unroll
   for (int q = 0; q < PASSES; ++q) {
     const int t = t0 + tid / PIECES + q * ROWS_PER_PASS;
     tt[q] = t;
     kx[q] = vx[q] = u32x4{0u, 0u, 0u, 0u};
-    if (t >= B) continue;
-    const int j = whole ? (t < L ? t : -1) : idx[t];
-    if (j >= 0 && j < L) {  // the bound also keeps a bad index list in range
+    int j = -1;
+    if (t < B) j = whole ? (t < L ? t : -1) : (t < m ? gs.pos[t - t0] : P + (t - m));
+    jj[q] = j;
+    if (j >= 0 && j < L) {  // the bound also keeps an inconsistent table in range
       kx[q] = *reinterpret_cast<const u32x4*>(ksrc + (size_t)j * tstride + piece * 8);
       vx[q] = *reinterpret_cast<const u32x4*>(vsrc + (size_t)j * tstride + piece * 8);
     }
@@ -55,7 +131,7 @@ __device__ __forceinline__ void snapkv_gather_item(const PathParams& p, int b, i
     if (t >= B) continue;
     *reinterpret_cast<u32x4*>(p.out_k + obase + (size_t)t * D + piece * 8) = kx[q];
     *reinterpret_cast<u32x4*>(p.out_v + obase + (size_t)t * D + piece * 8) = vx[q];
-    if (whole && piece == 0) idx[t] = t < L ? t : -1;
+    if (piece == 0) idx[t] = jj[q];
   }
 }
 

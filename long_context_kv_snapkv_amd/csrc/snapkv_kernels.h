@@ -15,6 +15,7 @@ constexpr int kKeyTile = 64;       // keys per LDS tile
 constexpr int kMaxChunk = 4096;    // keys per scoring work item
 constexpr int kGatherRows = 64;    // compressed rows per gather work item
 constexpr int kTopHistBins = 2048; // bins of the selection's first radix digit
+constexpr int kSegment = 256;      // positions per selection count-table entry
 
 // Per-prompt table passed by value in the kernel arguments.
 struct PromptTable {
@@ -33,12 +34,16 @@ struct PathParams {
   float2* part;       // [batch, Hkv, nchunk, rows_pad] per-chunk (max, sum) in log2 units
   float* pooled;      // [batch, Hkv, pooled_stride] pooled scores c_h[j], j < P
   uint32_t* top_hist;   // [batch * Hkv, kTopHistBins] histogram of the pooled keys' top 11 bits
+  uint32_t* sel_table;  // [batch * Hkv, table_stride, 2] per kSegment positions: keys above /
+                        // equal to the threshold before the segment
+  uint32_t* sel_meta;   // [batch * Hkv, 4]: threshold key, keys equal to it kept, settled
   int32_t batch, hq, hkv, window, group;
   int32_t rows, rows_pad;  // G*W and its round-up to 32
   int32_t nwr;             // waves that split the row tiles (power of two)
   int32_t chunk;           // keys per scoring item, multiple of kKeyTile
   int32_t nchunk;          // chunk slots per (prompt, head) in part
   int32_t pooled_stride;   // floats per pooled row (>= max P; a multiple of 64 in the workspace)
+  int32_t table_stride;    // segments per head in sel_table (>= ceil(max P / kSegment))
   int32_t budget, kernel, pool_mode;
   int32_t score_all;       // 1: score every prompt with P >= 1; 0: only L > budget
   int32_t export_scores;   // 1: pooled rows are the caller's, zero past P

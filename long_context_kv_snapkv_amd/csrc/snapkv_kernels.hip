@@ -2,8 +2,9 @@
 //
 //   snapkv_score_stats  (chunk, head, prompt)   per-row softmax statistics
 //   snapkv_score_vote   (chunk, head, prompt)   window vote + pooling
-//   snapkv_select       (head, prompt)          top-(B - W) positions
-//   snapkv_gather       (row block, head, prompt)
+//   snapkv_select       (head, prompt)          threshold of the top-(B - W)
+//                                               and its count table
+//   snapkv_gather       (row block, head, prompt)  slots -> positions, rows
 //
 // A compress call runs the four in stream order; the kernel boundaries carry
 // every hand-off between stages (no inter-workgroup waiting or flags). The
@@ -59,7 +60,8 @@ __global__ void __launch_bounds__(kThreads) snapkv_select(const PathParams p) {
 
 template <int D>
 __global__ void __launch_bounds__(kThreads) snapkv_gather(const PathParams p) {
-  snapkv_gather_item<D>(p, blockIdx.z, blockIdx.y, blockIdx.x);
+  __shared__ GatherSmem sm;
+  snapkv_gather_item<D>(p, sm, blockIdx.z, blockIdx.y, blockIdx.x);
 }
 
 template <typename F>

@@ -2,9 +2,10 @@
 // (glossary page "SnapKV(スナップケーブイ)", section "SnapKVの仕組み", step 3:
 // the top-budget positions by pooled score are kept; paper page "SnapKV: LLM
 // Knows What You are Looking for Before Generation", abstract: selection is
-// per attention head). Output: the m positions with the largest pooled
-// scores, ties going to the lower position, in ascending order, followed by
-// the window positions P .. L-1.
+// per attention head): the m positions with the largest pooled scores, ties
+// going to the lower position, in ascending order. This kernel finds the
+// threshold and a table of counts from which the gather places every kept
+// position in its output slot (the window positions P .. L-1 follow).
 //
 // One workgroup per (prompt, head), integer decisions only (exact given the
 // fp32 pooled scores):
@@ -25,11 +26,11 @@
 //     largest key is found from the row totals. When every key of that bin
 //     is needed the threshold is settled at that digit: the kept keys are
 //     exactly those >= the bin's lowest key;
-//   * ordered compaction: per-slab wave scans of packed (above, equal)
-//     counts and one exclusive scan of the per-(slab, wave) totals give
-//     every kept position its output slot. Only if the last digit leaves a
-//     bin of equal keys of which some are kept are the lowest-positioned
-//     ones of them taken.
+//   * count table: for every kSegment positions, how many keys before them
+//     lie above the threshold and how many equal it (per-slab wave scans of
+//     packed counts, one exclusive scan of the per-(slab, wave) totals).
+//     Only if the last digit leaves a bin of equal keys of which some are
+//     kept are the lowest-positioned ones of them taken.
 #pragma once
 
 #include "snapkv_device.h"
@@ -46,7 +47,6 @@ constexpr int kHistWords = kReplicas * kRepStride;
 struct alignas(16) SelectSmem {
   uint32_t rep[2][kHistWords];  // replicated histograms of digits 2 and 3
   uint32_t cnt[kMaxSlabsHeld * kWaves];      // per (slab, wave): above | equal << 16
-  uint32_t base[kMaxSlabsHeld * kWaves][2];  // exclusive prefix of cnt in position order
   uint32_t rowtot[kWaves];                   // histogram row totals (find)
   uint32_t sh_bin, sh_need, sh_count, sh_carry0, sh_carry1;
 };
@@ -134,7 +134,6 @@ __device__ __forceinline__ void select_head(const PathParams& p, SelectSmem& sm,
   const size_t head = (size_t)(b * p.hkv + h);
   const float* src = p.pooled + head * p.pooled_stride;
   const uint32_t* top = p.top_hist + head * kTopBins;
-  int32_t* out = p.out_idx + head * p.budget;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nbatch = RESIDENT ? 1 : (P + NS * kSlab - 1) / (NS * kSlab);
 
@@ -197,18 +196,20 @@ __device__ __forceinline__ void select_head(const PathParams& p, SelectSmem& sm,
   // tau = prefix exactly, and `need` of the keys equal to tau are kept.
   const uint32_t tau = prefix;
 
-  // ---- ordered compaction, one batch at a time. Per slab, each thread
-  // counts its keys above the threshold (settled: >= prefix; otherwise
-  // > tau) and equal to tau, packed as above | equal << 16; a wave scan
-  // gives every lane the counts of the lanes before it, the wave totals go
-  // through LDS, and wave 0 turns them into per-(slab, wave) bases in
-  // position order. A key above the threshold lands at (above before it) +
-  // min(equal before it, need); a key equal to tau is kept while (equal
-  // before it) < need and lands at (above before it) + (equal before it).
+  // ---- count table, one batch at a time. Per slab, each thread counts its
+  // keys above the threshold (settled: >= prefix; otherwise > tau) and equal
+  // to tau, packed as above | equal << 16 (a wave sums at most 256 of each);
+  // the wave totals go through LDS and wave 0 turns them into the counts
+  // before every kSegment positions (one (slab, wave) unit), in position
+  // order. The gather turns these into output slots: a key above the
+  // threshold lands at (above before it) + min(equal before it, need), a key
+  // equal to tau is kept while (equal before it) < need and lands at
+  // (above before it) + (equal before it).
+  static_assert(kSegment == 4 * 64, "a segment is one wave's share of a slab");
   const int nent = NS * kWaves;
+  uint32_t* table = p.sel_table + head * (size_t)p.table_stride * 2;
   for (int bt = 0; bt < nbatch; ++bt) {
     if (!RESIDENT) load_keys<NS>(key, src, P, bt * NS);
-    uint32_t lane_ex[NS];  // packed counts of the lanes before this one, per slab
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       uint32_t c = 0;
@@ -219,7 +220,6 @@ __device__ __forceinline__ void select_head(const PathParams& p, SelectSmem& sm,
         c += (!settled && u == tau) ? 0x10000u : 0u;
       }
       const uint32_t incl = wave_incl_scan(c);
-      lane_ex[s] = incl - c;
       if (lane == 63) sm.cnt[s * kWaves + wave] = incl;
     }
     __syncthreads();
@@ -230,42 +230,28 @@ __device__ __forceinline__ void select_head(const PathParams& p, SelectSmem& sm,
       const uint32_t ia = wave_incl_scan(a0 + a1), ib = wave_incl_scan(b0 + b1);
       const uint32_t ca = sm.sh_carry0, cb = sm.sh_carry1;
       const uint32_t xa = ca + ia - (a0 + a1), xb = cb + ib - (b0 + b1);
-      if (e0 < nent) {
-        sm.base[e0][0] = xa;
-        sm.base[e0][1] = xb;
+      const int g0 = bt * nent + e0, g1 = bt * nent + e1;  // segment index in the prefix
+      if (e0 < nent && g0 < p.table_stride) {
+        table[2 * g0] = xa;
+        table[2 * g0 + 1] = xb;
       }
-      if (e1 < nent) {
-        sm.base[e1][0] = xa + a0;
-        sm.base[e1][1] = xb + b0;
+      if (e1 < nent && g1 < p.table_stride) {
+        table[2 * g1] = xa + a0;
+        table[2 * g1 + 1] = xb + b0;
       }
       if (lane == 63) {
         sm.sh_carry0 = ca + ia;
         sm.sh_carry1 = cb + ib;
       }
     }
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int ent = s * kWaves + wave;
-      uint32_t above = sm.base[ent][0] + (lane_ex[s] & 0xFFFFu);
-      uint32_t equal = sm.base[ent][1] + (lane_ex[s] >> 16);
-      const int jb = (bt * NS + s) * kSlab + 4 * tid;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t u = key[s][e];
-        if (settled ? u >= tau : u > tau) {
-          const uint32_t pos = above + min(equal, need);
-          if (pos < m) out[pos] = jb + e;
-          ++above;
-        } else if (!settled && u == tau) {
-          if (equal < need && above + equal < m) out[above + equal] = jb + e;
-          ++equal;
-        }
-      }
-    }
-    __syncthreads();  // cnt / base are rewritten by the next batch
+    __syncthreads();  // cnt is rewritten by the next batch
   }
-  for (int i = tid; i < p.window; i += kThreads) out[m + i] = P + i;
+  if (tid == 0) {
+    uint32_t* meta = p.sel_meta + head * 4;
+    meta[0] = tau;
+    meta[1] = need;
+    meta[2] = settled ? 1u : 0u;
+  }
 }
 
 // Selection of one (prompt, head): the smallest register batch that holds
