@@ -29,8 +29,8 @@ HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 METRIC = "prompt tokens compressed/sec per layer; achieved HBM GB/s vs MI355X peak"
 CACHE_BYTES = 256 << 20       # Infinity Cache
-SCORE_SOURCES = ("snapkv_kernels.hip", "snapkv_score.h", "snapkv_select.h",
-                 "snapkv_gather.h", "snapkv_device.h")
+KERNEL_SOURCES = ("snapkv_api.cpp", "snapkv_kernels.h", "snapkv_kernels.hip", "snapkv_score.h",
+                  "snapkv_select.h", "snapkv_gather.h", "snapkv_device.h")
 
 
 def algorithmic_bytes(w, seq_lens):
@@ -83,7 +83,7 @@ def _traffic(kernel_key):
         return None
     with open(path) as f:
         rec = json.load(f).get(kernel_key)
-    if not rec or rec.get("source_hash") != _source_hash(SCORE_SOURCES):
+    if not rec or rec.get("source_hash") != _source_hash(KERNEL_SOURCES):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -182,8 +182,8 @@ def main():
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
 
-    # per-kernel durations: snapkv_compress_staged runs each stage as one
-    # kernel and records caller events around it on the same stream
+    # per-kernel durations: snapkv_compress_staged has each stage's dispatch
+    # record the caller's events at its kernel's start and end
     nprof = min(args.steps, 200)
     nst = skv.SNAPKV_NUM_STAGES
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nst)]

@@ -133,9 +133,10 @@ int32_t snapkv_compress(int32_t batch, int32_t num_q_heads,
 /*
  * snapkv_compress with optional per-stage timing: the same kernels (named by
  * snapkv_stage_name) and identical results. When stage_events is not NULL it
- * points to
- * 2 * SNAPKV_NUM_STAGES caller-owned hipEvent_t; stage_events[2*s] is
- * recorded before and stage_events[2*s+1] after stage s on the same stream.
+ * points to 2 * SNAPKV_NUM_STAGES caller-owned hipEvent_t: the dispatch of
+ * stage s records stage_events[2*s] when its kernel starts and
+ * stage_events[2*s+1] when it ends (a stage without work records both back
+ * to back), so elapsed times are the kernels' own durations.
  * Errors as for snapkv_compress.
  */
 int32_t snapkv_compress_staged(int32_t batch, int32_t num_q_heads,

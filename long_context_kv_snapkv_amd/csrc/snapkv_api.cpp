@@ -217,27 +217,39 @@ int32_t compress_impl(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const v
   p.out_v = static_cast<uint16_t*>(out_v);
   p.out_idx = out_idx;
   hipError_t e;
-  // optional caller events bracket every stage (snapkv_compress_staged)
+  // optional caller events, recorded by each stage's dispatch at the
+  // kernel's start and end (snapkv_compress_staged); a stage that has no
+  // work records both events back to back
   hipEvent_t const* ev = reinterpret_cast<hipEvent_t const*>(stage_events);
-  auto mark = [&](int i) {
-    if (ev) (void)hipEventRecord(ev[i], s);
+  auto events = [&](int stage) {
+    snapkv::StageEvents e;
+    if (ev) {
+      e.start = ev[2 * stage];
+      e.stop = ev[2 * stage + 1];
+    }
+    return e;
+  };
+  auto skip = [&](int stage) {
+    if (ev) {
+      (void)hipEventRecord(ev[2 * stage], s);
+      (void)hipEventRecord(ev[2 * stage + 1], s);
+    }
   };
   const bool scored = any_scored(pl, budget, false);
-  mark(0);
-  if (scored && (e = snapkv::launch_score_stats(p, d, s)) != hipSuccess)
-    return hip_fail(e, "snapkv_score_stats launch");
-  mark(1);
-  mark(2);
-  if (scored && (e = snapkv::launch_score_vote(p, d, s)) != hipSuccess)
-    return hip_fail(e, "snapkv_score_vote launch");
-  mark(3);
-  mark(4);
-  if (scored && (e = snapkv::launch_select(p, s)) != hipSuccess)
-    return hip_fail(e, "snapkv_select launch");
-  mark(5);
-  mark(6);
-  if ((e = snapkv::launch_gather(p, d, s)) != hipSuccess) return hip_fail(e, "snapkv_gather launch");
-  mark(7);
+  if (!scored) {
+    skip(0);
+    skip(1);
+    skip(2);
+  } else {
+    if ((e = snapkv::launch_score_stats(p, d, s, events(0))) != hipSuccess)
+      return hip_fail(e, "snapkv_score_stats launch");
+    if ((e = snapkv::launch_score_vote(p, d, s, events(1))) != hipSuccess)
+      return hip_fail(e, "snapkv_score_vote launch");
+    if ((e = snapkv::launch_select(p, s, events(2))) != hipSuccess)
+      return hip_fail(e, "snapkv_select launch");
+  }
+  if ((e = snapkv::launch_gather(p, d, s, events(3))) != hipSuccess)
+    return hip_fail(e, "snapkv_gather launch");
   return SNAPKV_OK;
 }
 

@@ -52,10 +52,19 @@ struct PathParams {
   PromptTable tab;
 };
 
+// Optional events recorded by the dispatch itself at the kernel's start and
+// end (so they time the kernel alone, as a profiler's kernel trace does).
+struct StageEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
 // Stage kernels: grids of work items.
-hipError_t launch_score_stats(const PathParams& p, int head_dim, hipStream_t stream);
-hipError_t launch_score_vote(const PathParams& p, int head_dim, hipStream_t stream);
-hipError_t launch_select(const PathParams& p, hipStream_t stream);
-hipError_t launch_gather(const PathParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_score_stats(const PathParams& p, int head_dim, hipStream_t stream,
+                              StageEvents ev = {});
+hipError_t launch_score_vote(const PathParams& p, int head_dim, hipStream_t stream,
+                             StageEvents ev = {});
+hipError_t launch_select(const PathParams& p, hipStream_t stream, StageEvents ev = {});
+hipError_t launch_gather(const PathParams& p, int head_dim, hipStream_t stream,
+                         StageEvents ev = {});
 
 }  // namespace snapkv

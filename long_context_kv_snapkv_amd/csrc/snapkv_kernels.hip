@@ -10,6 +10,8 @@
 // every hand-off between stages (no inter-workgroup waiting or flags). The
 // score export runs stats and vote only, with the caller's buffer as the
 // pooled rows.
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 #include "snapkv_gather.h"
@@ -64,6 +66,20 @@ __global__ void __launch_bounds__(kThreads) snapkv_gather(const PathParams p) {
   snapkv_gather_item<D>(p, sm, blockIdx.z, blockIdx.y, blockIdx.x);
 }
 
+// Launch with one PathParams argument; with events, through the extended
+// launch that records them at the kernel's own start and end.
+template <typename K>
+hipError_t launch(K kernel, dim3 grid, hipStream_t stream, const StageEvents& ev,
+                  const PathParams& p) {
+  if (ev.start != nullptr || ev.stop != nullptr) {
+    void* args[] = {const_cast<PathParams*>(&p)};
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, dim3(kThreads), args,
+                              0, stream, ev.start, ev.stop, 0);
+  }
+  hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <typename F>
 hipError_t dispatch_dim(int head_dim, F&& f) {
   if (head_dim == 128) return f(std::integral_constant<int, 128>());
@@ -90,32 +106,31 @@ int row_tiles_per_wave(const PathParams& p) {
 
 }  // namespace
 
-hipError_t launch_score_stats(const PathParams& p, int head_dim, hipStream_t stream) {
+hipError_t launch_score_stats(const PathParams& p, int head_dim, hipStream_t stream,
+                              StageEvents ev) {
   return dispatch_dim_rtw(head_dim, row_tiles_per_wave(p), [&](auto d, auto rtw) {
-    hipLaunchKernelGGL((snapkv_score_stats<decltype(d)::value, decltype(rtw)::value>),
-                       dim3(p.nchunk, p.hkv, p.batch), dim3(kThreads), 0, stream, p);
-    return hipGetLastError();
+    return launch(snapkv_score_stats<decltype(d)::value, decltype(rtw)::value>,
+                  dim3(p.nchunk, p.hkv, p.batch), stream, ev, p);
   });
 }
 
-hipError_t launch_score_vote(const PathParams& p, int head_dim, hipStream_t stream) {
+hipError_t launch_score_vote(const PathParams& p, int head_dim, hipStream_t stream,
+                             StageEvents ev) {
   return dispatch_dim_rtw(head_dim, row_tiles_per_wave(p), [&](auto d, auto rtw) {
-    hipLaunchKernelGGL((snapkv_score_vote<decltype(d)::value, decltype(rtw)::value>),
-                       dim3(p.nchunk, p.hkv, p.batch), dim3(kThreads), 0, stream, p);
-    return hipGetLastError();
+    return launch(snapkv_score_vote<decltype(d)::value, decltype(rtw)::value>,
+                  dim3(p.nchunk, p.hkv, p.batch), stream, ev, p);
   });
 }
 
-hipError_t launch_select(const PathParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(snapkv_select, dim3(p.hkv, p.batch), dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
+hipError_t launch_select(const PathParams& p, hipStream_t stream, StageEvents ev) {
+  return launch(snapkv_select, dim3(p.hkv, p.batch), stream, ev, p);
 }
 
-hipError_t launch_gather(const PathParams& p, int head_dim, hipStream_t stream) {
+hipError_t launch_gather(const PathParams& p, int head_dim, hipStream_t stream,
+                         StageEvents ev) {
   return dispatch_dim(head_dim, [&](auto d) {
-    hipLaunchKernelGGL(snapkv_gather<decltype(d)::value>, dim3(p.n_gather_blocks, p.hkv, p.batch),
-                       dim3(kThreads), 0, stream, p);
-    return hipGetLastError();
+    return launch(snapkv_gather<decltype(d)::value>, dim3(p.n_gather_blocks, p.hkv, p.batch),
+                  stream, ev, p);
   });
 }
 
