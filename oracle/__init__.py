@@ -22,5 +22,7 @@ from .snapkv_oracle import (  # noqa: F401
     prompt_scores,
     select_prefix,
     validate,
+    window_lse,
     window_vote,
+    window_vote_from_lse,
 )

@@ -19,6 +19,12 @@ O3  vote: for KV head h, every query head q in h's group and every window row
     paragraph and steps 1-2: the window tokens' attention scores per head are
     aggregated; FAQ Q1: MHA and GQA models; abstract of the SnapKV paper page:
     the pattern is read from an observation window at the end of the prompt);
+O3' the same vote from normalisers supplied by the caller's prefill: each
+    window row's natural-log normaliser lse_i = log sum_{j <= P+i}
+    exp(q_i . k_j / sqrt(D)) (window_lse), and s_h[j] as the sum of
+    exp(q_i . k_j / sqrt(D) - lse_i) (window_vote_from_lse) (glossary page
+    "SnapKV", FAQ Q3: the scores come out of the ordinary prefill attention
+    at almost no extra cost);
 O4  pool: smooth s_h along the position axis with a window of k positions,
     stride 1, same length, averaging (dividing by k, positions outside the
     prefix count as zero) or taking the in-range maximum (glossary page,
@@ -130,6 +136,60 @@ def window_vote(q_group: np.ndarray, k_head: np.ndarray, window: int) -> np.ndar
     return s
 
 
+def window_vote_from_lse(q_group: np.ndarray, k_head: np.ndarray, window: int,
+                         lse_group: np.ndarray) -> np.ndarray:
+    """s_h[j], j < P, from normalisers the caller supplies: the sum over the G
+    heads and W rows of exp(q_i . k_j / sqrt(D) - lse_i).
+
+    lse_group: [G, W] natural-log normalisers of the window rows (what
+    window_lse returns for this group). Every window row sees every prefix
+    key (j < P <= P + i), so no mask enters. With the exact normalisers this
+    is window_vote (glossary page "SnapKV", FAQ Q3: the scores can come out of
+    the ordinary prefill attention, whose kernels keep each row's log-sum-exp).
+    """
+    length, d = k_head.shape
+    prefix = length - window
+    s = np.zeros(prefix, dtype=np.float64)
+    for q_rows, lse_rows in zip(q_group, lse_group):
+        logits = (q_rows @ k_head[:prefix].T) / np.sqrt(d)
+        s += np.exp(logits - np.asarray(lse_rows, dtype=np.float64)[:, None]).sum(axis=0)
+    return s
+
+
+def window_lse(q_win_bits: np.ndarray, k_bits: np.ndarray, seq_lens,
+               window: int) -> np.ndarray:
+    """Natural-log softmax normaliser of every observation-window row.
+
+    Entry [b, q, i] is log sum_{j <= P+i} exp(q . k_j / sqrt(D)) for prompt b
+    (P = L_b - W), query head q against the keys of KV head q // G, window row
+    i; NaN where the row's position P + i is negative (a prompt shorter than
+    the window has no such query). float64 [batch, H_q, W]. This is the
+    quantity a prefill flash-attention kernel keeps per row (glossary page
+    "SnapKV", FAQ Q3); the maximum is factored out only to keep exp finite.
+    """
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    batch, h_q, w, d = q_win_bits.shape
+    h_kv = k_bits.shape[1]
+    if w != window or batch != seq_lens.size or h_q % h_kv != 0:
+        raise OracleError("q_win, seq_lens and the head counts disagree")
+    g = h_q // h_kv
+    out = np.full((batch, h_q, w), np.nan)
+    offset = 0
+    for b, length in enumerate(seq_lens.tolist()):
+        prefix = length - window
+        rows = [i for i in range(w) if prefix + i >= 0]
+        for q in range(h_q):
+            k_head = bf16_bits_to_f64(k_bits[offset:offset + length, q // g, :])
+            q_rows = bf16_bits_to_f64(q_win_bits[b, q])
+            logits = (q_rows @ k_head.T) / np.sqrt(d)
+            for i in rows:
+                row = logits[i, :prefix + i + 1]
+                top = row.max()
+                out[b, q, i] = top + np.log(np.exp(row - top).sum())
+        offset += length
+    return out
+
+
 # ------------------------------------------------------------------ O4 pool --
 def pool_scores(s: np.ndarray, kernel: int, pool) -> np.ndarray:
     """Same-length stride-1 pooling of a score vector with kernel k.
@@ -181,8 +241,9 @@ class OracleResult:
 
 def prompt_scores(q_win_bits, k_bits, offset: int, length: int, b: int,
                   h_q: int, h_kv: int, window: int, kernel: int, pool,
-                  heads=None):
-    """Raw and pooled scores of one prompt, per KV head ([H_kv, P])."""
+                  heads=None, lse=None):
+    """Raw and pooled scores of one prompt, per KV head ([H_kv, P]); with
+    lse ([H_q, W] normalisers of this prompt) the vote uses them."""
     prefix = length - window
     g = h_q // h_kv
     heads = range(h_kv) if heads is None else heads
@@ -191,18 +252,23 @@ def prompt_scores(q_win_bits, k_bits, offset: int, length: int, b: int,
     for h in heads:
         k_head = bf16_bits_to_f64(k_bits[offset:offset + length, h, :])
         q_group = bf16_bits_to_f64(q_win_bits[b, h * g:(h + 1) * g])
-        raw[h] = window_vote(q_group, k_head, window)
+        if lse is None:
+            raw[h] = window_vote(q_group, k_head, window)
+        else:
+            raw[h] = window_vote_from_lse(q_group, k_head, window, lse[h * g:(h + 1) * g])
         pooled[h] = pool_scores(raw[h], kernel, pool)
     return raw, pooled
 
 
 def compress(q_win_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
              seq_lens, window: int, kernel: int, pool, budget: int,
-             keep_scores: bool = True) -> OracleResult:
+             keep_scores: bool = True, lse=None) -> OracleResult:
     """Whole compression of one layer.
 
     q_win_bits: uint16 [batch, H_q, W, D]; k_bits, v_bits: uint16 [T, H_kv, D]
-    with the prompts packed back to back; seq_lens: [batch].
+    with the prompts packed back to back; seq_lens: [batch]. lse, when given,
+    is [batch, H_q, W] window-row normalisers that the vote takes in place of
+    its own (window_vote_from_lse).
     """
     seq_lens = np.asarray(seq_lens, dtype=np.int64)
     batch, h_q, w, d = q_win_bits.shape
@@ -226,7 +292,8 @@ def compress(q_win_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
         raw = pooled = None
         if prefix >= 1 and (length > budget or keep_scores):
             raw, pooled = prompt_scores(q_win_bits, k_bits, offset, length, b,
-                                        h_q, h_kv, window, kernel, pool)
+                                        h_q, h_kv, window, kernel, pool,
+                                        lse=None if lse is None else lse[b])
         for h in range(h_kv):
             sel = select_prefix(pooled[h], m) if length > budget else None
             idx = assemble_indices(length, window, budget, sel)
