@@ -150,6 +150,39 @@ int32_t snapkv_compress_staged(int32_t batch, int32_t num_q_heads,
                                void* stream, void* const* stage_events);
 
 /*
+ * snapkv_compress for a caller whose own prefill attention already produced
+ * the softmax normaliser of every observation-window row (glossary page
+ * "SnapKV(スナップケーブイ)", FAQ Q3: the scores are computed together with
+ * the ordinary prefill, at almost no extra cost). The window-statistics pass
+ * is skipped:
+ *
+ *   window_lse  device float32 [batch, H_q, W], row-major: for prompt b,
+ *               query head q and window row i (position P + i), the natural
+ *               log of sum_{j <= P + i} exp(q . k_j / sqrt(D)) over the
+ *               prompt's keys (what flash-attention kernels report as the
+ *               log-sum-exp of a row). 4-byte aligned. Read only. Only the
+ *               rows of prompts that are compressed (L_b > B) are read and
+ *               they must be finite; entries of other prompts are ignored.
+ *
+ * Results equal snapkv_compress's up to the normalisers' rounding (the
+ * votes are computed from them; selections are identical wherever the
+ * pooled scores are not within that rounding of a tie). Other arguments,
+ * the workspace and errors as for snapkv_compress; SNAPKV_ERR_INVALID_ARGUMENT
+ * also for a null or misaligned window_lse. It runs the kernels of
+ * snapkv_compress with the first (the statistics pass) replaced by a small
+ * one that clears the vote's histogram in the workspace.
+ */
+int32_t snapkv_compress_from_lse(int32_t batch, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim,
+                                 const void* q_win, const void* k,
+                                 const void* v, const int32_t* seq_lens,
+                                 int32_t window, const float* window_lse,
+                                 int32_t kernel_size, int32_t pool_mode,
+                                 int32_t budget, void* out_k, void* out_v,
+                                 int32_t* out_idx, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
  * The pooled scores c_h (steps 1-2) of every prompt with P = L - W >= 1,
  * whatever its length relative to a budget; raw scores when kernel_size = 1.
  *

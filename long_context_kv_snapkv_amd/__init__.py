@@ -23,6 +23,7 @@ from .snapkv import (  # noqa: F401
     new_workspace,
     pool_mode_code,
     snapkv_compress,
+    snapkv_compress_from_lse,
     snapkv_last_error,
     snapkv_stage_name,
     snapkv_status_string,

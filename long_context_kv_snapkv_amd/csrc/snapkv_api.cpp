@@ -197,7 +197,7 @@ int32_t compress_impl(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const v
                       const void* k, const void* v, const int32_t* seq_lens, int32_t window,
                       int32_t kernel, int32_t pool_mode, int32_t budget, void* out_k,
                       void* out_v, int32_t* out_idx, void* workspace, size_t workspace_bytes,
-                      void* stream, void* const* stage_events) {
+                      void* stream, void* const* stage_events, const float* window_lse) {
   int32_t st = check_tensors(q_win, k, v, out_k, out_v, out_idx);
   if (st != SNAPKV_OK) return st;
   Plan pl;
@@ -216,6 +216,8 @@ int32_t compress_impl(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const v
   p.out_k = static_cast<uint16_t*>(out_k);
   p.out_v = static_cast<uint16_t*>(out_v);
   p.out_idx = out_idx;
+  p.window_lse = window_lse;
+  const bool ext_lse = window_lse != nullptr;
   hipError_t e;
   // optional caller events, recorded by each stage's dispatch at the
   // kernel's start and end (snapkv_compress_staged); a stage that has no
@@ -241,9 +243,14 @@ int32_t compress_impl(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const v
     skip(1);
     skip(2);
   } else {
-    if ((e = snapkv::launch_score_stats(p, d, s, events(0))) != hipSuccess)
+    if (ext_lse) {
+      // the caller's normalisers replace the statistics pass, which would
+      // also have cleared the vote's digit histogram
+      if ((e = snapkv::launch_clear_hist(p, s, events(0))) != hipSuccess)
+        return hip_fail(e, "snapkv_clear_hist launch");
+    } else if ((e = snapkv::launch_score_stats(p, d, s, events(0))) != hipSuccess)
       return hip_fail(e, "snapkv_score_stats launch");
-    if ((e = snapkv::launch_score_vote(p, d, s, events(1))) != hipSuccess)
+    if ((e = snapkv::launch_score_vote(p, d, s, events(1), ext_lse)) != hipSuccess)
       return hip_fail(e, "snapkv_score_vote launch");
     if ((e = snapkv::launch_select(p, s, events(2))) != hipSuccess)
       return hip_fail(e, "snapkv_select launch");
@@ -276,7 +283,22 @@ int32_t snapkv_compress(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads
                         void* stream) {
   return compress_impl(batch, num_q_heads, num_kv_heads, head_dim, q_win, k, v, seq_lens, window,
                        kernel_size, pool_mode, budget, out_k, out_v, out_idx, workspace,
-                       workspace_bytes, stream, nullptr);
+                       workspace_bytes, stream, nullptr, nullptr);
+}
+
+int32_t snapkv_compress_from_lse(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, const void* q_win, const void* k,
+                                 const void* v, const int32_t* seq_lens, int32_t window,
+                                 const float* window_lse, int32_t kernel_size,
+                                 int32_t pool_mode, int32_t budget, void* out_k, void* out_v,
+                                 int32_t* out_idx, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (window_lse == nullptr) return fail(SNAPKV_ERR_INVALID_ARGUMENT, "window_lse is NULL");
+  if ((reinterpret_cast<uintptr_t>(window_lse) & 3u) != 0)
+    return fail(SNAPKV_ERR_INVALID_ARGUMENT, "window_lse must be 4-byte aligned");
+  return compress_impl(batch, num_q_heads, num_kv_heads, head_dim, q_win, k, v, seq_lens, window,
+                       kernel_size, pool_mode, budget, out_k, out_v, out_idx, workspace,
+                       workspace_bytes, stream, nullptr, window_lse);
 }
 
 int32_t snapkv_compress_staged(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
@@ -288,7 +310,7 @@ int32_t snapkv_compress_staged(int32_t batch, int32_t num_q_heads, int32_t num_k
                                void* const* stage_events) {
   return compress_impl(batch, num_q_heads, num_kv_heads, head_dim, q_win, k, v, seq_lens, window,
                        kernel_size, pool_mode, budget, out_k, out_v, out_idx, workspace,
-                       workspace_bytes, stream, stage_events);
+                       workspace_bytes, stream, stage_events, nullptr);
 }
 
 int32_t snapkv_window_scores(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

@@ -33,6 +33,8 @@ struct PathParams {
   int32_t* out_idx;   // [batch, Hkv, budget]
   float2* part;       // [batch, Hkv, nchunk, rows_pad] per-chunk (max, sum) in log2 units
   float* pooled;      // [batch, Hkv, pooled_stride] pooled scores c_h[j], j < P
+  const float* window_lse;  // [batch, Hq, W] caller's natural-log normaliser of each window
+                            // row (snapkv_compress_from_lse), or null
   uint32_t* top_hist;   // [batch * Hkv, kTopHistBins] histogram of the pooled keys' top 11 bits
   uint32_t* sel_table;  // [batch * Hkv, table_stride, 2] per kSegment positions: keys above /
                         // equal to the threshold before the segment
@@ -61,8 +63,12 @@ struct StageEvents {
 // Stage kernels: grids of work items.
 hipError_t launch_score_stats(const PathParams& p, int head_dim, hipStream_t stream,
                               StageEvents ev = {});
+// with ext_lse the row normalisers come from PathParams::window_lse
 hipError_t launch_score_vote(const PathParams& p, int head_dim, hipStream_t stream,
-                             StageEvents ev = {});
+                             StageEvents ev = {}, bool ext_lse = false);
+// zeroes top_hist of the scored heads (stands in for the statistics pass,
+// which does it otherwise)
+hipError_t launch_clear_hist(const PathParams& p, hipStream_t stream, StageEvents ev = {});
 hipError_t launch_select(const PathParams& p, hipStream_t stream, StageEvents ev = {});
 hipError_t launch_gather(const PathParams& p, int head_dim, hipStream_t stream,
                          StageEvents ev = {});

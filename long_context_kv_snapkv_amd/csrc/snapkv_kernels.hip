@@ -6,6 +6,10 @@
 //                                               and its count table
 //   snapkv_gather       (row block, head, prompt)  slots -> positions, rows
 //
+//   snapkv_clear_hist   (head, prompt)          zeroes the vote's digit
+//                                               histogram when the caller
+//                                               supplies the normalisers
+//
 // A compress call runs the four in stream order; the kernel boundaries carry
 // every hand-off between stages (no inter-workgroup waiting or flags). The
 // score export runs stats and vote only, with the caller's buffer as the
@@ -38,7 +42,7 @@ __global__ void __launch_bounds__(kThreads) snapkv_score_stats(const PathParams 
   snapkv_score_stats_item<D, RTW>(p, sm, b, h, c);
 }
 
-template <int D, int RTW>
+template <int D, int RTW, bool EXT_LSE>
 __global__ void __launch_bounds__(kThreads) snapkv_score_vote(const PathParams p) {
   __shared__ VoteSmem<D> sm;
   const int b = blockIdx.z, h = blockIdx.y, c = blockIdx.x;
@@ -50,7 +54,16 @@ __global__ void __launch_bounds__(kThreads) snapkv_score_vote(const PathParams p
     for (int j = max(P, 0) + (int)threadIdx.x; j < p.pooled_stride; j += kThreads) row[j] = 0.f;
   }
   if (!is_scored(p, b) || c >= nvote) return;
-  snapkv_score_vote_item<D, RTW>(p, sm, b, h, c);
+  snapkv_score_vote_item<D, RTW, EXT_LSE>(p, sm, b, h, c);
+}
+
+// With the caller's row normalisers there is no statistics pass to clear the
+// vote's histogram of top radix digits: one workgroup per head does it.
+__global__ void __launch_bounds__(kThreads) snapkv_clear_hist(const PathParams p) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  if (!is_scored(p, b)) return;
+  uint4* top = reinterpret_cast<uint4*>(p.top_hist + (size_t)(b * p.hkv + h) * kTopBins);
+  for (int i = threadIdx.x; i < kTopBins / 4; i += kThreads) top[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 __global__ void __launch_bounds__(kThreads) snapkv_select(const PathParams p) {
@@ -115,11 +128,19 @@ hipError_t launch_score_stats(const PathParams& p, int head_dim, hipStream_t str
 }
 
 hipError_t launch_score_vote(const PathParams& p, int head_dim, hipStream_t stream,
-                             StageEvents ev) {
+                             StageEvents ev, bool ext_lse) {
   return dispatch_dim_rtw(head_dim, row_tiles_per_wave(p), [&](auto d, auto rtw) {
-    return launch(snapkv_score_vote<decltype(d)::value, decltype(rtw)::value>,
-                  dim3(p.nchunk, p.hkv, p.batch), stream, ev, p);
+    const dim3 grid(p.nchunk, p.hkv, p.batch);
+    if (ext_lse)
+      return launch(snapkv_score_vote<decltype(d)::value, decltype(rtw)::value, true>, grid,
+                    stream, ev, p);
+    return launch(snapkv_score_vote<decltype(d)::value, decltype(rtw)::value, false>, grid,
+                  stream, ev, p);
   });
+}
+
+hipError_t launch_clear_hist(const PathParams& p, hipStream_t stream, StageEvents ev) {
+  return launch(snapkv_clear_hist, dim3(p.hkv, p.batch), stream, ev, p);
 }
 
 hipError_t launch_select(const PathParams& p, hipStream_t stream, StageEvents ev) {

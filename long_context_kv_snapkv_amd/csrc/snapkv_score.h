@@ -271,12 +271,13 @@ __device__ __forceinline__ void snapkv_score_stats_item(const PathParams& p, Sta
 
 // ----------------------------------------------------------------- vote ---
 // Loads are issued in the order the item needs them to be complete: first
-// the per-chunk statistics (the first kPartBatch per thread), then the
-// query rows and the first key tile. The lse merge then waits only for the
-// statistics while the rest is still in flight.
+// the row normalisers' inputs (the first kPartBatch per-chunk statistics per
+// thread, or with EXT_LSE the caller's log-sum-exp of each row), then the
+// query rows and the first key tile. The lse computation then waits only
+// for its own inputs while the rest is still in flight.
 constexpr int kPartBatch = 8;
 
-template <int D, int RTW>
+template <int D, int RTW, bool EXT_LSE>
 __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, VoteSmem<D>& sm,
                                                        int b, int h, int c) {
   const int L = p.tab.len[b];
@@ -299,11 +300,17 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
   const int row = tid % span, sub = tid / span;
   const bool row_ok = row < p.rows;
   const int row_c = min(row, p.rows - 1);
-  float2 pe[kPartBatch];
+  float2 pe[EXT_LSE ? 1 : kPartBatch];
+  float ext = 0.f;
+  if (EXT_LSE) {
+    // the group's rows are consecutive in [batch, H_q, W]
+    ext = p.window_lse[(size_t)(b * p.hq + h * p.group) * p.window + min(tid, p.rows - 1)];
+  } else {
 #pragma unroll
-  for (int u = 0; u < kPartBatch; ++u)
-    pe[u] = part[(size_t)min(sub + u * tpr, nch - 1) * p.rows_pad + row_c];
-  asm volatile("" ::: "memory");  // statistics loads stay older than the rest
+    for (int u = 0; u < kPartBatch; ++u)
+      pe[u] = part[(size_t)min(sub + u * tpr, nch - 1) * p.rows_pad + row_c];
+  }
+  asm volatile("" ::: "memory");  // these loads stay older than the rest
 
   bf16x8 qf[RTW][D / 16];
   KeyStream<D> ks{{}, {}, p.k + ((size_t)p.tab.off[b] * p.hkv + h) * D, (size_t)p.hkv * D,
@@ -313,9 +320,13 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
                             [&] { ks.prefetch(); });
 
   for (int i = tid; i < kTopBins; i += kThreads) sm.top[i] = 0u;
-  // lse of every row: `tpr` threads share a row, each merging every tpr-th
-  // chunk (max first, then the rescaled sum), then a fixed-order fold in LDS
-  {
+  if (EXT_LSE) {
+    // natural-log normaliser -> log2 units of the scaled logits
+    if (tid < p.rows_pad) sm.lse[tid] = tid < p.rows ? ext * 1.4426950408889634f : kInf;
+    lds_barrier();
+  } else {
+    // lse of every row: `tpr` threads share a row, each merging every tpr-th
+    // chunk (max first, then the rescaled sum), then a fixed-order fold in LDS
     float m = -kInf, s = 0.f;
 #pragma unroll
     for (int u = 0; u < kPartBatch; ++u)

@@ -72,6 +72,9 @@ def load_library():
     lib.snapkv_compress.restype = _i32
     lib.snapkv_compress_staged.argtypes = compress_args + [ctypes.POINTER(_vp)]
     lib.snapkv_compress_staged.restype = _i32
+    lib.snapkv_compress_from_lse.argtypes = [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _pi32, _i32,
+                                             _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
+    lib.snapkv_compress_from_lse.restype = _i32
     lib.snapkv_window_scores.argtypes = [_i32, _i32, _i32, _i32, _vp, _vp, _pi32, _i32,
                                          _i32, _i32, _vp, _i32, _vp, _sz, _vp]
     lib.snapkv_window_scores.restype = _i32
@@ -161,6 +164,23 @@ def _shapes(q_win, k, seq_vals):
     return batch, hq, hkv, d, w
 
 
+def _outputs(batch, hkv, budget, d, dev, out_k, out_v, out_idx):
+    """The caller's output tensors (checked), or new ones."""
+    if out_k is None:
+        out_k = torch.empty((batch, hkv, budget, d), dtype=torch.bfloat16, device=dev)
+    if out_v is None:
+        out_v = torch.empty((batch, hkv, budget, d), dtype=torch.bfloat16, device=dev)
+    if out_idx is None:
+        out_idx = torch.empty((batch, hkv, budget), dtype=torch.int32, device=dev)
+    _check_tensor("out_k", out_k, 4)
+    _check_tensor("out_v", out_v, 4)
+    _check_tensor("out_idx", out_idx, 3, torch.int32)
+    if tuple(out_k.shape) != (batch, hkv, budget, d) or out_v.shape != out_k.shape \
+            or tuple(out_idx.shape) != (batch, hkv, budget):
+        raise ValueError("output shapes must be [batch, H_kv, budget, D] and [batch, H_kv, budget]")
+    return out_k, out_v, out_idx
+
+
 def snapkv_compress(q_win: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                     seq_lens: Sequence[int], window: int, kernel_size: int, pool_mode,
                     budget: int, *, out_k: Optional[torch.Tensor] = None,
@@ -184,18 +204,7 @@ def snapkv_compress(q_win: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if w != window:
         raise ValueError(f"q_win holds {w} window rows but window={window}")
     dev = q_win.device
-    if out_k is None:
-        out_k = torch.empty((batch, hkv, budget, d), dtype=torch.bfloat16, device=dev)
-    if out_v is None:
-        out_v = torch.empty((batch, hkv, budget, d), dtype=torch.bfloat16, device=dev)
-    if out_idx is None:
-        out_idx = torch.empty((batch, hkv, budget), dtype=torch.int32, device=dev)
-    _check_tensor("out_k", out_k, 4)
-    _check_tensor("out_v", out_v, 4)
-    _check_tensor("out_idx", out_idx, 3, torch.int32)
-    if tuple(out_k.shape) != (batch, hkv, budget, d) or out_v.shape != out_k.shape \
-            or tuple(out_idx.shape) != (batch, hkv, budget):
-        raise ValueError("output shapes must be [batch, H_kv, budget, D] and [batch, H_kv, budget]")
+    out_k, out_v, out_idx = _outputs(batch, hkv, budget, d, dev, out_k, out_v, out_idx)
     if workspace is None:
         workspace = new_workspace(hq, hkv, d, vals, window, dev)
     args = (batch, hq, hkv, d, _ptr(q_win), _ptr(k), _ptr(v), arr, window, kernel_size,
@@ -210,6 +219,39 @@ def snapkv_compress(q_win: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         _check(lib.snapkv_compress_staged(*args, None))
     else:
         _check(lib.snapkv_compress(*args))
+    return out_k, out_v, out_idx
+
+
+def snapkv_compress_from_lse(q_win: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                             seq_lens: Sequence[int], window: int, window_lse: torch.Tensor,
+                             kernel_size: int, pool_mode, budget: int, *,
+                             out_k: Optional[torch.Tensor] = None,
+                             out_v: Optional[torch.Tensor] = None,
+                             out_idx: Optional[torch.Tensor] = None,
+                             workspace: Optional[torch.Tensor] = None, stream=None):
+    """snapkv_compress with the window rows' natural-log normalisers supplied
+    (float32 [batch, H_q, W]); see include/snapkv.h."""
+    lib = load_library()
+    _check_tensor("q_win", q_win, 4)
+    _check_tensor("k", k, 3)
+    _check_tensor("v", v, 3)
+    _check_tensor("window_lse", window_lse, 3, torch.float32)
+    arr, vals = _lens(seq_lens)
+    batch, hq, hkv, d, w = _shapes(q_win, k, vals)
+    if v.shape != k.shape:
+        raise ValueError("k and v shapes differ")
+    if w != window:
+        raise ValueError(f"q_win holds {w} window rows but window={window}")
+    if tuple(window_lse.shape) != (batch, hq, window):
+        raise ValueError("window_lse must be [batch, H_q, W]")
+    dev = q_win.device
+    out_k, out_v, out_idx = _outputs(batch, hkv, budget, d, dev, out_k, out_v, out_idx)
+    if workspace is None:
+        workspace = new_workspace(hq, hkv, d, vals, window, dev)
+    _check(lib.snapkv_compress_from_lse(
+        batch, hq, hkv, d, _ptr(q_win), _ptr(k), _ptr(v), arr, window, _ptr(window_lse),
+        kernel_size, pool_mode_code(pool_mode), budget, _ptr(out_k), _ptr(out_v), _ptr(out_idx),
+        _ptr(workspace), workspace.numel(), _stream(stream, dev)))
     return out_k, out_v, out_idx
 
 

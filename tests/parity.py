@@ -151,3 +151,39 @@ def full_check(x, window, kernel, pool, budget, ref=None, res=None):
             np.testing.assert_array_equal(res["out_idx"][b], ref.out_idx[b])
             np.testing.assert_array_equal(res["out_k"][b], ref.out_k[b])
     return dict(worst_score_ratio=worst, exact_heads=exact, res=res, ref=ref)
+
+
+def torch_window_lse(q, k, seq_lens, window):
+    """Window-row normalisers [batch, H_q, W] computed on the device in
+    float32 with plain torch ops, the way a caller's prefill attention
+    would hand them over (rows of prompts shorter than the window are -inf)."""
+    batch, hq, w, d = q.shape
+    hkv = k.shape[1]
+    g = hq // hkv
+    out = torch.full((batch, hq, w), float("-inf"), dtype=torch.float32, device=q.device)
+    off = 0
+    for b, length in enumerate(seq_lens):
+        p = length - window
+        i = torch.arange(w, device=q.device).repeat(g)
+        visible = torch.arange(length, device=q.device)[None, :] <= (p + i)[:, None]
+        for h in range(hkv):
+            kh = k[off:off + length, h].float().t().contiguous()
+            qg = q[b, h * g:(h + 1) * g].float().reshape(g * w, d)
+            logits = (qg @ kh) / (d ** 0.5)
+            logits = logits.masked_fill(~visible, float("-inf"))
+            out[b, h * g:(h + 1) * g] = torch.logsumexp(logits, dim=1).reshape(g, w)
+        off += length
+    return out
+
+
+def run_gpu_from_lse(x, window, kernel, pool, budget, lse):
+    """snapkv_compress_from_lse on x with normalisers lse (float32 numpy or
+    device tensor), as numpy outputs."""
+    q, k, v = upload(x)
+    t = lse if isinstance(lse, torch.Tensor) else torch.from_numpy(
+        np.ascontiguousarray(lse, dtype=np.float32)).cuda()
+    out_k, out_v, out_idx = skv.snapkv_compress_from_lse(
+        q, k, v, x.seq_lens.tolist(), window, t, kernel, pool, budget)
+    torch.cuda.synchronize()
+    return dict(out_k=bits_from_device(out_k), out_v=bits_from_device(out_v),
+                out_idx=out_idx.cpu().numpy())

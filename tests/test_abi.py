@@ -22,8 +22,9 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = skv.header_functions()
-    assert len(names) == 7, names
+    assert len(names) == 8, names
     assert "snapkv_compress_staged" in names
+    assert "snapkv_compress_from_lse" in names
     for name in names:
         assert hasattr(lib, name), name
 
@@ -109,3 +110,18 @@ def test_pooling_names_match_page_snippet():
     params = inspect.signature(skv.compress).parameters
     for name in ("window_size", "max_capacity_prompt", "kernel_size", "pooling"):
         assert name in params
+
+
+def test_compress_from_lse_validation(lib):
+    lens = (ctypes.c_int32 * 1)(100)
+
+    def call(lse, ws_bytes=1, kernel=5):
+        return lib.snapkv_compress_from_lse(1, 4, 2, 128, FAKE, FAKE, FAKE, lens, 8, lse,
+                                            kernel, 0, 32, FAKE, FAKE, FAKE, FAKE,
+                                            ws_bytes, None)
+
+    assert call(None) == 1 and "window_lse" in skv.snapkv_last_error()
+    assert call(FAKE + 2) == 1 and "window_lse" in skv.snapkv_last_error()
+    assert call(FAKE, kernel=4) == 1
+    # a 4-byte aligned normaliser buffer passes; the undersized workspace stops the call
+    assert call(FAKE + 4) == 3

@@ -1,0 +1,135 @@
+"""GPU parity of snapkv_compress_from_lse: the compression driven by window-row
+normalisers that the caller's prefill attention supplies.
+
+The oracle takes the same float32 normalisers (widened to float64) through
+window_vote_from_lse, so the comparison checks the kernels' use of the
+supplied values, including normalisers that are not the exact ones.
+Acceptance as for snapkv_compress: identical kept sets wherever the oracle's
+pooled scores leave a gap above the tolerance band, bit-exact gather, and
+the fixed layout of the outputs.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import (check_index_sets, check_structure_and_gather, run_gpu,
+                    run_gpu_from_lse, torch_window_lse, upload)
+from synth import WORKLOADS, make_custom, make_layer
+
+pytestmark = pytest.mark.gpu
+
+needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")
+
+CASES = [
+    # lens, h_q, h_kv, d, window, kernel, pool, budget
+    ([3000, 2500], 16, 4, 128, 64, 5, "avg", 1024),
+    ([500], 6, 2, 128, 20, 7, "avg", 100),           # 60 rows, not a multiple of 32
+    ([700], 6, 2, 64, 24, 9, "max", 80),             # D = 64
+    ([1200], 64, 8, 128, 64, 7, "max", 300),         # 512 rows (maximum)
+    ([64, 300, 65, 5, 1000], 8, 2, 128, 32, 5, "avg", 96),  # ragged, some kept whole
+    ([40000], 8, 2, 128, 16, 7, "max", 2048),        # streaming selection
+]
+
+
+def _oracle_lse_f32(x, window, budget):
+    """Oracle normalisers rounded to float32; rows the library must not read
+    (prompts kept whole) are set to NaN so that reading them would show."""
+    lse = oracle.window_lse(x.q_win, x.k, x.seq_lens, window).astype(np.float32)
+    for b, length in enumerate(x.seq_lens.tolist()):
+        if length <= budget:
+            lse[b] = np.nan
+    return lse
+
+
+def _check(x, window, kernel, pool, budget, lse32):
+    res = run_gpu_from_lse(x, window, kernel, pool, budget, lse32)
+    ref = oracle.compress(x.q_win, x.k, x.v, x.seq_lens.tolist(), window, kernel, pool,
+                          budget, lse=lse32.astype(np.float64))
+    check_structure_and_gather(res, x, window, budget)
+    exact = check_index_sets(res["out_idx"], ref.pooled, x.seq_lens.tolist(), window, budget)
+    return res, ref, exact
+
+
+@needs_gpu
+@pytest.mark.parametrize("case", CASES, ids=[f"case{i}" for i in range(len(CASES))])
+def test_oracle_normalisers(case):
+    lens, hq, hkv, d, window, kernel, pool, budget = case
+    print(f"[from_lse] {case}", flush=True)
+    x = make_custom(lens, hq, hkv, d, window, seed=sum(lens) % 89)
+    _check(x, window, kernel, pool, budget, _oracle_lse_f32(x, window, budget))
+
+
+@needs_gpu
+def test_perturbed_normalisers_are_followed():
+    # row-dependent offsets reweight the window rows: the selection then
+    # differs from snapkv_compress's and must follow the supplied values
+    x = make_custom([6000, 4100], 32, 8, 128, 32, seed=11)
+    lse = _oracle_lse_f32(x, 32, 512)
+    rng = np.random.default_rng(12)
+    lse += rng.uniform(-3.0, 3.0, size=lse.shape).astype(np.float32)
+    print("[from_lse] perturbed", flush=True)
+    res, ref, _ = _check(x, 32, 7, "avg", 512, lse)
+    # the tolerance band leaves few positions open: nearly every kept
+    # position is one the oracle's scores force
+    m = 512 - 32
+    for pooled in ref.pooled:
+        for o in pooled:
+            srt = np.sort(o)[::-1]
+            forced = (o > srt[m] + 1e-3 * srt[m - 1] + 1e-6 * srt[0]).sum()
+            assert forced >= 0.8 * m, forced
+    plain = run_gpu(x, 32, 7, "avg", 512)
+    assert (plain["out_idx"] != res["out_idx"]).any()
+
+
+@needs_gpu
+def test_llama3_8b_16k_with_device_normalisers():
+    # full size, normalisers computed on the device in float32 (the bench's
+    # launch configuration); the result must agree with the oracle's own
+    # compression and with snapkv_compress where the oracle leaves no near-tie
+    w = WORKLOADS["llama3_8b_16k"]
+    x = make_layer(w)
+    print(f"[from_lse] llama3_8b_16k lens={x.seq_lens.tolist()}", flush=True)
+    q, k, _ = upload(x)
+    lens = x.seq_lens.tolist()
+    lse = torch_window_lse(q, k, lens, w.window)
+    ref_lse = oracle.window_lse(x.q_win, x.k, x.seq_lens, w.window)
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-5, atol=1e-5)
+    res = run_gpu_from_lse(x, w.window, w.kernel, w.pool, w.budget, lse)
+    ref = oracle.compress(x.q_win, x.k, x.v, lens, w.window, w.kernel, w.pool, w.budget)
+    check_structure_and_gather(res, x, w.window, w.budget)
+    # max pooling leaves plateaus: ties at the threshold are common, and the
+    # band rule decides every position outside them
+    check_index_sets(res["out_idx"], ref.pooled, lens, w.window, w.budget)
+    plain = run_gpu(x, w.window, w.kernel, w.pool, w.budget)
+    m = w.budget - w.window
+    for b, length in enumerate(lens):
+        for h, o in enumerate(ref.pooled[b]):
+            srt = np.sort(o)[::-1]
+            if srt[m - 1] - srt[m] > 1e-3 * srt[m - 1] + 1e-6 * srt[0]:
+                np.testing.assert_array_equal(res["out_idx"][b, h], plain["out_idx"][b, h])
+                np.testing.assert_array_equal(res["out_k"][b, h], plain["out_k"][b, h])
+
+
+@needs_gpu
+def test_repeated_calls_are_bitwise_identical():
+    x = make_custom([9000], 32, 8, 128, 32, seed=13)
+    lse = _oracle_lse_f32(x, 32, 1024)
+    a = run_gpu_from_lse(x, 32, 7, "avg", 1024, lse)
+    b = run_gpu_from_lse(x, 32, 7, "avg", 1024, lse)
+    for key in a:
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+@needs_gpu
+def test_binding_rejects_a_wrong_normaliser_shape():
+    import long_context_kv_snapkv_amd as skv
+    x = make_custom([300], 8, 2, 128, 16, seed=14)
+    q, k, v = upload(x)
+    bad = torch.zeros((1, 8, 15), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        skv.snapkv_compress_from_lse(q, k, v, [300], 16, bad, 5, "avg", 64)
+    with pytest.raises(ValueError):
+        skv.snapkv_compress_from_lse(q, k, v, [300], 16, bad.double()[:, :, :1].expand(1, 8, 16),
+                                     5, "avg", 64)
