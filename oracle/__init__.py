@@ -26,3 +26,12 @@ from .snapkv_oracle import (  # noqa: F401
     window_vote,
     window_vote_from_lse,
 )
+from .kv_quant import (  # noqa: F401
+    Int4Result,
+    compress_int4,
+    dequantize_int4,
+    pack_int4,
+    quantize_cache,
+    quantize_rows_int4,
+    unpack_int4,
+)
