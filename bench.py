@@ -244,6 +244,30 @@ def main():
     torch.cuda.synchronize()
     ms_step_lse = t_start.elapsed_time(t_end) / args.steps
 
+    # the same compression storing the kept rows at 4 bits per value
+    # (snapkv_compress_int4)
+    for s_ in sets:
+        s_["kq"] = torch.empty((batch, hkv, B, d // 2), dtype=torch.uint8, device=dev)
+        s_["vq"] = torch.empty_like(s_["kq"])
+        s_["ks"] = torch.empty((batch, hkv, B), dtype=torch.float32, device=dev)
+        s_["vs"] = torch.empty_like(s_["ks"])
+
+    def step_int4(i):
+        s = sets[i % nsets]
+        skv.snapkv_compress_int4(s["q"], s["k"], s["v"], lens, w.window, w.kernel, w.pool, B,
+                                 out=(s["kq"], s["ks"], s["vq"], s["vs"], s["oi"]),
+                                 workspace=ws, stream=stream)
+
+    for i in range(args.warmup):
+        step_int4(i)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step_int4(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step_int4 = t_start.elapsed_time(t_end) / args.steps
+
     sbytes = stage_bytes(w, lens)
     dominant = max(stage_ms, key=stage_ms.get)
     kernel_ms = stage_ms[dominant]
@@ -286,6 +310,12 @@ def main():
                      "unit": "tokens/s/layer",
                      "note": "snapkv_compress_from_lse: window-row log-sum-exp supplied by "
                              "the caller's prefill, computed before the timed region"},
+        "int4": {"ms_per_step": round(ms_step_int4, 5),
+                 "value": round(sum(lens) / (ms_step_int4 * 1e-3), 1),
+                 "unit": "tokens/s/layer",
+                 "cache_bytes": 2 * batch * hkv * B * (d // 2 + 4),
+                 "note": "snapkv_compress_int4: kept rows stored as 4-bit codes with a "
+                         "float32 scale per row"},
     }
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)

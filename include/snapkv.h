@@ -183,6 +183,40 @@ int32_t snapkv_compress_from_lse(int32_t batch, int32_t num_q_heads,
                                  size_t workspace_bytes, void* stream);
 
 /*
+ * snapkv_compress with the compressed cache stored at 4 bits per value
+ * (Scissorhands page, section "4ビット量子化との併用" and its FAQ on
+ * quantisation: token reduction and a 4-bit value width are separate levers
+ * that combine). The selection is snapkv_compress's (identical out_idx);
+ * each kept K or V row x of one head (D values) is stored as
+ *
+ *   scale = amax / 7,  code_d = rint(x_d * (7 / amax)) in [-7, 7]
+ *
+ * with amax = max_d |x_d|, in float32 with round-to-nearest-even (rint ties
+ * to even); x_d ~= code_d * scale within scale / 2. A zero row has codes 0
+ * and scale 0. K and V must be finite.
+ *
+ *   out_kq, out_vq  device uint8 [batch, H_kv, B, D/2]: codes as two's-
+ *                   complement nibbles, element 2i in the low nibble of byte i
+ *   out_ks, out_vs  device float32 [batch, H_kv, B]: the rows' scales
+ *   window_lse      NULL (the statistics pass runs) or as for
+ *                   snapkv_compress_from_lse
+ *
+ * Slots past min(L_b, B) hold codes 0, scale 0 and index -1. Other
+ * arguments, the workspace and errors as for snapkv_compress (the scale
+ * buffers must also be non-null and 16-byte aligned; a non-null window_lse
+ * 4-byte aligned).
+ */
+int32_t snapkv_compress_int4(int32_t batch, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim,
+                             const void* q_win, const void* k, const void* v,
+                             const int32_t* seq_lens, int32_t window,
+                             const float* window_lse, int32_t kernel_size,
+                             int32_t pool_mode, int32_t budget,
+                             uint8_t* out_kq, float* out_ks, uint8_t* out_vq,
+                             float* out_vs, int32_t* out_idx, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
  * The pooled scores c_h (steps 1-2) of every prompt with P = L - W >= 1,
  * whatever its length relative to a budget; raw scores when kernel_size = 1.
  *

@@ -24,6 +24,7 @@ from .snapkv import (  # noqa: F401
     pool_mode_code,
     snapkv_compress,
     snapkv_compress_from_lse,
+    snapkv_compress_int4,
     snapkv_last_error,
     snapkv_stage_name,
     snapkv_status_string,

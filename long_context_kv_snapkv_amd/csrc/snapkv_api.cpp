@@ -138,7 +138,7 @@ int32_t check_pool(int32_t kernel, int32_t pool_mode) {
 snapkv::PathParams path_params(const Plan& pl, const void* q, const void* k, const void* v,
                                void* ws, int32_t budget, int32_t kernel, int32_t pool_mode,
                                bool score_all) {
-  snapkv::PathParams p;
+  snapkv::PathParams p{};
   std::memset(&p, 0, sizeof(p));
   char* w = static_cast<char*>(ws);
   p.q = static_cast<const uint16_t*>(q);
@@ -193,13 +193,25 @@ int32_t check_tensors(const void* q_win, const void* k, const void* v, const voi
   return SNAPKV_OK;
 }
 
+// Output buffers of the 4-bit form (snapkv_compress_int4).
+struct Int4Out {
+  uint8_t* kq;
+  float* ks;
+  uint8_t* vq;
+  float* vs;
+};
+
 int32_t compress_impl(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const void* q_win,
                       const void* k, const void* v, const int32_t* seq_lens, int32_t window,
                       int32_t kernel, int32_t pool_mode, int32_t budget, void* out_k,
                       void* out_v, int32_t* out_idx, void* workspace, size_t workspace_bytes,
-                      void* stream, void* const* stage_events, const float* window_lse) {
-  int32_t st = check_tensors(q_win, k, v, out_k, out_v, out_idx);
+                      void* stream, void* const* stage_events, const float* window_lse,
+                      const Int4Out* q4 = nullptr) {
+  int32_t st = q4 ? check_tensors(q_win, k, v, q4->kq, q4->vq, out_idx)
+                  : check_tensors(q_win, k, v, out_k, out_v, out_idx);
   if (st != SNAPKV_OK) return st;
+  if (q4 && (!q4->ks || !q4->vs || misaligned(q4->ks) || misaligned(q4->vs)))
+    return fail(SNAPKV_ERR_INVALID_ARGUMENT, "scale buffers must be non-null and 16-byte aligned");
   Plan pl;
   st = make_plan(batch, hq, hkv, d, seq_lens, window, &pl);
   if (st != SNAPKV_OK) return st;
@@ -215,6 +227,12 @@ int32_t compress_impl(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const v
       path_params(pl, q_win, k, v, workspace, budget, kernel, pool_mode, /*score_all=*/false);
   p.out_k = static_cast<uint16_t*>(out_k);
   p.out_v = static_cast<uint16_t*>(out_v);
+  if (q4) {
+    p.out_kq = q4->kq;
+    p.out_ks = q4->ks;
+    p.out_vq = q4->vq;
+    p.out_vs = q4->vs;
+  }
   p.out_idx = out_idx;
   p.window_lse = window_lse;
   const bool ext_lse = window_lse != nullptr;
@@ -255,7 +273,7 @@ int32_t compress_impl(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const v
     if ((e = snapkv::launch_select(p, s, events(2))) != hipSuccess)
       return hip_fail(e, "snapkv_select launch");
   }
-  if ((e = snapkv::launch_gather(p, d, s, events(3))) != hipSuccess)
+  if ((e = snapkv::launch_gather(p, d, s, events(3), q4 != nullptr)) != hipSuccess)
     return hip_fail(e, "snapkv_gather launch");
   return SNAPKV_OK;
 }
@@ -311,6 +329,21 @@ int32_t snapkv_compress_staged(int32_t batch, int32_t num_q_heads, int32_t num_k
   return compress_impl(batch, num_q_heads, num_kv_heads, head_dim, q_win, k, v, seq_lens, window,
                        kernel_size, pool_mode, budget, out_k, out_v, out_idx, workspace,
                        workspace_bytes, stream, stage_events, nullptr);
+}
+
+int32_t snapkv_compress_int4(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, const void* q_win, const void* k, const void* v,
+                             const int32_t* seq_lens, int32_t window, const float* window_lse,
+                             int32_t kernel_size, int32_t pool_mode, int32_t budget,
+                             uint8_t* out_kq, float* out_ks, uint8_t* out_vq, float* out_vs,
+                             int32_t* out_idx, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (window_lse != nullptr && (reinterpret_cast<uintptr_t>(window_lse) & 3u) != 0)
+    return fail(SNAPKV_ERR_INVALID_ARGUMENT, "window_lse must be 4-byte aligned");
+  const Int4Out q4{out_kq, out_ks, out_vq, out_vs};
+  return compress_impl(batch, num_q_heads, num_kv_heads, head_dim, q_win, k, v, seq_lens, window,
+                       kernel_size, pool_mode, budget, nullptr, nullptr, out_idx, workspace,
+                       workspace_bytes, stream, nullptr, window_lse, &q4);
 }
 
 int32_t snapkv_window_scores(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

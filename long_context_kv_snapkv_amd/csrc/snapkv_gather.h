@@ -15,7 +15,8 @@
 // Each lane moves one 16-byte piece of a row, so a wave moves whole rows:
 // reads are row-granular gathers from the packed [T, H_kv, D] cache, writes
 // are contiguous. All of a thread's loads are issued before its stores.
-// Rows are bit copies; out_idx is written here for every slot.
+// Rows are bit copies; out_idx is written here for every slot. The 4-bit
+// instance stores each row instead as codes and a scale (quantize_piece_int4).
 #pragma once
 
 #include "snapkv_device.h"
@@ -90,7 +91,34 @@ __device__ __forceinline__ void locate_kept(const PathParams& p, GatherSmem& s, 
   __syncthreads();
 }
 
-template <int D>
+// 4-bit form of one 16-byte piece (8 bf16 values) of a row spread over
+// PIECES consecutive lanes: the row's largest magnitude (compared as bf16
+// magnitude bits, which order finite values) gives scale = amax / 7 and
+// codes rint(x * (7 / amax)) in [-7, 7], in float32 with IEEE rounding;
+// returns the 8 codes as nibbles, element e at bits 4e. Every lane of the
+// group must call it (the reduction reads the other lanes).
+template <int PIECES>
+__device__ __forceinline__ uint32_t quantize_piece_int4(const u32x4& w, float& scale) {
+  uint32_t mx = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mx = max(mx, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+#pragma unroll
+  for (int o = 1; o < PIECES; o <<= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+  const float amax = __uint_as_float(mx << 16);
+  scale = amax / 7.0f;
+  const float inv = amax > 0.f ? 7.0f / amax : 0.f;
+  uint32_t out = 0u;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t word = w[e >> 1];
+    const float x = __uint_as_float((e & 1) ? (word & 0xFFFF0000u) : (word << 16));
+    const int c = min(max((int)rintf(x * inv), -7), 7);
+    out |= ((uint32_t)c & 0xFu) << (4 * e);
+  }
+  return out;
+}
+
+template <int D, bool INT4>
 __device__ __forceinline__ void snapkv_gather_item(const PathParams& p, GatherSmem& gs, int b,
                                                    int h, int rb) {
   constexpr int PIECES = D / 8;
@@ -125,13 +153,33 @@ __device__ __forceinline__ void snapkv_gather_item(const PathParams& p, GatherSm
       vx[q] = *reinterpret_cast<const u32x4*>(vsrc + (size_t)j * tstride + piece * 8);
     }
   }
+  if constexpr (INT4) {
+    // rows of slots >= B and padding rows are zero and quantise to zero
+    const size_t hrow = (size_t)(b * p.hkv + h) * B;
 #pragma unroll
-  for (int q = 0; q < PASSES; ++q) {
-    const int t = tt[q];
-    if (t >= B) continue;
-    *reinterpret_cast<u32x4*>(p.out_k + obase + (size_t)t * D + piece * 8) = kx[q];
-    *reinterpret_cast<u32x4*>(p.out_v + obase + (size_t)t * D + piece * 8) = vx[q];
-    if (piece == 0) idx[t] = jj[q];
+    for (int q = 0; q < PASSES; ++q) {
+      float ks, vs;
+      const uint32_t kc = quantize_piece_int4<PIECES>(kx[q], ks);
+      const uint32_t vc = quantize_piece_int4<PIECES>(vx[q], vs);
+      const int t = tt[q];
+      if (t >= B) continue;
+      *reinterpret_cast<uint32_t*>(p.out_kq + (hrow + t) * (D / 2) + piece * 4) = kc;
+      *reinterpret_cast<uint32_t*>(p.out_vq + (hrow + t) * (D / 2) + piece * 4) = vc;
+      if (piece == 0) {
+        idx[t] = jj[q];
+        p.out_ks[hrow + t] = ks;
+        p.out_vs[hrow + t] = vs;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < PASSES; ++q) {
+      const int t = tt[q];
+      if (t >= B) continue;
+      *reinterpret_cast<u32x4*>(p.out_k + obase + (size_t)t * D + piece * 8) = kx[q];
+      *reinterpret_cast<u32x4*>(p.out_v + obase + (size_t)t * D + piece * 8) = vx[q];
+      if (piece == 0) idx[t] = jj[q];
+    }
   }
 }
 

@@ -31,6 +31,13 @@ struct PathParams {
   uint16_t* out_k;    // bf16 [batch, Hkv, budget, D]
   uint16_t* out_v;
   int32_t* out_idx;   // [batch, Hkv, budget]
+  // 4-bit storage (snapkv_compress_int4), else null: codes [batch, Hkv,
+  // budget, D/2] (two's-complement nibbles, even element low) and per-row
+  // scales [batch, Hkv, budget]
+  uint8_t* out_kq;
+  float* out_ks;
+  uint8_t* out_vq;
+  float* out_vs;
   float2* part;       // [batch, Hkv, nchunk, rows_pad] per-chunk (max, sum) in log2 units
   float* pooled;      // [batch, Hkv, pooled_stride] pooled scores c_h[j], j < P
   const float* window_lse;  // [batch, Hq, W] caller's natural-log normaliser of each window
@@ -70,7 +77,8 @@ hipError_t launch_score_vote(const PathParams& p, int head_dim, hipStream_t stre
 // which does it otherwise)
 hipError_t launch_clear_hist(const PathParams& p, hipStream_t stream, StageEvents ev = {});
 hipError_t launch_select(const PathParams& p, hipStream_t stream, StageEvents ev = {});
+// with int4 the rows are stored through out_kq/out_ks/out_vq/out_vs
 hipError_t launch_gather(const PathParams& p, int head_dim, hipStream_t stream,
-                         StageEvents ev = {});
+                         StageEvents ev = {}, bool int4 = false);
 
 }  // namespace snapkv

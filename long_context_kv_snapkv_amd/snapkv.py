@@ -75,6 +75,10 @@ def load_library():
     lib.snapkv_compress_from_lse.argtypes = [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _pi32, _i32,
                                              _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
     lib.snapkv_compress_from_lse.restype = _i32
+    lib.snapkv_compress_int4.argtypes = [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _pi32, _i32, _vp,
+                                         _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                         _vp]
+    lib.snapkv_compress_int4.restype = _i32
     lib.snapkv_window_scores.argtypes = [_i32, _i32, _i32, _i32, _vp, _vp, _pi32, _i32,
                                          _i32, _i32, _vp, _i32, _vp, _sz, _vp]
     lib.snapkv_window_scores.restype = _i32
@@ -253,6 +257,57 @@ def snapkv_compress_from_lse(q_win: torch.Tensor, k: torch.Tensor, v: torch.Tens
         kernel_size, pool_mode_code(pool_mode), budget, _ptr(out_k), _ptr(out_v), _ptr(out_idx),
         _ptr(workspace), workspace.numel(), _stream(stream, dev)))
     return out_k, out_v, out_idx
+
+
+def snapkv_compress_int4(q_win: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                         seq_lens: Sequence[int], window: int, kernel_size: int, pool_mode,
+                         budget: int, *, window_lse: Optional[torch.Tensor] = None,
+                         out: Optional[Sequence[torch.Tensor]] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None):
+    """Compression with the kept rows stored at 4 bits per value. Returns
+    (kq, ks, vq, vs, idx): uint8 codes [batch, H_kv, B, D/2], float32 scales
+    [batch, H_kv, B] for K and V, and int32 indices; see include/snapkv.h.
+    window_lse (float32 [batch, H_q, W]) optionally replaces the statistics
+    pass as in snapkv_compress_from_lse."""
+    lib = load_library()
+    _check_tensor("q_win", q_win, 4)
+    _check_tensor("k", k, 3)
+    _check_tensor("v", v, 3)
+    arr, vals = _lens(seq_lens)
+    batch, hq, hkv, d, w = _shapes(q_win, k, vals)
+    if v.shape != k.shape:
+        raise ValueError("k and v shapes differ")
+    if w != window:
+        raise ValueError(f"q_win holds {w} window rows but window={window}")
+    if window_lse is not None:
+        _check_tensor("window_lse", window_lse, 3, torch.float32)
+        if tuple(window_lse.shape) != (batch, hq, window):
+            raise ValueError("window_lse must be [batch, H_q, W]")
+    dev = q_win.device
+    if out is None:
+        kq = torch.empty((batch, hkv, budget, d // 2), dtype=torch.uint8, device=dev)
+        vq = torch.empty_like(kq)
+        ks = torch.empty((batch, hkv, budget), dtype=torch.float32, device=dev)
+        vs = torch.empty_like(ks)
+        idx = torch.empty((batch, hkv, budget), dtype=torch.int32, device=dev)
+    else:
+        kq, ks, vq, vs, idx = out
+    for name, t, dt, shape in (("kq", kq, torch.uint8, (batch, hkv, budget, d // 2)),
+                               ("vq", vq, torch.uint8, (batch, hkv, budget, d // 2)),
+                               ("ks", ks, torch.float32, (batch, hkv, budget)),
+                               ("vs", vs, torch.float32, (batch, hkv, budget)),
+                               ("idx", idx, torch.int32, (batch, hkv, budget))):
+        _check_tensor(name, t, len(shape), dt)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must have shape {shape}")
+    if workspace is None:
+        workspace = new_workspace(hq, hkv, d, vals, window, dev)
+    _check(lib.snapkv_compress_int4(
+        batch, hq, hkv, d, _ptr(q_win), _ptr(k), _ptr(v), arr, window,
+        _ptr(window_lse) if window_lse is not None else None, kernel_size,
+        pool_mode_code(pool_mode), budget, _ptr(kq), _ptr(ks), _ptr(vq), _ptr(vs), _ptr(idx),
+        _ptr(workspace), workspace.numel(), _stream(stream, dev)))
+    return kq, ks, vq, vs, idx
 
 
 def snapkv_window_scores(q_win: torch.Tensor, k: torch.Tensor, seq_lens: Sequence[int],

@@ -22,7 +22,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = skv.header_functions()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     assert "snapkv_compress_staged" in names
     assert "snapkv_compress_from_lse" in names
     for name in names:
@@ -125,3 +125,19 @@ def test_compress_from_lse_validation(lib):
     assert call(FAKE, kernel=4) == 1
     # a 4-byte aligned normaliser buffer passes; the undersized workspace stops the call
     assert call(FAKE + 4) == 3
+
+
+def test_compress_int4_validation(lib):
+    lens = (ctypes.c_int32 * 1)(100)
+
+    def call(ks=FAKE, vs=FAKE, kq=FAKE, lse=None, ws_bytes=1):
+        return lib.snapkv_compress_int4(1, 4, 2, 128, FAKE, FAKE, FAKE, lens, 8, lse, 5, 0, 32,
+                                        kq, ks, FAKE, vs, FAKE, FAKE, ws_bytes, None)
+
+    assert call(ks=None) == 1 and "scale" in skv.snapkv_last_error()
+    assert call(vs=FAKE + 4) == 1
+    assert call(kq=None) == 1
+    assert call(lse=FAKE + 2) == 1 and "window_lse" in skv.snapkv_last_error()
+    # valid pointers: the undersized workspace stops the call
+    assert call() == 3
+    assert call(lse=FAKE + 4) == 3
