@@ -26,6 +26,7 @@ from .snapkv_oracle import (  # noqa: F401
     window_vote,
     window_vote_from_lse,
 )
+from .decode import attend, decode_compressed, decode_packed  # noqa: F401
 from .kv_quant import (  # noqa: F401
     Int4Result,
     compress_int4,
