@@ -268,6 +268,44 @@ def main():
     torch.cuda.synchronize()
     ms_step_int4 = t_start.elapsed_time(t_end) / args.steps
 
+    # one decode step's attention over the compressed cache against the full
+    # prefill cache (snapkv_decode_attention), each cache streamed from HBM:
+    # enough distinct compressed caches rotate to exceed the Infinity Cache
+    n_kept = [min(L, B) for L in lens]
+    qdec = torch.randn((batch, w.h_q, d), device=dev).to(torch.bfloat16)
+    dout = torch.empty((batch, w.h_q, d), dtype=torch.float32, device=dev)
+    comp_bytes = 2 * batch * hkv * B * d * 2
+    ncomp = max(2, -(-4 * CACHE_BYTES // comp_bytes))
+    comp = [(sets[i % nsets]["ok"].clone(), sets[i % nsets]["ov"].clone()) for i in range(ncomp)]
+    ws_c = torch.empty(max(16, skv.snapkv_decode_workspace_size(
+        w.h_q, hkv, d, n_kept, skv.SNAPKV_CACHE_COMPRESSED, B)), dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(max(16, skv.snapkv_decode_workspace_size(
+        w.h_q, hkv, d, lens, skv.SNAPKV_CACHE_PACKED)), dtype=torch.uint8, device=dev)
+
+    def dec_comp(i):
+        kc, vc = comp[i % ncomp]
+        skv.snapkv_decode_attention(qdec, kc, vc, n_kept, out=dout, workspace=ws_c, stream=stream)
+
+    def dec_full(i):
+        s = sets[i % nsets]
+        skv.snapkv_decode_attention(qdec, s["k"], s["v"], lens, out=dout, workspace=ws_f,
+                                    stream=stream)
+
+    dec_ms = {}
+    for name, fn in (("compressed", dec_comp), ("full", dec_full)):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        dec_ms[name] = t_start.elapsed_time(t_end) / args.steps
+    dec_bytes = {"compressed": 2 * hkv * sum(n_kept) * d * 2,
+                 "full": 2 * hkv * sum(lens) * d * 2}
+    del comp
+
     sbytes = stage_bytes(w, lens)
     dominant = max(stage_ms, key=stage_ms.get)
     kernel_ms = stage_ms[dominant]
@@ -310,6 +348,18 @@ def main():
                      "unit": "tokens/s/layer",
                      "note": "snapkv_compress_from_lse: window-row log-sum-exp supplied by "
                              "the caller's prefill, computed before the timed region"},
+        "decode": {
+            "note": "snapkv_decode_attention: one decode step's attention per layer over the "
+                    "compressed cache (B rows per head) and over the full prefill cache",
+            "compressed_us": round(dec_ms["compressed"] * 1e3, 3),
+            "full_us": round(dec_ms["full"] * 1e3, 3),
+            "speedup": round(dec_ms["full"] / dec_ms["compressed"], 2),
+            "compressed_gbps": round(dec_bytes["compressed"] / (dec_ms["compressed"] * 1e-3) / 1e9,
+                                     1),
+            "full_gbps": round(dec_bytes["full"] / (dec_ms["full"] * 1e-3) / 1e9, 1),
+            "full_hbm_frac": round(dec_bytes["full"] / (dec_ms["full"] * 1e-3) / 1e9 /
+                                   HBM_PEAK_GBPS, 4),
+            "cache_bytes": dec_bytes},
         "int4": {"ms_per_step": round(ms_step_int4, 5),
                  "value": round(sum(lens) / (ms_step_int4 * 1e-3), 1),
                  "unit": "tokens/s/layer",

@@ -237,6 +237,53 @@ int32_t snapkv_window_scores(int32_t batch, int32_t num_q_heads,
                              void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/*
+ * Decode-step attention over a KV cache, to run decoding on the compressed
+ * cache (glossary page "SnapKV(スナップケーブイ)", section "SnapKVの仕組み",
+ * step 4: the decode phase uses the compressed cache; paper page, results:
+ * the generation speed-up at 16K input tokens) or, for comparison, on the
+ * uncompressed one. For prompt b and query head q of KV head h = q / G:
+ *
+ *   out[b, q, :] = sum_t softmax_t(q[b, q, :] . k_t / sqrt(D)) v_t
+ *
+ * over the cache_lens[b] rows t of head h (no mask; the token being generated
+ * is attended only if the caller has appended it to the cache).
+ *
+ *   q        device bf16 [batch, H_q, D]
+ *   layout   SNAPKV_CACHE_COMPRESSED: k_cache, v_cache bf16
+ *              [batch, H_kv, capacity, D] (snapkv_compress's out_k / out_v
+ *              with capacity = B), rows 0 .. cache_lens[b]-1 read;
+ *            SNAPKV_CACHE_PACKED: bf16 [T, H_kv, D] with the prompts back to
+ *              back, T = sum(cache_lens) (the prefill cache); capacity unused
+ *   cache_lens  HOST int32[batch], each >= 1 (and <= capacity when compressed)
+ *   out      device float32 [batch, H_q, D]
+ *   workspace   at least snapkv_decode_workspace_size bytes (per-chunk
+ *            partial softmax; no initialisation, not shared by calls in flight)
+ *
+ * Two kernels on `stream`; computed in float32 from the bf16 inputs with
+ * fixed summation orders (repeated calls give identical bits). Conventions
+ * and error behaviour as for snapkv_compress: SNAPKV_ERR_INVALID_ARGUMENT
+ * for null or misaligned pointers, batch outside [1, SNAPKV_MAX_BATCH], bad
+ * head counts, an unknown layout, a cache length < 1 or above capacity;
+ * SNAPKV_ERR_UNSUPPORTED for head_dim not in {64, 128} or more than 8 query
+ * heads per KV head; SNAPKV_ERR_WORKSPACE for a small workspace.
+ */
+#define SNAPKV_CACHE_COMPRESSED 0
+#define SNAPKV_CACHE_PACKED 1
+
+int32_t snapkv_decode_workspace_size(int32_t batch, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t layout, int32_t capacity,
+                                     const int32_t* cache_lens, size_t* bytes);
+
+int32_t snapkv_decode_attention(int32_t batch, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim,
+                                const void* q, const void* k_cache,
+                                const void* v_cache, int32_t layout,
+                                int32_t capacity, const int32_t* cache_lens,
+                                float* out, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Static text of a status code ("ok", "invalid argument", ...). */
 const char* snapkv_status_string(int32_t status);
 

@@ -7,6 +7,8 @@ csrc/); this package is its Python binding. Build the library with
 
 from .snapkv import (  # noqa: F401
     LIB_PATH,
+    SNAPKV_CACHE_COMPRESSED,
+    SNAPKV_CACHE_PACKED,
     SNAPKV_ERR_HIP,
     SNAPKV_ERR_INVALID_ARGUMENT,
     SNAPKV_ERR_UNSUPPORTED,
@@ -25,6 +27,8 @@ from .snapkv import (  # noqa: F401
     snapkv_compress,
     snapkv_compress_from_lse,
     snapkv_compress_int4,
+    snapkv_decode_attention,
+    snapkv_decode_workspace_size,
     snapkv_last_error,
     snapkv_stage_name,
     snapkv_status_string,

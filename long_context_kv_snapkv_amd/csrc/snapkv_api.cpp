@@ -9,6 +9,7 @@
 #include <string>
 
 #include "snapkv.h"
+#include "snapkv_decode.h"
 #include "snapkv_kernels.h"
 
 namespace {
@@ -278,6 +279,73 @@ int32_t compress_impl(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const v
   return SNAPKV_OK;
 }
 
+// Decode step: rows per prompt, chunking and workspace, from shapes alone.
+//   part  float[batch * H_kv, nchunk, G, D + 2]  per-chunk partial softmax
+struct DecodePlan {
+  int batch, hq, hkv, d, group, layout, capacity, chunk, nchunk;
+  size_t bytes;
+  int32_t off[snapkv::kMaxBatch], len[snapkv::kMaxBatch];
+};
+
+int32_t make_decode_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t d, int32_t layout,
+                         int32_t capacity, const int32_t* cache_lens, DecodePlan* pl) {
+  if (cache_lens == nullptr) return fail(SNAPKV_ERR_INVALID_ARGUMENT, "cache_lens is NULL");
+  if (batch < 1 || batch > SNAPKV_MAX_BATCH)
+    return fail(SNAPKV_ERR_INVALID_ARGUMENT,
+                "batch must be in [1, " + std::to_string(SNAPKV_MAX_BATCH) + "]");
+  if (hq < 1 || hkv < 1 || hq % hkv != 0)
+    return fail(SNAPKV_ERR_INVALID_ARGUMENT,
+                "num_q_heads must be a positive multiple of num_kv_heads");
+  if (layout != SNAPKV_CACHE_COMPRESSED && layout != SNAPKV_CACHE_PACKED)
+    return fail(SNAPKV_ERR_INVALID_ARGUMENT, "unknown cache layout " + std::to_string(layout));
+  if (layout == SNAPKV_CACHE_COMPRESSED && capacity < 1)
+    return fail(SNAPKV_ERR_INVALID_ARGUMENT, "capacity must be >= 1");
+  if (d != 64 && d != 128)
+    return fail(SNAPKV_ERR_UNSUPPORTED, "head_dim must be 64 or 128, got " + std::to_string(d));
+  if (hq / hkv > snapkv::kDecodeMaxGroup)
+    return fail(SNAPKV_ERR_UNSUPPORTED, "num_q_heads / num_kv_heads must be <= " +
+                                            std::to_string(snapkv::kDecodeMaxGroup));
+  if ((int64_t)batch * hkv > (1 << 20))
+    return fail(SNAPKV_ERR_UNSUPPORTED, "batch * num_kv_heads must be <= 2^20");
+  int64_t total = 0, rows = 0;
+  int n_max = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int32_t n = cache_lens[b];
+    if (n < 1)
+      return fail(SNAPKV_ERR_INVALID_ARGUMENT,
+                  "cache_lens[" + std::to_string(b) + "] must be >= 1, got " + std::to_string(n));
+    if (layout == SNAPKV_CACHE_COMPRESSED && n > capacity)
+      return fail(SNAPKV_ERR_INVALID_ARGUMENT,
+                  "cache_lens[" + std::to_string(b) + "] exceeds the capacity");
+    pl->off[b] = (int32_t)total;
+    pl->len[b] = n;
+    total += n;
+    if (total > INT32_MAX) return fail(SNAPKV_ERR_INVALID_ARGUMENT, "more than 2^31-1 rows");
+    rows += n;
+    n_max = n > n_max ? n : n_max;
+  }
+  for (int b = batch; b < snapkv::kMaxBatch; ++b) pl->off[b] = pl->len[b] = 0;
+  pl->batch = batch;
+  pl->hq = hq;
+  pl->hkv = hkv;
+  pl->d = d;
+  pl->group = hq / hkv;
+  pl->layout = layout;
+  pl->capacity = layout == SNAPKV_CACHE_COMPRESSED ? capacity : 0;
+  // rows per work item: about 1024 items over the call (four per CU), in
+  // multiples of 128 rows, 128 .. 8192
+  const int64_t q = snapkv::kDecodeRowQuantum;
+  int64_t chunk = (rows * hkv + 1023) / 1024;
+  chunk = (chunk + q - 1) / q * q;
+  if (chunk < q) chunk = q;
+  if (chunk > 8192) chunk = 8192;
+  pl->chunk = (int)chunk;
+  pl->nchunk = (int)((n_max + chunk - 1) / chunk);
+  pl->bytes = align_up((size_t)batch * hkv * pl->nchunk * pl->group * (d + 2) * sizeof(float),
+                       256);
+  return SNAPKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -379,6 +447,56 @@ int32_t snapkv_window_scores(int32_t batch, int32_t num_q_heads, int32_t num_kv_
     return hip_fail(e, "snapkv_score_stats launch");
   if ((e = snapkv::launch_score_vote(p, head_dim, s)) != hipSuccess)
     return hip_fail(e, "snapkv_score_vote launch");
+  return SNAPKV_OK;
+}
+
+int32_t snapkv_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t layout, int32_t capacity,
+                                     const int32_t* cache_lens, size_t* bytes) {
+  if (bytes == nullptr) return fail(SNAPKV_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  DecodePlan pl;
+  const int32_t st = make_decode_plan(batch, num_q_heads, num_kv_heads, head_dim, layout,
+                                      capacity, cache_lens, &pl);
+  if (st != SNAPKV_OK) return st;
+  *bytes = pl.bytes;
+  return SNAPKV_OK;
+}
+
+int32_t snapkv_decode_attention(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, const void* q, const void* k_cache,
+                                const void* v_cache, int32_t layout, int32_t capacity,
+                                const int32_t* cache_lens, float* out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !out)
+    return fail(SNAPKV_ERR_INVALID_ARGUMENT, "a tensor pointer is NULL");
+  if (misaligned(q) || misaligned(k_cache) || misaligned(v_cache) || misaligned(out))
+    return fail(SNAPKV_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+  DecodePlan pl;
+  int32_t st = make_decode_plan(batch, num_q_heads, num_kv_heads, head_dim, layout, capacity,
+                                cache_lens, &pl);
+  if (st != SNAPKV_OK) return st;
+  if (workspace == nullptr || workspace_bytes < pl.bytes || misaligned(workspace))
+    return fail(SNAPKV_ERR_WORKSPACE, "workspace must be 16-byte aligned and hold " +
+                                          std::to_string(pl.bytes) + " bytes");
+  snapkv::DecodeParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k_cache);
+  p.v = static_cast<const uint16_t*>(v_cache);
+  p.out = out;
+  p.part = static_cast<float*>(workspace);
+  p.batch = pl.batch;
+  p.hq = pl.hq;
+  p.hkv = pl.hkv;
+  p.group = pl.group;
+  p.chunk = pl.chunk;
+  p.nchunk = pl.nchunk;
+  p.layout = pl.layout;
+  p.capacity = pl.capacity;
+  p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+  std::memcpy(p.off, pl.off, sizeof(p.off));
+  std::memcpy(p.len, pl.len, sizeof(p.len));
+  const hipError_t e = snapkv::launch_decode(p, head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "snapkv_decode launch");
   return SNAPKV_OK;
 }
 

@@ -29,6 +29,8 @@ SNAPKV_ERR_HIP = 4
 SNAPKV_POOL_AVG = 0
 SNAPKV_POOL_MAX = 1
 SNAPKV_NUM_STAGES = 4
+SNAPKV_CACHE_COMPRESSED = 0
+SNAPKV_CACHE_PACKED = 1
 
 _POOL_NAMES = {"avg": SNAPKV_POOL_AVG, "avgpool": SNAPKV_POOL_AVG,
                "max": SNAPKV_POOL_MAX, "maxpool": SNAPKV_POOL_MAX}
@@ -79,6 +81,12 @@ def load_library():
                                          _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                          _vp]
     lib.snapkv_compress_int4.restype = _i32
+    lib.snapkv_decode_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _pi32,
+                                                 ctypes.POINTER(_sz)]
+    lib.snapkv_decode_workspace_size.restype = _i32
+    lib.snapkv_decode_attention.argtypes = [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _i32,
+                                            _pi32, _vp, _vp, _sz, _vp]
+    lib.snapkv_decode_attention.restype = _i32
     lib.snapkv_window_scores.argtypes = [_i32, _i32, _i32, _i32, _vp, _vp, _pi32, _i32,
                                          _i32, _i32, _vp, _i32, _vp, _sz, _vp]
     lib.snapkv_window_scores.restype = _i32
@@ -308,6 +316,62 @@ def snapkv_compress_int4(q_win: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         pool_mode_code(pool_mode), budget, _ptr(kq), _ptr(ks), _ptr(vq), _ptr(vs), _ptr(idx),
         _ptr(workspace), workspace.numel(), _stream(stream, dev)))
     return kq, ks, vq, vs, idx
+
+
+def _decode_layout(k_cache: torch.Tensor):
+    if k_cache.dim() == 4:
+        return SNAPKV_CACHE_COMPRESSED, k_cache.shape[1], k_cache.shape[2], k_cache.shape[3]
+    if k_cache.dim() == 3:
+        return SNAPKV_CACHE_PACKED, k_cache.shape[1], 0, k_cache.shape[2]
+    raise ValueError("k_cache must be [batch, H_kv, capacity, D] or [T, H_kv, D]")
+
+
+def snapkv_decode_workspace_size(num_q_heads: int, num_kv_heads: int, head_dim: int,
+                                 cache_lens: Sequence[int], layout: int,
+                                 capacity: int = 0) -> int:
+    lib = load_library()
+    arr, vals = _lens(cache_lens)
+    out = _sz(0)
+    _check(lib.snapkv_decode_workspace_size(len(vals), num_q_heads, num_kv_heads, head_dim,
+                                            layout, capacity, arr, ctypes.byref(out)))
+    return out.value
+
+
+def snapkv_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            cache_lens: Sequence[int], *, out: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None, stream=None):
+    """One decode step's attention, float32 [batch, H_q, D]. The layout
+    follows k_cache's rank: [batch, H_kv, capacity, D] is a compressed cache
+    (snapkv_compress's out_k / out_v), [T, H_kv, D] the packed prefill cache;
+    see include/snapkv.h."""
+    lib = load_library()
+    _check_tensor("q", q, 3)
+    layout, hkv, capacity, d = _decode_layout(k_cache)
+    _check_tensor("k_cache", k_cache, k_cache.dim())
+    _check_tensor("v_cache", v_cache, k_cache.dim())
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    arr, vals = _lens(cache_lens)
+    batch, hq, dq = q.shape
+    if dq != d or batch != len(vals):
+        raise ValueError("q must be [batch, H_q, D] matching the cache and cache_lens")
+    if layout == SNAPKV_CACHE_COMPRESSED and k_cache.shape[0] != batch:
+        raise ValueError("compressed cache batch differs from q")
+    if layout == SNAPKV_CACHE_PACKED and k_cache.shape[0] != sum(vals):
+        raise ValueError("packed cache rows must equal sum(cache_lens)")
+    dev = q.device
+    if out is None:
+        out = torch.empty((batch, hq, d), dtype=torch.float32, device=dev)
+    _check_tensor("out", out, 3, torch.float32)
+    if tuple(out.shape) != (batch, hq, d):
+        raise ValueError("out must be [batch, H_q, D]")
+    if workspace is None:
+        nbytes = snapkv_decode_workspace_size(hq, hkv, d, vals, layout, capacity)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    _check(lib.snapkv_decode_attention(batch, hq, hkv, d, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                       layout, capacity, arr, _ptr(out), _ptr(workspace),
+                                       workspace.numel(), _stream(stream, dev)))
+    return out
 
 
 def snapkv_window_scores(q_win: torch.Tensor, k: torch.Tensor, seq_lens: Sequence[int],

@@ -22,7 +22,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = skv.header_functions()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     assert "snapkv_compress_staged" in names
     assert "snapkv_compress_from_lse" in names
     for name in names:
@@ -141,3 +141,34 @@ def test_compress_int4_validation(lib):
     # valid pointers: the undersized workspace stops the call
     assert call() == 3
     assert call(lse=FAKE + 4) == 3
+
+
+def test_decode_validation_and_workspace(lib):
+    def ws(lens, layout=0, cap=1024, hq=32, hkv=8, d=128):
+        arr = (ctypes.c_int32 * len(lens))(*lens)
+        out = ctypes.c_size_t(0)
+        st = lib.snapkv_decode_workspace_size(len(lens), hq, hkv, d, layout, cap, arr,
+                                              ctypes.byref(out))
+        return st, out.value
+
+    st, small = ws([1024])
+    assert st == 0 and small >= 8 * 4 * 130 * 4
+    st, full = ws([16384], layout=1)
+    assert st == 0 and full >= small
+    assert ws([1025])[0] == 1          # above the capacity
+    assert ws([0])[0] == 1
+    assert ws([10], layout=2)[0] == 1
+    assert ws([10], cap=0)[0] == 1
+    assert ws([10], d=96)[0] == 2
+    assert ws([10], hq=72, hkv=8)[0] == 2  # 9 query heads per KV head
+    assert ws([10], hq=30, hkv=8)[0] == 1
+    lens = (ctypes.c_int32 * 1)(100)
+    st = lib.snapkv_decode_attention(1, 32, 8, 128, FAKE, FAKE, FAKE + 8, 0, 128, lens, FAKE,
+                                     FAKE, 1 << 30, None)
+    assert st == 1 and "aligned" in skv.snapkv_last_error()
+    st = lib.snapkv_decode_attention(1, 32, 8, 128, FAKE, None, FAKE, 0, 128, lens, FAKE,
+                                     FAKE, 1 << 30, None)
+    assert st == 1
+    st = lib.snapkv_decode_attention(1, 32, 8, 128, FAKE, FAKE, FAKE, 0, 128, lens, FAKE,
+                                     FAKE, 1, None)
+    assert st == 3
