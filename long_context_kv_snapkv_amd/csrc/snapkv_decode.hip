@@ -10,14 +10,17 @@
 // kernels:
 //
 //   snapkv_decode_partial  (chunk, KV head, prompt)  one chunk of rows for all
-//                          G query heads of the KV head: each row is read by
-//                          D/8 lanes (16 bytes each, so a wave reads whole
-//                          rows), the G dot products are reduced over those
-//                          lanes with DPP row exchanges, and an online
-//                          softmax keeps (max, sum of weights, weighted V)
-//                          per lane group while the next rows load; the lane
-//                          groups merge through LDS in a fixed order and the
-//                          chunk's partial goes to the workspace;
+//                          G query heads of the KV head, in tiles of 16 rows
+//                          per wave: the scores of a tile for all G queries
+//                          come from v_mfma_f32_16x16x32_bf16 (K rows as the
+//                          A operand, the queries as B); the online softmax
+//                          (running max, weights, rescale factor) runs in
+//                          that layout, one lane per (row, query), and the
+//                          weights pass through a per-wave LDS tile to the
+//                          row layout (D/8 lanes per V row, 16 bytes each)
+//                          that accumulates the weighted V; the waves merge
+//                          through LDS in a fixed order and the chunk's
+//                          partial goes to the workspace;
 //   snapkv_decode_merge    (query head of the group, KV head, prompt)
 //                          merges the chunks in a fixed order and writes out.
 //
@@ -66,13 +69,21 @@ __device__ __forceinline__ float group_max(float x) {
   return x;
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 template <int D, int GM>
 __global__ void __launch_bounds__(kDecodeThreads) snapkv_decode_partial(const DecodeParams p) {
-  constexpr int PIECES = D / 8;                 // lanes per row
-  constexpr int GROUPS = 64 / PIECES;           // rows per wave per step
+  constexpr int PIECES = D / 8;         // lanes per row in the row layout
+  constexpr int RPI = 64 / PIECES;      // rows per wave instruction in the row layout
+  constexpr int TILE = 16;              // rows per score tile (one MFMA row block)
+  constexpr int STEPS = TILE / RPI;     // row-layout steps per tile
+  constexpr int KB = D / 32;            // MFMA k blocks
   constexpr int NW = kDecodeThreads / 64;
-  constexpr int NG = GROUPS * NW;               // lane groups (rows per workgroup step)
-  constexpr int NB = GM >= 8 ? 2 : 4;           // steps whose rows load together
+  constexpr int NG = NW * RPI;          // lane groups of the row layout per workgroup
+  constexpr int SP = 20;                // LDS pitch of a score-tile row (floats)
+  constexpr int ROUND = 2 * NW * TILE;  // rows per workgroup round (two tiles per wave)
+  static_assert(ROUND == kDecodeRowQuantum, "chunk quantum");
+  __shared__ float sm_s[NW][(TILE + 1) * SP];
   __shared__ float sm_ml[NG][GM][2];
   __shared__ float sm_acc[NG][GM][D];
   __shared__ float sm_f[NG][GM];
@@ -84,7 +95,8 @@ __global__ void __launch_bounds__(kDecodeThreads) snapkv_decode_partial(const De
   if (r0 >= n) return;
   const int r1 = min(r0 + p.chunk, n);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int piece = lane % PIECES, gi = wave * GROUPS + lane / PIECES;
+  const int piece = lane % PIECES, grp = lane / PIECES, gi = wave * RPI + grp;
+  const int mrow = lane % 16, mk = lane / 16;  // MFMA operand layout
   size_t base, rs;
   if (p.layout == 0) {
     base = (size_t)(b * p.hkv + h) * p.capacity * D;
@@ -93,111 +105,141 @@ __global__ void __launch_bounds__(kDecodeThreads) snapkv_decode_partial(const De
     base = ((size_t)p.off[b] * p.hkv + h) * D;
     rs = (size_t)p.hkv * D;
   }
-  const uint16_t* kb = p.k + base + piece * 8;
-  const uint16_t* vb = p.v + base + piece * 8;
+  const uint16_t* kbase = p.k + base + mk * 8;
+  const uint16_t* vbase = p.v + base + piece * 8;
 
-  // rows of this lane group: r0 + gi, r0 + gi + NG, ...; two register sets
-  // alternate so that one set's rows load while the other's are used. Row
-  // indices past the chunk are clamped to its last row (a cached re-read)
-  // and masked, so every load is unconditional.
-  constexpr int STEP = NG * NB;
-  // the query slice first (query heads past the group re-read the last one
-  // and are zeroed), so that waiting for it leaves the rows in flight
-  u32x4 qw[GM];
+  // Q^T as the MFMA B operand: query mrow, elements kb * 32 + 8 * mk + e
+  // (slots past the group repeat its last query; their results are unused)
+  u32x4 qop[KB];
+  const uint16_t* qrow = p.q + (size_t)(b * p.hq + h * p.group + min(mrow, p.group - 1)) * D;
 #pragma unroll
-  for (int g = 0; g < GM; ++g)
-    qw[g] = *reinterpret_cast<const u32x4*>(
-        p.q + (size_t)(b * p.hq + h * p.group + min(g, p.group - 1)) * D + piece * 8);
-  u32x4 ka[NB], va[NB], kb2[NB], vb2[NB];
-  auto load = [&](u32x4 (&kd)[NB], u32x4 (&vd)[NB], int rb) {
+  for (int kb = 0; kb < KB; ++kb) qop[kb] = *reinterpret_cast<const u32x4*>(qrow + kb * 32 + mk * 8);
+
+  // a tile of 16 rows t0 .. t0 + 15: K in the MFMA A layout (row t0 + mrow),
+  // V in the row layout (row t0 + RPI * s + grp for step s). Rows past the
+  // chunk are clamped to its last row (a cached re-read) and masked, so every
+  // load is unconditional.
+  struct Tile {
+    u32x4 k[KB];
+    u32x4 v[STEPS];
+  };
+  auto load_tile = [&](Tile& T, int t0) {
+    const size_t rk = (size_t)min(t0 + mrow, r1 - 1);
 #pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const size_t r = (size_t)min(rb + u * NG + gi, r1 - 1);
-      kd[u] = *reinterpret_cast<const u32x4*>(kb + r * rs);
-      vd[u] = *reinterpret_cast<const u32x4*>(vb + r * rs);
+    for (int kb = 0; kb < KB; ++kb)
+      T.k[kb] = *reinterpret_cast<const u32x4*>(kbase + rk * rs + kb * 32);
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+      const size_t rv = (size_t)min(t0 + st * RPI + grp, r1 - 1);
+      T.v[st] = *reinterpret_cast<const u32x4*>(vbase + rv * rs);
     }
     // issued before the work that follows (neither memory operations nor
     // arithmetic move across)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
-  load(ka, va, r0);
-  load(kb2, vb2, r0 + STEP);
 
-  float qv[GM][8];
+  // softmax state: the running max and (partial) sum of weights of query
+  // mrow over the wave's rows live in the MFMA layout (the four lanes mk of
+  // a query share the max; each sums its own rows), the weighted V sums in
+  // the row layout
+  float m_run = -kInf, l_run = 0.f;
+  float acc[GM][8];
 #pragma unroll
-  for (int g = 0; g < GM; ++g) {
-    const float sc = g < p.group ? p.scale_log2 : 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qv[g][e] = bf16_elem(qw[g], e) * sc;
-  }
-  float m[GM], l[GM], acc[GM][8];
-#pragma unroll
-  for (int g = 0; g < GM; ++g) {
-    m[g] = -kInf;
-    l[g] = 0.f;
+  for (int g = 0; g < GM; ++g)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
-  }
+  float* stile = sm_s[wave];
 
-  auto process = [&](const u32x4 (&kd)[NB], const u32x4 (&vd)[NB], int rb) {
-    float s[NB][GM];
+  auto process = [&](const Tile& T, int t0) {
+    // scores of the tile's rows 4 * mk + r for query mrow on the MFMA
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const bool ok = rb + u * NG + gi < r1;
+    for (int kb = 0; kb < KB; ++kb)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(T.k[kb]), as_bf16x8(qop[kb]), sc,
+                                                   0, 0, 0);
+    float x[4];
 #pragma unroll
-      for (int g = 0; g < GM; ++g) {
-        float dot = 0.f;
+    for (int r = 0; r < 4; ++r) x[r] = t0 + 4 * mk + r < r1 ? sc[r] * p.scale_log2 : -kInf;
+    float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float mnew = fmaxf(m_run, tmax);
+    float cs = 1.f, pr[4] = {0.f, 0.f, 0.f, 0.f};
+    if (mnew != -kInf) {  // some row of the wave seen so far
+      cs = exp2_fast(m_run - mnew);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dot = fmaf(qv[g][e], bf16_elem(kd[u], e), dot);
-        dot = group_sum<PIECES>(dot);
-        s[u][g] = ok ? dot : -kInf;
-      }
+      for (int r = 0; r < 4; ++r) pr[r] = exp2_fast(x[r] - mnew);
     }
+    l_run = l_run * cs + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+    m_run = mnew;
+    // weights and rescale factors through this wave's LDS tile to the row
+    // layout (one wave writes and reads it, in order)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) stile[(4 * mk + r) * SP + mrow] = pr[r];
+    if (mk == 0) stile[TILE * SP + mrow] = cs;
+    __builtin_amdgcn_wave_barrier();
+    float csv[GM];
+#pragma unroll
+    for (int g = 0; g < GM; ++g) csv[g] = stile[TILE * SP + g];
 #pragma unroll
     for (int g = 0; g < GM; ++g) {
-      float mx = m[g];
+      // the same word for every lane: a scalar test skips the common cs == 1
+      const float csg = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(csv[g])));
+      if (csg != 1.f) {
 #pragma unroll
-      for (int u = 0; u < NB; ++u) mx = fmaxf(mx, s[u][g]);
-      if (mx == -kInf) continue;  // no row of this lane group yet
-      const float cs = exp2_fast(m[g] - mx);
-      l[g] *= cs;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[g][e] *= cs;
-#pragma unroll
-      for (int u = 0; u < NB; ++u) {
-        const float pw = exp2_fast(s[u][g] - mx);
-        l[g] += pw;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(pw, bf16_elem(vd[u], e), acc[g][e]);
+        for (int e = 0; e < 8; ++e) acc[g][e] *= csg;
       }
-      m[g] = mx;
     }
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+      const float* prow = stile + (st * RPI + grp) * SP;
+      float pg[GM];
+#pragma unroll
+      for (int g = 0; g < GM; ++g) pg[g] = prow[g];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float ve = bf16_elem(T.v[st], e);
+#pragma unroll
+        for (int g = 0; g < GM; ++g) acc[g][e] = fmaf(pg[g], ve, acc[g][e]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
   };
 
-  // rounds of two register sets: both sets' loads are in flight before the
-  // first is used (a chunk is a whole number of rounds, 2 * STEP rows)
-  process(ka, va, r0);
-  process(kb2, vb2, r0 + STEP);
-  for (int rb = r0 + 2 * STEP; rb < r1; rb += 2 * STEP) {
-    load(ka, va, rb);
-    load(kb2, vb2, rb + STEP);
-    process(ka, va, rb);
-    process(kb2, vb2, rb + STEP);
+  // rounds: each wave loads two tiles (rows t0 and t0 + 64 of the round)
+  // before using the first
+  Tile ta, tb;
+  const int w0 = wave * TILE;
+  load_tile(ta, r0 + w0);
+  load_tile(tb, r0 + w0 + NW * TILE);
+  process(ta, r0 + w0);
+  process(tb, r0 + w0 + NW * TILE);
+  for (int rb = r0 + ROUND; rb < r1; rb += ROUND) {
+    load_tile(ta, rb + w0);
+    load_tile(tb, rb + w0 + NW * TILE);
+    process(ta, rb + w0);
+    process(tb, rb + w0 + NW * TILE);
   }
 
   // every lane group's state to LDS; then, per query head, the groups'
   // weights 2^(m_w - max) and the sum of weights by DPP reductions over NG
   // lanes, and each output element as a fixed-order sum over the groups
+  // the wave's sum of weights per query (fixed-order butterfly over mk); its
+  // lane groups share the wave's max, and the sum is carried by group 0
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (mk == 0 && mrow < GM) {
 #pragma unroll
-  for (int g = 0; g < GM; ++g) {
-    if (piece == 0) {
-      sm_ml[gi][g][0] = m[g];
-      sm_ml[gi][g][1] = l[g];
+    for (int j = 0; j < RPI; ++j) {
+      sm_ml[wave * RPI + j][mrow][0] = m_run;
+      sm_ml[wave * RPI + j][mrow][1] = j == 0 ? l_run : 0.f;
     }
+  }
+#pragma unroll
+  for (int g = 0; g < GM; ++g)
 #pragma unroll
     for (int e = 0; e < 8; ++e) sm_acc[gi][g][piece * 8 + e] = acc[g][e];
-  }
   __syncthreads();
   float* dst = p.part + ((size_t)(b * p.hkv + h) * p.nchunk + c) * p.group * (D + 2);
   if (tid < NG * GM) {  // whole waves: NG * GM is a multiple of 16, and of 64 or below it
