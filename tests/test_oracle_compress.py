@@ -3,6 +3,7 @@
 import numpy as np
 import pytest
 
+import oracle
 from oracle import OracleError, compress, pool_scores, select_prefix, validate
 from synth import WORKLOADS, make_custom, make_layer
 
@@ -95,3 +96,24 @@ def test_validation(args):
     base.update(args)
     with pytest.raises(OracleError):
         validate(**base)
+
+
+def test_prompt_scores_map_query_groups_to_kv_heads():
+    # query head q reads KV head q // G: with rank-one queries and keys each
+    # KV head's raw scores follow the closed form of its own group's queries
+    from test_oracle_vote import _rank_one_closed_form
+    from synth import bf16_round_bits
+    hq, hkv, d, length, w = 6, 3, 16, 20, 4
+    g = hq // hkv
+    rng = np.random.default_rng(11)
+    alphas = rng.choice([-2.0, -1.0, -0.5, 0.5, 1.0, 1.5, 2.0], size=hq)
+    kappa = rng.integers(-3, 4, size=(hkv, length)).astype(float)
+    q = np.zeros((1, hq, w, d), dtype=np.float32)
+    q[0, :, :, 0] = alphas[:, None]
+    k = np.zeros((length, hkv, d), dtype=np.float32)
+    k[:, :, 0] = kappa.T
+    raw, _ = oracle.prompt_scores(bf16_round_bits(q), bf16_round_bits(k), 0, length, 0, hq,
+                                  hkv, w, 1, "avg")
+    for h in range(hkv):
+        ref = _rank_one_closed_form(alphas[h * g:(h + 1) * g], kappa[h], d, w)
+        np.testing.assert_allclose(raw[h], ref, rtol=1e-12, atol=1e-15)
