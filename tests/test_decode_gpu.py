@@ -150,3 +150,27 @@ def test_decode_repeatable():
     b = skv.snapkv_decode_attention(qd, k, v, lens)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@needs_gpu
+def test_decode_70b_shape_128k_packed_and_compressed():
+    # G = 8 query heads per KV head over a 131K-row cache and its compression
+    w = WORKLOADS["llama3_70b_128k_x80"]
+    x = make_layer(w, 0)
+    lens = x.seq_lens.tolist()
+    print("[decode] 70b 128k", flush=True)
+    qd = _query(1, w.h_q, w.head_dim, 9)
+    got = skv.snapkv_decode_attention(bits_to_device(qd), bits_to_device(x.k), bits_to_device(x.v),
+                                      lens).cpu().numpy().astype(np.float64)
+    want = oracle.decode_packed(qd, x.k, x.v, lens)
+    vmax = [[np.abs(oracle.bf16_bits_to_f64(x.v[:, h])).max() for h in range(w.h_kv)]]
+    _check(got, want, vmax, w.h_kv)
+    # a compressed layout of B rows per head taken at fixed positions (the
+    # decode step does not depend on how the rows were chosen)
+    pos = np.linspace(0, lens[0] - 1, w.budget).astype(np.int64)
+    kc = np.ascontiguousarray(x.k[pos].transpose(1, 0, 2))[None]
+    vc = np.ascontiguousarray(x.v[pos].transpose(1, 0, 2))[None]
+    got_c = skv.snapkv_decode_attention(bits_to_device(qd), bits_to_device(kc), bits_to_device(vc),
+                                        [w.budget]).cpu().numpy()
+    want_c = oracle.decode_compressed(qd, kc, vc, [w.budget])
+    _check(got_c.astype(np.float64), want_c, vmax, w.h_kv)

@@ -133,3 +133,19 @@ def test_binding_rejects_a_wrong_normaliser_shape():
     with pytest.raises(ValueError):
         skv.snapkv_compress_from_lse(q, k, v, [300], 16, bad.double()[:, :, :1].expand(1, 8, 16),
                                      5, "avg", 64)
+
+
+@needs_gpu
+def test_llama3_70b_128k_with_device_normalisers():
+    # 512 window rows per KV head and the streaming selection (131K positions),
+    # normalisers computed on the device
+    w = WORKLOADS["llama3_70b_128k_x80"]
+    x = make_layer(w, 0)
+    print("[from_lse] llama3_70b_128k layer 0", flush=True)
+    q, k, _ = upload(x)
+    lens = x.seq_lens.tolist()
+    lse = torch_window_lse(q, k, lens, w.window)
+    res = run_gpu_from_lse(x, w.window, w.kernel, w.pool, w.budget, lse)
+    ref = oracle.compress(x.q_win, x.k, x.v, lens, w.window, w.kernel, w.pool, w.budget)
+    check_structure_and_gather(res, x, w.window, w.budget)
+    check_index_sets(res["out_idx"], ref.pooled, lens, w.window, w.budget)
