@@ -168,7 +168,13 @@ snapkv::PathParams path_params(const Plan& pl, const void* q, const void* k, con
   p.score_all = score_all ? 1 : 0;
   p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)pl.d));
   p.tab = pl.tab;
-  p.n_gather_blocks = budget > 0 ? (budget + snapkv::kGatherRows - 1) / snapkv::kGatherRows : 0;
+  // half-size gather items (D = 128) when full ones would leave CUs idle:
+  // fewer than about two per CU over the call
+  const int full_items =
+      budget > 0 ? pl.batch * pl.hkv * ((budget + snapkv::kGatherRows - 1) / snapkv::kGatherRows)
+                 : 0;
+  p.gather_rows = pl.d == 128 && full_items < 512 ? snapkv::kGatherRows / 2 : snapkv::kGatherRows;
+  p.n_gather_blocks = budget > 0 ? (budget + p.gather_rows - 1) / p.gather_rows : 0;
   return p;
 }
 

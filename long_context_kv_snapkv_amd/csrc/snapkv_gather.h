@@ -118,19 +118,19 @@ __device__ __forceinline__ uint32_t quantize_piece_int4(const u32x4& w, float& s
   return out;
 }
 
-template <int D, bool INT4>
+template <int D, bool INT4, int RW>
 __device__ __forceinline__ void snapkv_gather_item(const PathParams& p, GatherSmem& gs, int b,
                                                    int h, int rb) {
   constexpr int PIECES = D / 8;
   constexpr int ROWS_PER_PASS = kThreads / PIECES;
-  constexpr int PASSES = kGatherRows / ROWS_PER_PASS;
-  static_assert(PASSES >= 1 && kGatherRows % ROWS_PER_PASS == 0, "row split");
-  const int t0 = rb * kGatherRows;
+  constexpr int PASSES = RW / ROWS_PER_PASS;  // RW: rows of this item
+  static_assert(PASSES >= 1 && RW % ROWS_PER_PASS == 0, "row split");
+  const int t0 = rb * RW;
   const int L = p.tab.len[b];
   const int B = p.budget;
   const bool whole = L <= B;
   const int P = L - p.window, m = B - p.window;
-  if (!whole && t0 < m) locate_kept(p, gs, b, h, t0, min(t0 + kGatherRows, m));
+  if (!whole && t0 < m) locate_kept(p, gs, b, h, t0, min(t0 + RW, m));
   const int tid = threadIdx.x;
   int32_t* idx = p.out_idx + (size_t)(b * p.hkv + h) * B;
   const size_t tstride = (size_t)p.hkv * D;

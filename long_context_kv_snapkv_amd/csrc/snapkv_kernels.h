@@ -13,7 +13,7 @@ constexpr int kMaxKernel = 2049;   // pooling kernel
 constexpr int kThreads = 512;      // workgroup size of every kernel
 constexpr int kKeyTile = 64;       // keys per LDS tile
 constexpr int kMaxChunk = 4096;    // keys per scoring work item
-constexpr int kGatherRows = 64;    // compressed rows per gather work item
+constexpr int kGatherRows = 64;    // compressed rows per gather work item (at most)
 constexpr int kTopHistBins = 2048; // bins of the selection's first radix digit
 constexpr int kSegment = 256;      // positions per selection count-table entry
 
@@ -57,6 +57,8 @@ struct PathParams {
   int32_t score_all;       // 1: score every prompt with P >= 1; 0: only L > budget
   int32_t export_scores;   // 1: pooled rows are the caller's, zero past P
   int32_t n_gather_blocks; // gather items per (prompt, head)
+  int32_t gather_rows;     // rows per gather item: kGatherRows, or half of it when
+                           // there are few items (D = 128 only)
   float scale_log2;        // log2(e) / sqrt(D)
   PromptTable tab;
 };

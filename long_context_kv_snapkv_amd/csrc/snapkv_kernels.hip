@@ -73,10 +73,10 @@ __global__ void __launch_bounds__(kThreads) snapkv_select(const PathParams p) {
   snapkv_select_item(p, sm, b, h);
 }
 
-template <int D, bool INT4>
+template <int D, bool INT4, int RW>
 __global__ void __launch_bounds__(kThreads) snapkv_gather(const PathParams p) {
   __shared__ GatherSmem sm;
-  snapkv_gather_item<D, INT4>(p, sm, blockIdx.z, blockIdx.y, blockIdx.x);
+  snapkv_gather_item<D, INT4, RW>(p, sm, blockIdx.z, blockIdx.y, blockIdx.x);
 }
 
 // Launch with one PathParams argument; with events, through the extended
@@ -150,9 +150,16 @@ hipError_t launch_select(const PathParams& p, hipStream_t stream, StageEvents ev
 hipError_t launch_gather(const PathParams& p, int head_dim, hipStream_t stream,
                          StageEvents ev, bool int4) {
   return dispatch_dim(head_dim, [&](auto d) {
+    constexpr int D = decltype(d)::value;
     const dim3 grid(p.n_gather_blocks, p.hkv, p.batch);
-    if (int4) return launch(snapkv_gather<decltype(d)::value, true>, grid, stream, ev, p);
-    return launch(snapkv_gather<decltype(d)::value, false>, grid, stream, ev, p);
+    if constexpr (D == 128) {
+      if (p.gather_rows == kGatherRows / 2) {
+        if (int4) return launch(snapkv_gather<D, true, kGatherRows / 2>, grid, stream, ev, p);
+        return launch(snapkv_gather<D, false, kGatherRows / 2>, grid, stream, ev, p);
+      }
+    }
+    if (int4) return launch(snapkv_gather<D, true, kGatherRows>, grid, stream, ev, p);
+    return launch(snapkv_gather<D, false, kGatherRows>, grid, stream, ev, p);
   });
 }
 
