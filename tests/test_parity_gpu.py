@@ -210,3 +210,26 @@ def test_validation_error_surfaces_through_binding():
     with pytest.raises(skv.SnapKVError) as e:
         skv.snapkv_compress(q, k, v, [100], 8, 4, "avg", 32)
     assert e.value.status == skv.SNAPKV_ERR_INVALID_ARGUMENT
+
+
+@needs_gpu
+def test_caller_stream_is_used():
+    # work enqueued on a side stream: results equal the default stream's once
+    # that stream is synchronised
+    w = WORKLOADS["llama3_8b_16k"]
+    x = make_layer(w)
+    dev = upload(x)
+    lens = x.seq_lens.tolist()
+    ref = skv.snapkv_compress(*dev, lens, w.window, w.kernel, w.pool, w.budget)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        out = skv.snapkv_compress(*dev, lens, w.window, w.kernel, w.pool, w.budget, stream=side)
+        dq = dev[0][:, :, -1].contiguous()
+        dec = skv.snapkv_decode_attention(dq, out[0], out[1], [w.budget], stream=side)
+    side.synchronize()
+    dec_ref = skv.snapkv_decode_attention(dq, ref[0], ref[1], [w.budget])
+    torch.cuda.synchronize()
+    for a, b in zip(out, ref):
+        assert torch.equal(a, b)
+    assert torch.equal(dec, dec_ref)
