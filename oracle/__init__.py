@@ -28,7 +28,12 @@ from .snapkv_oracle import (  # noqa: F401
 )
 from .decode import attend, decode_compressed, decode_packed  # noqa: F401
 from .kv_quant import (  # noqa: F401
+    Fp8Result,
     Int4Result,
+    e4m3_decode,
+    e4m3_encode,
+    quantize_cache_fp8,
+    quantize_rows_fp8,
     compress_int4,
     dequantize_int4,
     pack_int4,

@@ -173,3 +173,19 @@ def test_flipped_normaliser_sign_mutant_is_caught(monkeypatch):
     _patch(monkeypatch, "window_vote_from_lse", flipped, [orc, oracle, t_lse])
     assert _caught(lambda: t_lse.test_vote_from_exact_normalisers_equals_vote(),
                    lambda: t_lse.test_shifted_normalisers_scale_the_vote())
+
+
+def test_truncating_fp8_mutant_is_caught(monkeypatch):
+    import test_oracle_fp8 as t_fp8
+    real = oquant.e4m3_encode
+
+    def truncating(v):
+        # round toward zero: shave a quarter step before rounding to nearest
+        v = np.asarray(v, dtype=np.float32)
+        a = np.abs(v.astype(np.float64))
+        step = np.exp2(np.floor(np.log2(np.maximum(a, 2.0 ** -6))) - 3)
+        return real((np.sign(v) * np.maximum(a - 0.499 * step, 0)).astype(np.float32))
+
+    _patch(monkeypatch, "e4m3_encode", truncating, [oquant, oracle, t_fp8])
+    assert _caught(lambda: t_fp8.test_encoding_matches_torch_float8_e4m3fn(),
+                   lambda: t_fp8.test_hand_written_encodings())
