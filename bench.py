@@ -258,15 +258,32 @@ def main():
                                  out=(s["kq"], s["ks"], s["vq"], s["vs"], s["oi"]),
                                  workspace=ws, stream=stream)
 
-    for i in range(args.warmup):
-        step_int4(i)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step_int4(i)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_step_int4 = t_start.elapsed_time(t_end) / args.steps
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        return t_start.elapsed_time(t_end) / args.steps
+
+    ms_step_int4 = timed(step_int4)
+    # and as FP8 E4M3 bytes (snapkv_compress_fp8)
+    for s_ in sets:
+        s_["kq8"] = torch.empty((batch, hkv, B, d), dtype=torch.uint8, device=dev)
+        s_["vq8"] = torch.empty_like(s_["kq8"])
+
+    def step_fp8(i):
+        s = sets[i % nsets]
+        skv.snapkv_compress_fp8(s["q"], s["k"], s["v"], lens, w.window, w.kernel, w.pool, B,
+                                out=(s["kq8"], s["ks"], s["vq8"], s["vs"], s["oi"]),
+                                workspace=ws, stream=stream)
+
+    ms_step_fp8 = timed(step_fp8)
+    for s_ in sets:
+        del s_["kq8"], s_["vq8"]
 
     # one decode step's attention over the compressed cache against the full
     # prefill cache (snapkv_decode_attention), each cache streamed from HBM:
@@ -366,6 +383,12 @@ def main():
                  "cache_bytes": 2 * batch * hkv * B * (d // 2 + 4),
                  "note": "snapkv_compress_int4: kept rows stored as 4-bit codes with a "
                          "float32 scale per row"},
+        "fp8": {"ms_per_step": round(ms_step_fp8, 5),
+                "value": round(sum(lens) / (ms_step_fp8 * 1e-3), 1),
+                "unit": "tokens/s/layer",
+                "cache_bytes": 2 * batch * hkv * B * (d + 4),
+                "note": "snapkv_compress_fp8: kept rows stored as FP8 E4M3 bytes with a "
+                        "float32 scale per row"},
     }
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)

@@ -217,6 +217,31 @@ int32_t snapkv_compress_int4(int32_t batch, int32_t num_q_heads,
                              size_t workspace_bytes, void* stream);
 
 /*
+ * snapkv_compress with the kept rows stored at 8 bits per value in the OCP
+ * FP8 E4M3 format (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinities, largest finite value 448), the format MI355X's matrix cores
+ * read: per kept K or V row, scale = amax / 448 and code_d =
+ * E4M3(x_d * (448 / amax)), the product in float32 and the conversion
+ * rounding to nearest even (code * scale is within 2^-4 of x_d relative, or
+ * 2^-10 * scale below 2^-6 * scale). A zero row has codes 0 and scale 0.
+ *
+ *   out_kq, out_vq  device uint8 [batch, H_kv, B, D]: E4M3 bytes
+ *   out_ks, out_vs  device float32 [batch, H_kv, B]
+ *
+ * Everything else as for snapkv_compress_int4 (same selection, index list,
+ * padding, optional window_lse and errors).
+ */
+int32_t snapkv_compress_fp8(int32_t batch, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim,
+                            const void* q_win, const void* k, const void* v,
+                            const int32_t* seq_lens, int32_t window,
+                            const float* window_lse, int32_t kernel_size,
+                            int32_t pool_mode, int32_t budget,
+                            uint8_t* out_kq, float* out_ks, uint8_t* out_vq,
+                            float* out_vs, int32_t* out_idx, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
  * The pooled scores c_h (steps 1-2) of every prompt with P = L - W >= 1,
  * whatever its length relative to a budget; raw scores when kernel_size = 1.
  *

@@ -25,6 +25,7 @@ from .snapkv import (  # noqa: F401
     new_workspace,
     pool_mode_code,
     snapkv_compress,
+    snapkv_compress_fp8,
     snapkv_compress_from_lse,
     snapkv_compress_int4,
     snapkv_decode_attention,

@@ -200,12 +200,13 @@ int32_t check_tensors(const void* q_win, const void* k, const void* v, const voi
   return SNAPKV_OK;
 }
 
-// Output buffers of the 4-bit form (snapkv_compress_int4).
-struct Int4Out {
+// Output buffers of the 4-bit and 8-bit forms (snapkv_compress_int4 / _fp8).
+struct QuantOut {
   uint8_t* kq;
   float* ks;
   uint8_t* vq;
   float* vs;
+  int form;  // 1: 4-bit, 2: FP8 E4M3
 };
 
 int32_t compress_impl(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const void* q_win,
@@ -213,7 +214,7 @@ int32_t compress_impl(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const v
                       int32_t kernel, int32_t pool_mode, int32_t budget, void* out_k,
                       void* out_v, int32_t* out_idx, void* workspace, size_t workspace_bytes,
                       void* stream, void* const* stage_events, const float* window_lse,
-                      const Int4Out* q4 = nullptr) {
+                      const QuantOut* q4 = nullptr) {
   int32_t st = q4 ? check_tensors(q_win, k, v, q4->kq, q4->vq, out_idx)
                   : check_tensors(q_win, k, v, out_k, out_v, out_idx);
   if (st != SNAPKV_OK) return st;
@@ -280,7 +281,7 @@ int32_t compress_impl(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const v
     if ((e = snapkv::launch_select(p, s, events(2))) != hipSuccess)
       return hip_fail(e, "snapkv_select launch");
   }
-  if ((e = snapkv::launch_gather(p, d, s, events(3), q4 != nullptr)) != hipSuccess)
+  if ((e = snapkv::launch_gather(p, d, s, events(3), q4 ? q4->form : 0)) != hipSuccess)
     return hip_fail(e, "snapkv_gather launch");
   return SNAPKV_OK;
 }
@@ -414,10 +415,25 @@ int32_t snapkv_compress_int4(int32_t batch, int32_t num_q_heads, int32_t num_kv_
                              void* stream) {
   if (window_lse != nullptr && (reinterpret_cast<uintptr_t>(window_lse) & 3u) != 0)
     return fail(SNAPKV_ERR_INVALID_ARGUMENT, "window_lse must be 4-byte aligned");
-  const Int4Out q4{out_kq, out_ks, out_vq, out_vs};
+  const QuantOut q4{out_kq, out_ks, out_vq, out_vs, 1};
   return compress_impl(batch, num_q_heads, num_kv_heads, head_dim, q_win, k, v, seq_lens, window,
                        kernel_size, pool_mode, budget, nullptr, nullptr, out_idx, workspace,
                        workspace_bytes, stream, nullptr, window_lse, &q4);
+}
+
+int32_t snapkv_compress_fp8(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, const void* q_win, const void* k, const void* v,
+                            const int32_t* seq_lens, int32_t window, const float* window_lse,
+                            int32_t kernel_size, int32_t pool_mode, int32_t budget,
+                            uint8_t* out_kq, float* out_ks, uint8_t* out_vq, float* out_vs,
+                            int32_t* out_idx, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (window_lse != nullptr && (reinterpret_cast<uintptr_t>(window_lse) & 3u) != 0)
+    return fail(SNAPKV_ERR_INVALID_ARGUMENT, "window_lse must be 4-byte aligned");
+  const QuantOut q8{out_kq, out_ks, out_vq, out_vs, 2};
+  return compress_impl(batch, num_q_heads, num_kv_heads, head_dim, q_win, k, v, seq_lens, window,
+                       kernel_size, pool_mode, budget, nullptr, nullptr, out_idx, workspace,
+                       workspace_bytes, stream, nullptr, window_lse, &q8);
 }
 
 int32_t snapkv_window_scores(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

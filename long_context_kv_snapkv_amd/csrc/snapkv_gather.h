@@ -16,7 +16,8 @@
 // reads are row-granular gathers from the packed [T, H_kv, D] cache, writes
 // are contiguous. All of a thread's loads are issued before its stores.
 // Rows are bit copies; out_idx is written here for every slot. The 4-bit
-// instance stores each row instead as codes and a scale (quantize_piece_int4).
+// and 8-bit instances store each row instead as codes and a scale
+// (quantize_piece_int4, quantize_piece_fp8).
 #pragma once
 
 #include "snapkv_device.h"
@@ -91,34 +92,63 @@ __device__ __forceinline__ void locate_kept(const PathParams& p, GatherSmem& s, 
   __syncthreads();
 }
 
-// 4-bit form of one 16-byte piece (8 bf16 values) of a row spread over
-// PIECES consecutive lanes: the row's largest magnitude (compared as bf16
-// magnitude bits, which order finite values) gives scale = amax / 7 and
-// codes rint(x * (7 / amax)) in [-7, 7], in float32 with IEEE rounding;
-// returns the 8 codes as nibbles, element e at bits 4e. Every lane of the
-// group must call it (the reduction reads the other lanes).
+// Largest magnitude of a row spread over PIECES consecutive lanes, each
+// holding one 16-byte piece (8 bf16 values): bf16 magnitude bits order
+// finite values, so an integer maximum over the lanes finds it. Every lane
+// of the group must call it (the reduction reads the other lanes).
 template <int PIECES>
-__device__ __forceinline__ uint32_t quantize_piece_int4(const u32x4& w, float& scale) {
+__device__ __forceinline__ float row_amax(const u32x4& w) {
   uint32_t mx = 0u;
 #pragma unroll
   for (int i = 0; i < 4; ++i) mx = max(mx, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
 #pragma unroll
   for (int o = 1; o < PIECES; o <<= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
-  const float amax = __uint_as_float(mx << 16);
+  return __uint_as_float(mx << 16);
+}
+
+__device__ __forceinline__ float piece_elem(const u32x4& w, int e) {
+  const uint32_t word = w[e >> 1];
+  return __uint_as_float((e & 1) ? (word & 0xFFFF0000u) : (word << 16));
+}
+
+// 4-bit form of one piece: scale = amax / 7 and codes rint(x * (7 / amax))
+// in [-7, 7], in float32 with IEEE rounding; the 8 codes as nibbles,
+// element e at bits 4e.
+template <int PIECES>
+__device__ __forceinline__ uint32_t quantize_piece_int4(const u32x4& w, float& scale) {
+  const float amax = row_amax<PIECES>(w);
   scale = amax / 7.0f;
   const float inv = amax > 0.f ? 7.0f / amax : 0.f;
   uint32_t out = 0u;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const uint32_t word = w[e >> 1];
-    const float x = __uint_as_float((e & 1) ? (word & 0xFFFF0000u) : (word << 16));
-    const int c = min(max((int)rintf(x * inv), -7), 7);
+    const int c = min(max((int)rintf(piece_elem(w, e) * inv), -7), 7);
     out |= ((uint32_t)c & 0xFu) << (4 * e);
   }
   return out;
 }
 
-template <int D, bool INT4, int RW>
+// 8-bit form of one piece in OCP FP8 E4M3: scale = amax / 448 and codes
+// E4M3(x * (448 / amax)) (float32 product, the conversion instruction
+// rounding to nearest even); byte e holds element e.
+template <int PIECES>
+__device__ __forceinline__ uint2 quantize_piece_fp8(const u32x4& w, float& scale) {
+  const float amax = row_amax<PIECES>(w);
+  scale = amax / 448.0f;
+  const float inv = amax > 0.f ? 448.0f / amax : 0.f;
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(piece_elem(w, 0) * inv, piece_elem(w, 1) * inv, 0,
+                                           false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(piece_elem(w, 2) * inv, piece_elem(w, 3) * inv, lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(piece_elem(w, 4) * inv, piece_elem(w, 5) * inv, 0,
+                                           false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(piece_elem(w, 6) * inv, piece_elem(w, 7) * inv, hi, true);
+  return make_uint2((uint32_t)lo, (uint32_t)hi);
+}
+
+// Storage forms of the kept rows.
+constexpr int kStoreBf16 = 0, kStoreInt4 = 1, kStoreFp8 = 2;
+
+template <int D, int FORM, int RW>
 __device__ __forceinline__ void snapkv_gather_item(const PathParams& p, GatherSmem& gs, int b,
                                                    int h, int rb) {
   constexpr int PIECES = D / 8;
@@ -153,7 +183,7 @@ __device__ __forceinline__ void snapkv_gather_item(const PathParams& p, GatherSm
       vx[q] = *reinterpret_cast<const u32x4*>(vsrc + (size_t)j * tstride + piece * 8);
     }
   }
-  if constexpr (INT4) {
+  if constexpr (FORM == kStoreInt4) {
     // rows of slots >= B and padding rows are zero and quantise to zero
     const size_t hrow = (size_t)(b * p.hkv + h) * B;
 #pragma unroll
@@ -165,6 +195,23 @@ __device__ __forceinline__ void snapkv_gather_item(const PathParams& p, GatherSm
       if (t >= B) continue;
       *reinterpret_cast<uint32_t*>(p.out_kq + (hrow + t) * (D / 2) + piece * 4) = kc;
       *reinterpret_cast<uint32_t*>(p.out_vq + (hrow + t) * (D / 2) + piece * 4) = vc;
+      if (piece == 0) {
+        idx[t] = jj[q];
+        p.out_ks[hrow + t] = ks;
+        p.out_vs[hrow + t] = vs;
+      }
+    }
+  } else if constexpr (FORM == kStoreFp8) {
+    const size_t hrow = (size_t)(b * p.hkv + h) * B;
+#pragma unroll
+    for (int q = 0; q < PASSES; ++q) {
+      float ks, vs;
+      const uint2 kc = quantize_piece_fp8<PIECES>(kx[q], ks);
+      const uint2 vc = quantize_piece_fp8<PIECES>(vx[q], vs);
+      const int t = tt[q];
+      if (t >= B) continue;
+      *reinterpret_cast<uint2*>(p.out_kq + (hrow + t) * D + piece * 8) = kc;
+      *reinterpret_cast<uint2*>(p.out_vq + (hrow + t) * D + piece * 8) = vc;
       if (piece == 0) {
         idx[t] = jj[q];
         p.out_ks[hrow + t] = ks;

@@ -31,9 +31,10 @@ struct PathParams {
   uint16_t* out_k;    // bf16 [batch, Hkv, budget, D]
   uint16_t* out_v;
   int32_t* out_idx;   // [batch, Hkv, budget]
-  // 4-bit storage (snapkv_compress_int4), else null: codes [batch, Hkv,
-  // budget, D/2] (two's-complement nibbles, even element low) and per-row
-  // scales [batch, Hkv, budget]
+  // 4-bit or 8-bit storage (snapkv_compress_int4 / _fp8), else null: codes
+  // [batch, Hkv, budget, D/2] (two's-complement nibbles, even element low) or
+  // [batch, Hkv, budget, D] (FP8 E4M3 bytes), and per-row scales [batch, Hkv,
+  // budget]
   uint8_t* out_kq;
   float* out_ks;
   uint8_t* out_vq;
@@ -79,8 +80,9 @@ hipError_t launch_score_vote(const PathParams& p, int head_dim, hipStream_t stre
 // which does it otherwise)
 hipError_t launch_clear_hist(const PathParams& p, hipStream_t stream, StageEvents ev = {});
 hipError_t launch_select(const PathParams& p, hipStream_t stream, StageEvents ev = {});
-// with int4 the rows are stored through out_kq/out_ks/out_vq/out_vs
+// form 0: bf16 rows; 1: 4-bit, 2: FP8 E4M3 codes with per-row scales, through
+// out_kq/out_ks/out_vq/out_vs
 hipError_t launch_gather(const PathParams& p, int head_dim, hipStream_t stream,
-                         StageEvents ev = {}, bool int4 = false);
+                         StageEvents ev = {}, int form = 0);
 
 }  // namespace snapkv

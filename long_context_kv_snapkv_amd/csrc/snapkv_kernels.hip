@@ -73,10 +73,10 @@ __global__ void __launch_bounds__(kThreads) snapkv_select(const PathParams p) {
   snapkv_select_item(p, sm, b, h);
 }
 
-template <int D, bool INT4, int RW>
+template <int D, int FORM, int RW>
 __global__ void __launch_bounds__(kThreads) snapkv_gather(const PathParams p) {
   __shared__ GatherSmem sm;
-  snapkv_gather_item<D, INT4, RW>(p, sm, blockIdx.z, blockIdx.y, blockIdx.x);
+  snapkv_gather_item<D, FORM, RW>(p, sm, blockIdx.z, blockIdx.y, blockIdx.x);
 }
 
 // Launch with one PathParams argument; with events, through the extended
@@ -148,18 +148,21 @@ hipError_t launch_select(const PathParams& p, hipStream_t stream, StageEvents ev
 }
 
 hipError_t launch_gather(const PathParams& p, int head_dim, hipStream_t stream,
-                         StageEvents ev, bool int4) {
+                         StageEvents ev, int form) {
   return dispatch_dim(head_dim, [&](auto d) {
     constexpr int D = decltype(d)::value;
     const dim3 grid(p.n_gather_blocks, p.hkv, p.batch);
+    auto go = [&](auto rw) {
+      constexpr int RW = decltype(rw)::value;
+      if (form == kStoreInt4) return launch(snapkv_gather<D, kStoreInt4, RW>, grid, stream, ev, p);
+      if (form == kStoreFp8) return launch(snapkv_gather<D, kStoreFp8, RW>, grid, stream, ev, p);
+      return launch(snapkv_gather<D, kStoreBf16, RW>, grid, stream, ev, p);
+    };
     if constexpr (D == 128) {
-      if (p.gather_rows == kGatherRows / 2) {
-        if (int4) return launch(snapkv_gather<D, true, kGatherRows / 2>, grid, stream, ev, p);
-        return launch(snapkv_gather<D, false, kGatherRows / 2>, grid, stream, ev, p);
-      }
+      if (p.gather_rows == kGatherRows / 2)
+        return go(std::integral_constant<int, kGatherRows / 2>());
     }
-    if (int4) return launch(snapkv_gather<D, true, kGatherRows>, grid, stream, ev, p);
-    return launch(snapkv_gather<D, false, kGatherRows>, grid, stream, ev, p);
+    return go(std::integral_constant<int, kGatherRows>());
   });
 }
 

@@ -81,6 +81,8 @@ def load_library():
                                          _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                          _vp]
     lib.snapkv_compress_int4.restype = _i32
+    lib.snapkv_compress_fp8.argtypes = lib.snapkv_compress_int4.argtypes
+    lib.snapkv_compress_fp8.restype = _i32
     lib.snapkv_decode_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _pi32,
                                                  ctypes.POINTER(_sz)]
     lib.snapkv_decode_workspace_size.restype = _i32
@@ -277,6 +279,24 @@ def snapkv_compress_int4(q_win: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     [batch, H_kv, B] for K and V, and int32 indices; see include/snapkv.h.
     window_lse (float32 [batch, H_q, W]) optionally replaces the statistics
     pass as in snapkv_compress_from_lse."""
+    return _compress_quant("snapkv_compress_int4", 2, q_win, k, v, seq_lens, window,
+                           kernel_size, pool_mode, budget, window_lse, out, workspace, stream)
+
+
+def snapkv_compress_fp8(q_win: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                        seq_lens: Sequence[int], window: int, kernel_size: int, pool_mode,
+                        budget: int, *, window_lse: Optional[torch.Tensor] = None,
+                        out: Optional[Sequence[torch.Tensor]] = None,
+                        workspace: Optional[torch.Tensor] = None, stream=None):
+    """Compression with the kept rows stored as FP8 E4M3 bytes. Returns (kq,
+    ks, vq, vs, idx) with codes [batch, H_kv, B, D] (uint8); see
+    include/snapkv.h."""
+    return _compress_quant("snapkv_compress_fp8", 1, q_win, k, v, seq_lens, window,
+                           kernel_size, pool_mode, budget, window_lse, out, workspace, stream)
+
+
+def _compress_quant(fn, per_byte, q_win, k, v, seq_lens, window, kernel_size, pool_mode, budget,
+                    window_lse, out, workspace, stream):
     lib = load_library()
     _check_tensor("q_win", q_win, 4)
     _check_tensor("k", k, 3)
@@ -293,15 +313,15 @@ def snapkv_compress_int4(q_win: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             raise ValueError("window_lse must be [batch, H_q, W]")
     dev = q_win.device
     if out is None:
-        kq = torch.empty((batch, hkv, budget, d // 2), dtype=torch.uint8, device=dev)
+        kq = torch.empty((batch, hkv, budget, d // per_byte), dtype=torch.uint8, device=dev)
         vq = torch.empty_like(kq)
         ks = torch.empty((batch, hkv, budget), dtype=torch.float32, device=dev)
         vs = torch.empty_like(ks)
         idx = torch.empty((batch, hkv, budget), dtype=torch.int32, device=dev)
     else:
         kq, ks, vq, vs, idx = out
-    for name, t, dt, shape in (("kq", kq, torch.uint8, (batch, hkv, budget, d // 2)),
-                               ("vq", vq, torch.uint8, (batch, hkv, budget, d // 2)),
+    for name, t, dt, shape in (("kq", kq, torch.uint8, (batch, hkv, budget, d // per_byte)),
+                               ("vq", vq, torch.uint8, (batch, hkv, budget, d // per_byte)),
                                ("ks", ks, torch.float32, (batch, hkv, budget)),
                                ("vs", vs, torch.float32, (batch, hkv, budget)),
                                ("idx", idx, torch.int32, (batch, hkv, budget))):
@@ -310,7 +330,7 @@ def snapkv_compress_int4(q_win: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             raise ValueError(f"{name} must have shape {shape}")
     if workspace is None:
         workspace = new_workspace(hq, hkv, d, vals, window, dev)
-    _check(lib.snapkv_compress_int4(
+    _check(getattr(lib, fn)(
         batch, hq, hkv, d, _ptr(q_win), _ptr(k), _ptr(v), arr, window,
         _ptr(window_lse) if window_lse is not None else None, kernel_size,
         pool_mode_code(pool_mode), budget, _ptr(kq), _ptr(ks), _ptr(vq), _ptr(vs), _ptr(idx),
