@@ -161,35 +161,44 @@ struct KeyStream {
   const uint16_t* kb;
   size_t tstride;
   int key0, kend;
+  bool reverse = false;  // visit the tiles last to first
+
+  __device__ __forceinline__ int ntiles() const { return (kend - key0 + T::KEYS - 1) / T::KEYS; }
+  // first key of the i-th tile visited
+  __device__ __forceinline__ int tile_key(int i) const {
+    return key0 + (reverse ? ntiles() - 1 - i : i) * T::KEYS;
+  }
 
   // Only tile 0 is requested up front: when every CU starts at once, the
   // first tile arrives sooner if it does not compete with deeper prefetch.
   __device__ __forceinline__ void prefetch() {
-    load_key_tile<D>(ra, kb, tstride, key0, kend, threadIdx.x);
+    load_key_tile<D>(ra, kb, tstride, tile_key(0), kend, threadIdx.x);
   }
 
   template <typename Compute, typename After>
   __device__ __forceinline__ void run(unsigned char (*ring)[T::BYTES], Compute&& compute,
                                       After&& after_barrier) {
     const int tid = threadIdx.x;
-    const int ntiles = (kend - key0 + T::KEYS - 1) / T::KEYS;
+    const int ntiles = this->ntiles();
+    // tiles past the end (visited indices >= ntiles) re-read a valid tile
+    auto start = [&](int i) { return tile_key(min(i, ntiles - 1)); };
     store_key_tile<D>(ra, ring[0], tid);
-    load_key_tile<D>(rb, kb, tstride, key0 + T::KEYS, kend, tid);
+    load_key_tile<D>(rb, kb, tstride, start(1), kend, tid);
     asm volatile("" ::: "memory");  // keep tile 1's loads older than tile 2's
-    load_key_tile<D>(ra, kb, tstride, key0 + 2 * T::KEYS, kend, tid);
+    load_key_tile<D>(ra, kb, tstride, start(2), kend, tid);
     lds_barrier();
     after_barrier(0);
     for (int i = 0;; i += 2) {
       compute(ring[0], i);
       if (i + 1 >= ntiles) break;
       store_key_tile<D>(rb, ring[1], tid);
-      load_key_tile<D>(rb, kb, tstride, key0 + (i + 3) * T::KEYS, kend, tid);
+      load_key_tile<D>(rb, kb, tstride, start(i + 3), kend, tid);
       lds_barrier();
       after_barrier(i + 1);
       compute(ring[1], i + 1);
       if (i + 2 >= ntiles) break;
       store_key_tile<D>(ra, ring[0], tid);
-      load_key_tile<D>(ra, kb, tstride, key0 + (i + 4) * T::KEYS, kend, tid);
+      load_key_tile<D>(ra, kb, tstride, start(i + 4), kend, tid);
       lds_barrier();
       after_barrier(i + 2);
     }

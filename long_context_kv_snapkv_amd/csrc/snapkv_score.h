@@ -128,8 +128,11 @@ __device__ __forceinline__ void snapkv_score_stats_item(const PathParams& p, Sta
   const WaveRole role = wave_role(p, wave);
 
   bf16x8 qf[RTW][D / 16];
+  // last tile first: the vote item of the same chunk (same workgroup index,
+  // so the same XCD) starts with the tiles this item read last, which are
+  // then the most likely to still be in that XCD's L2
   KeyStream<D> ks{{}, {}, p.k + ((size_t)p.tab.off[b] * p.hkv + h) * D, (size_t)p.hkv * D,
-                  key0, kend};
+                  key0, kend, true};
   stage_query_frags<D, RTW>(qf, p.q + (size_t)(b * p.hq + h * p.group) * p.window * D, p.rows,
                             p.rows_pad, role.wr, role.nwr, role.my_nrt, sm.ring[1],
                             [&] { ks.prefetch(); });
@@ -199,7 +202,7 @@ __device__ __forceinline__ void snapkv_score_stats_item(const PathParams& p, Sta
 #pragma unroll
     for (int v = 0; v < 16; ++v) pacc[t][v] = -kInf;
   auto compute = [&](const unsigned char* tile, int i) {
-    const int tk0 = key0 + i * KTile<D>::KEYS;
+    const int tk0 = ks.tile_key(i);
     if (tk0 + KTile<D>::KEYS <= full_end) {
       for (int kb = role.wk; kb < KTile<D>::KEYS / 32; kb += role.nwk) {
         bf16x8 kf[D / 16];
