@@ -36,8 +36,8 @@ int largest_pow2_at_most(int x) {
 
 // Everything a call needs, derived from shapes alone, so the workspace size
 // computed ahead of a call matches the call. Workspace layout:
-//   top_hist  uint32[batch * H_kv, 2048]            top-digit histogram per head
-//   sel_table uint32[batch * H_kv, t_stride, 2]     per-segment counts before it
+//   top_hist  uint32[batch * H_kv, 5120]            radix-digit histograms per head
+//   sel_table uint32[batch * H_kv, t_stride, 2]     per-segment counts
 //   sel_meta  uint32[batch * H_kv, 4]               threshold of each head
 //   part      float2[batch, H_kv, nchunk, rows_pad]  per-chunk row statistics
 //   pooled    float [batch, H_kv, p_stride]      pooled scores, p_stride =
@@ -110,7 +110,7 @@ int32_t make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const int32
   const size_t heads = (size_t)batch * hkv;
   size_t off = 0;
   pl->off_top = off;
-  off = align_up(off + heads * snapkv::kTopHistBins * sizeof(uint32_t), 256);
+  off = align_up(off + heads * snapkv::kSelHistWords * sizeof(uint32_t), 256);
   pl->t_stride = (pl->p_stride + snapkv::kSegment - 1) / snapkv::kSegment;
   pl->off_table = off;
   off = align_up(off + heads * pl->t_stride * 2 * sizeof(uint32_t), 256);
@@ -175,6 +175,11 @@ snapkv::PathParams path_params(const Plan& pl, const void* q, const void* k, con
                  : 0;
   p.gather_rows = pl.d == 128 && full_items < 512 ? snapkv::kGatherRows / 2 : snapkv::kGatherRows;
   p.n_gather_blocks = budget > 0 ? (budget + p.gather_rows - 1) / p.gather_rows : 0;
+  // prefixes longer than one selection workgroup holds in registers are
+  // spread over workgroups of kSliceKeys positions
+  p.sel_slices = pl.p_max > snapkv::kSelectHeldKeys
+                     ? (pl.p_max + snapkv::kSliceKeys - 1) / snapkv::kSliceKeys
+                     : 0;
   return p;
 }
 

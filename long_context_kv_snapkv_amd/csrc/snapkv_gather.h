@@ -25,8 +25,11 @@
 namespace snapkv {
 
 struct GatherSmem {
-  int32_t pos[kGatherRows];  // kept position of each of the item's slots
-  int32_t seg[kGatherRows];  // segments holding them
+  int32_t pos[kGatherRows];     // kept position of each of the item's slots
+  int32_t seg[kGatherRows];     // segments holding them
+  uint32_t above[kGatherRows];  // keys above the threshold before each such segment
+  uint32_t equal[kGatherRows];  // keys equal to it before each such segment
+  uint32_t wa[kWaves], we[kWaves];  // per-wave totals of one round of the scan
   uint32_t nseg;
 };
 
@@ -36,7 +39,6 @@ __device__ __forceinline__ void locate_kept(const PathParams& p, GatherSmem& s, 
                                             int lo, int hi) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int P = p.tab.len[b] - p.window;
-  const uint32_t m = (uint32_t)(p.budget - p.window);
   const size_t head = (size_t)(b * p.hkv + h);
   const uint32_t* tab = p.sel_table + head * (size_t)p.table_stride * 2;
   const uint32_t* meta = p.sel_meta + head * 4;
@@ -46,18 +48,44 @@ __device__ __forceinline__ void locate_kept(const PathParams& p, GatherSmem& s, 
   if (tid < kGatherRows) s.pos[tid] = -1;
   if (tid == 0) s.nseg = 0u;
   __syncthreads();
-  // segments whose kept slots [before, before next) meet [lo, hi): each
-  // holds at least one of the item's slots, so there are at most
-  // kGatherRows of them (empty segments are skipped)
-  for (int e = tid; e < nseg; e += kThreads) {
-    const uint32_t kb = tab[2 * e] + min(tab[2 * e + 1], need);
-    const uint32_t ka = e + 1 < nseg ? tab[2 * e + 2] + min(tab[2 * e + 3], need) : m;
-    if (kb < ka && kb < (uint32_t)hi && ka > (uint32_t)lo) {
-      const uint32_t q = atomicAdd(&s.nseg, 1u);
-      if (q < (uint32_t)kGatherRows) s.seg[q] = e;
+  // running sums of the per-segment counts (kThreads segments per round),
+  // then the segments whose kept slots [before, before next) meet [lo, hi):
+  // each holds at least one of the item's slots, so there are at most
+  // kGatherRows of them (empty segments are skipped). After the last
+  // segment the kept count is m.
+  uint32_t carry_a = 0u, carry_e = 0u;
+  for (int base = 0; base < nseg; base += kThreads) {
+    const int e = base + tid;
+    const uint32_t a = e < nseg ? tab[2 * e] : 0u, q = e < nseg ? tab[2 * e + 1] : 0u;
+    const uint32_t ia = wave_incl_scan(a), iq = wave_incl_scan(q);
+    if (lane == 63) {
+      s.wa[wave] = ia;
+      s.we[wave] = iq;
     }
+    __syncthreads();
+    uint32_t ba = carry_a + ia - a, bq = carry_e + iq - q;  // before segment e
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const uint32_t ta = s.wa[w], tq = s.we[w];
+      if (w < wave) {
+        ba += ta;
+        bq += tq;
+      }
+      carry_a += ta;
+      carry_e += tq;
+    }
+    const uint32_t kb = ba + min(bq, need);
+    const uint32_t ka = ba + a + min(bq + q, need);
+    if (e < nseg && kb < ka && kb < (uint32_t)hi && ka > (uint32_t)lo) {
+      const uint32_t slot = atomicAdd(&s.nseg, 1u);
+      if (slot < (uint32_t)kGatherRows) {
+        s.seg[slot] = e;
+        s.above[slot] = ba;
+        s.equal[slot] = bq;
+      }
+    }
+    __syncthreads();  // wa / we are rewritten by the next round
   }
-  __syncthreads();
   const int nneed = min((int)s.nseg, kGatherRows);
   const float* src = p.pooled + head * p.pooled_stride;
   const int last = (P - 1) & ~3;
@@ -74,8 +102,8 @@ __device__ __forceinline__ void locate_kept(const PathParams& p, GatherSmem& s, 
       c += (!settled && key[k] == tau) ? 0x10000u : 0u;
     }
     const uint32_t ex = wave_incl_scan(c) - c;
-    uint32_t above = tab[2 * e] + (ex & 0xFFFFu);
-    uint32_t equal = tab[2 * e + 1] + (ex >> 16);
+    uint32_t above = s.above[q] + (ex & 0xFFFFu);
+    uint32_t equal = s.equal[q] + (ex >> 16);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       uint32_t slot = 0xFFFFFFFFu;

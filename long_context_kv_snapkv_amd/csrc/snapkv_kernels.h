@@ -16,6 +16,12 @@ constexpr int kMaxChunk = 4096;    // keys per scoring work item
 constexpr int kGatherRows = 64;    // compressed rows per gather work item (at most)
 constexpr int kTopHistBins = 2048; // bins of the selection's first radix digit
 constexpr int kSegment = 256;      // positions per selection count-table entry
+// per head: the selection's radix histograms of digits 1, 2 and 3 (2048,
+// 2048 and 1024 bins), adjacent
+constexpr int kSelHistWords = 2048 + 2048 + 1024;
+constexpr int kSliceKeys = 4096;   // prefix positions per sliced-selection work item
+constexpr int kSelectHeldKeys = 64 * kThreads;  // prefix positions one selection workgroup
+                                                // keeps in registers (longer: sliced)
 
 // Per-prompt table passed by value in the kernel arguments.
 struct PromptTable {
@@ -43,9 +49,10 @@ struct PathParams {
   float* pooled;      // [batch, Hkv, pooled_stride] pooled scores c_h[j], j < P
   const float* window_lse;  // [batch, Hq, W] caller's natural-log normaliser of each window
                             // row (snapkv_compress_from_lse), or null
-  uint32_t* top_hist;   // [batch * Hkv, kTopHistBins] histogram of the pooled keys' top 11 bits
-  uint32_t* sel_table;  // [batch * Hkv, table_stride, 2] per kSegment positions: keys above /
-                        // equal to the threshold before the segment
+  uint32_t* top_hist;   // [batch * Hkv, kSelHistWords] histograms of the pooled keys' radix
+                        // digits: top 11 bits, next 11 bits, low 10 bits
+  uint32_t* sel_table;  // [batch * Hkv, table_stride, 2] per kSegment positions: keys in the
+                        // segment above / equal to the threshold
   uint32_t* sel_meta;   // [batch * Hkv, 4]: threshold key, keys equal to it kept, settled
   int32_t batch, hq, hkv, window, group;
   int32_t rows, rows_pad;  // G*W and its round-up to 32
@@ -60,6 +67,8 @@ struct PathParams {
   int32_t n_gather_blocks; // gather items per (prompt, head)
   int32_t gather_rows;     // rows per gather item: kGatherRows, or half of it when
                            // there are few items (D = 128 only)
+  int32_t sel_slices;      // 0: one selection workgroup per head; else kSliceKeys-position
+                           // slices per head of the sliced selection
   float scale_log2;        // log2(e) / sqrt(D)
   PromptTable tab;
 };
@@ -79,6 +88,7 @@ hipError_t launch_score_vote(const PathParams& p, int head_dim, hipStream_t stre
 // zeroes top_hist of the scored heads (stands in for the statistics pass,
 // which does it otherwise)
 hipError_t launch_clear_hist(const PathParams& p, hipStream_t stream, StageEvents ev = {});
+// one workgroup per head, or (sel_slices > 0) three sliced kernels
 hipError_t launch_select(const PathParams& p, hipStream_t stream, StageEvents ev = {});
 // form 0: bf16 rows; 1: 4-bit, 2: FP8 E4M3 codes with per-row scales, through
 // out_kq/out_ks/out_vq/out_vs

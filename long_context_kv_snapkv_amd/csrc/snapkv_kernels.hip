@@ -4,6 +4,8 @@
 //   snapkv_score_vote   (chunk, head, prompt)   window vote + pooling
 //   snapkv_select       (head, prompt)          threshold of the top-(B - W)
 //                                               and its count table
+//     or, for long prefixes, snapkv_select_digit<2>, snapkv_select_digit<3>
+//     and snapkv_select_count over (slice, head, prompt)
 //   snapkv_gather       (row block, head, prompt)  slots -> positions, rows
 //
 //   snapkv_clear_hist   (head, prompt)          zeroes the vote's digit
@@ -58,12 +60,12 @@ __global__ void __launch_bounds__(kThreads) snapkv_score_vote(const PathParams p
 }
 
 // With the caller's row normalisers there is no statistics pass to clear the
-// vote's histogram of top radix digits: one workgroup per head does it.
+// selection's radix histograms: one workgroup per head does it.
 __global__ void __launch_bounds__(kThreads) snapkv_clear_hist(const PathParams p) {
   const int h = blockIdx.x, b = blockIdx.y;
   if (!is_scored(p, b)) return;
-  uint4* top = reinterpret_cast<uint4*>(p.top_hist + (size_t)(b * p.hkv + h) * kTopBins);
-  for (int i = threadIdx.x; i < kTopBins / 4; i += kThreads) top[i] = make_uint4(0u, 0u, 0u, 0u);
+  uint4* top = reinterpret_cast<uint4*>(p.top_hist + (size_t)(b * p.hkv + h) * kSelHistWords);
+  for (int i = threadIdx.x; i < kSelHistWords / 4; i += kThreads) top[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 __global__ void __launch_bounds__(kThreads) snapkv_select(const PathParams p) {
@@ -71,6 +73,22 @@ __global__ void __launch_bounds__(kThreads) snapkv_select(const PathParams p) {
   const int h = blockIdx.x, b = blockIdx.y;
   if (p.tab.len[b] <= p.budget) return;  // kept whole by the gather
   snapkv_select_item(p, sm, b, h);
+}
+
+// sliced selection of long prefixes: grid (slice, head, prompt)
+template <int DIGIT>
+__global__ void __launch_bounds__(kThreads) snapkv_select_digit(const PathParams p) {
+  __shared__ SliceSmem sm;
+  const int sl = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  if (p.tab.len[b] <= p.budget) return;
+  select_digit_slice<DIGIT>(p, sm, b, h, sl);
+}
+
+__global__ void __launch_bounds__(kThreads) snapkv_select_count(const PathParams p) {
+  __shared__ SliceSmem sm;
+  const int sl = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  if (p.tab.len[b] <= p.budget) return;
+  select_count_slice(p, sm, b, h, sl);
 }
 
 template <int D, int FORM, int RW>
@@ -144,7 +162,16 @@ hipError_t launch_clear_hist(const PathParams& p, hipStream_t stream, StageEvent
 }
 
 hipError_t launch_select(const PathParams& p, hipStream_t stream, StageEvents ev) {
-  return launch(snapkv_select, dim3(p.hkv, p.batch), stream, ev, p);
+  if (p.sel_slices == 0) return launch(snapkv_select, dim3(p.hkv, p.batch), stream, ev, p);
+  // the stage's events bracket the three kernels
+  const dim3 grid(p.sel_slices, p.hkv, p.batch);
+  StageEvents first, last;
+  first.start = ev.start;
+  last.stop = ev.stop;
+  hipError_t e = launch(snapkv_select_digit<2>, grid, stream, first, p);
+  if (e == hipSuccess) e = launch(snapkv_select_digit<3>, grid, stream, StageEvents{}, p);
+  if (e == hipSuccess) e = launch(snapkv_select_count, grid, stream, last, p);
+  return e;
 }
 
 hipError_t launch_gather(const PathParams& p, int head_dim, hipStream_t stream,

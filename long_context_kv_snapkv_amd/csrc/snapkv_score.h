@@ -257,9 +257,9 @@ __device__ __forceinline__ void snapkv_score_stats_item(const PathParams& p, Sta
   }
   __syncthreads();
   float2* dst = p.part + ((size_t)(b * p.hkv + h) * p.nchunk + c) * p.rows_pad;
-  if (c == 0) {  // the vote items of this head accumulate into it next
-    uint32_t* top = p.top_hist + (size_t)(b * p.hkv + h) * kTopBins;
-    for (int i = tid; i < kTopBins; i += kThreads) top[i] = 0u;
+  if (c == 0) {  // the vote items (digit 1) and a sliced selection (digits 2, 3) add to these
+    uint32_t* top = p.top_hist + (size_t)(b * p.hkv + h) * kSelHistWords;
+    for (int i = tid; i < kSelHistWords; i += kThreads) top[i] = 0u;
   }
   for (int r = tid; r < p.rows; r += kThreads) {
     const int rt = r >> 5, owner = rt % role.nwr, t = rt / role.nwr;
@@ -440,7 +440,7 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
     // histogram (few distinct bins per chunk, so few global atomics); the
     // barrier covers LDS only, the pooled stores need not have landed
     lds_barrier();
-    uint32_t* top = p.top_hist + head * kTopBins;
+    uint32_t* top = p.top_hist + head * kSelHistWords;
     for (int i = tid; i < kTopBins; i += kThreads) {
       const uint32_t n = sm.top[i];
       if (n != 0u) atomicAdd(&top[i], n);

@@ -26,11 +26,19 @@
 //     largest key is found from the row totals. When every key of that bin
 //     is needed the threshold is settled at that digit: the kept keys are
 //     exactly those >= the bin's lowest key;
-//   * count table: for every kSegment positions, how many keys before them
-//     lie above the threshold and how many equal it (per-slab wave scans of
-//     packed counts, one exclusive scan of the per-(slab, wave) totals).
-//     Only if the last digit leaves a bin of equal keys of which some are
-//     kept are the lowest-positioned ones of them taken.
+//   * count table: for every kSegment positions, how many of its keys lie
+//     above the threshold and how many equal it (one wave sum of packed
+//     counts per segment). Only if the last digit leaves a bin of equal keys
+//     of which some are kept are the lowest-positioned ones of them taken.
+//
+// Long prefixes (sel_slices > 0) spread each head over workgroups of
+// kSliceKeys positions instead, in three kernels: digit 2's histogram,
+// digit 3's histogram and the count table. Each workgroup re-derives the
+// threshold digits known so far from the head's global histograms (the same
+// integer search in every workgroup, so all agree), counts its slice into
+// LDS and adds the non-zero bins to the head's next histogram with global
+// atomics; the kernel boundaries order the passes. Integer sums do not
+// depend on the order of the atomics, so the result is the same.
 #pragma once
 
 #include "snapkv_device.h"
@@ -39,6 +47,7 @@ namespace snapkv {
 
 constexpr int kSlab = 4 * kThreads;  // positions per slab
 constexpr int kMaxSlabsHeld = 16;    // slabs per thread batch: 64 keys in VGPRs
+static_assert(kMaxSlabsHeld * kSlab == kSelectHeldKeys, "resident prefix length");
 constexpr int kBins = kTopBins;      // bins per digit (the last digit uses 1024)
 constexpr int kReplicas = 8;         // histogram copies
 constexpr int kRepStride = kBins + 4;  // words between copies: 16-byte aligned, 4 banks apart
@@ -46,9 +55,8 @@ constexpr int kHistWords = kReplicas * kRepStride;
 
 struct alignas(16) SelectSmem {
   uint32_t rep[2][kHistWords];  // replicated histograms of digits 2 and 3
-  uint32_t cnt[kMaxSlabsHeld * kWaves];      // per (slab, wave): above | equal << 16
   uint32_t rowtot[kWaves];                   // histogram row totals (find)
-  uint32_t sh_bin, sh_need, sh_count, sh_carry0, sh_carry1;
+  uint32_t sh_bin, sh_need, sh_count;
 };
 
 // Keys of slabs slab0 .. slab0+NS-1 for this thread; 0 past P. Loads are
@@ -89,8 +97,8 @@ __device__ __forceinline__ void clear_hist(uint32_t* h, int first) {
 // .. +3. Row totals are exchanged through LDS; the wave holding the
 // threshold then finds it with its lane scan. Requires 1 <= need <= total.
 // Contains two barriers; the result is valid after the second.
-template <typename Counts>
-__device__ __forceinline__ void find_bin(Counts&& counts, uint32_t need, SelectSmem& sm) {
+template <typename Counts, typename Smem>
+__device__ __forceinline__ void find_bin(Counts&& counts, uint32_t need, Smem& sm) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   static_assert(kWaves * 256 == kBins, "one histogram row per wave");
   const u32x4 c = counts();
@@ -133,17 +141,13 @@ __device__ __forceinline__ void select_head(const PathParams& p, SelectSmem& sm,
   const uint32_t m = (uint32_t)(p.budget - p.window);  // 1 <= m < P
   const size_t head = (size_t)(b * p.hkv + h);
   const float* src = p.pooled + head * p.pooled_stride;
-  const uint32_t* top = p.top_hist + head * kTopBins;
+  const uint32_t* top = p.top_hist + head * kSelHistWords;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nbatch = RESIDENT ? 1 : (P + NS * kSlab - 1) / (NS * kSlab);
 
   uint32_t key[NS][4];
   if (RESIDENT) load_keys<NS>(key, src, P, 0);
   clear_hist(sm.rep[0], 0);
-  if (tid == 0) {
-    sm.sh_carry0 = 0u;
-    sm.sh_carry1 = 0u;
-  }
   // digit 1: the histogram the vote kernel accumulated
   find_bin([&] { return *reinterpret_cast<const u32x4*>(top + 256 * wave + 4 * lane); }, m, sm);
   uint32_t prefix = sm.sh_bin << kTopShift;  // resolved high bits of tau
@@ -196,61 +200,184 @@ __device__ __forceinline__ void select_head(const PathParams& p, SelectSmem& sm,
   // tau = prefix exactly, and `need` of the keys equal to tau are kept.
   const uint32_t tau = prefix;
 
-  // ---- count table, one batch at a time. Per slab, each thread counts its
-  // keys above the threshold (settled: >= prefix; otherwise > tau) and equal
-  // to tau, packed as above | equal << 16 (a wave sums at most 256 of each);
-  // the wave totals go through LDS and wave 0 turns them into the counts
-  // before every kSegment positions (one (slab, wave) unit), in position
-  // order. The gather turns these into output slots: a key above the
-  // threshold lands at (above before it) + min(equal before it, need), a key
-  // equal to tau is kept while (equal before it) < need and lands at
-  // (above before it) + (equal before it).
+  // ---- count table: per kSegment positions (one wave's share of a slab),
+  // the keys above the threshold (settled: >= prefix; otherwise > tau) and
+  // the keys equal to tau. The gather turns the running sums of these into
+  // output slots: a key above the threshold lands at (above before it) +
+  // min(equal before it, need), a key equal to tau is kept while (equal
+  // before it) < need and lands at (above before it) + (equal before it).
   static_assert(kSegment == 4 * 64, "a segment is one wave's share of a slab");
-  const int nent = NS * kWaves;
+  const int nseg = (P + kSegment - 1) / kSegment;
   uint32_t* table = p.sel_table + head * (size_t)p.table_stride * 2;
   for (int bt = 0; bt < nbatch; ++bt) {
     if (!RESIDENT) load_keys<NS>(key, src, P, bt * NS);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      uint32_t c = 0;
+      uint32_t c = 0;  // above | equal << 16 (a wave sums at most 256 of each)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t u = key[s][e];
         c += (settled ? u >= tau : u > tau) ? 1u : 0u;
         c += (!settled && u == tau) ? 0x10000u : 0u;
       }
-      const uint32_t incl = wave_incl_scan(c);
-      if (lane == 63) sm.cnt[s * kWaves + wave] = incl;
-    }
-    __syncthreads();
-    if (wave == 0) {  // exclusive prefix of the (above, equal) totals, slab-major
-      const int e0 = 2 * lane, e1 = 2 * lane + 1;
-      const uint32_t c0 = e0 < nent ? sm.cnt[e0] : 0u, c1 = e1 < nent ? sm.cnt[e1] : 0u;
-      const uint32_t a0 = c0 & 0xFFFFu, b0 = c0 >> 16, a1 = c1 & 0xFFFFu, b1 = c1 >> 16;
-      const uint32_t ia = wave_incl_scan(a0 + a1), ib = wave_incl_scan(b0 + b1);
-      const uint32_t ca = sm.sh_carry0, cb = sm.sh_carry1;
-      const uint32_t xa = ca + ia - (a0 + a1), xb = cb + ib - (b0 + b1);
-      const int g0 = bt * nent + e0, g1 = bt * nent + e1;  // segment index in the prefix
-      if (e0 < nent && g0 < p.table_stride) {
-        table[2 * g0] = xa;
-        table[2 * g0 + 1] = xb;
-      }
-      if (e1 < nent && g1 < p.table_stride) {
-        table[2 * g1] = xa + a0;
-        table[2 * g1 + 1] = xb + b0;
-      }
-      if (lane == 63) {
-        sm.sh_carry0 = ca + ia;
-        sm.sh_carry1 = cb + ib;
+      const uint32_t tot = wave_total(wave_incl_scan(c));
+      const int g = (bt * NS + s) * kWaves + wave;  // segment index in the prefix
+      if (lane == 0 && g < nseg) {
+        table[2 * g] = tot & 0xFFFFu;
+        table[2 * g + 1] = tot >> 16;
       }
     }
-    __syncthreads();  // cnt is rewritten by the next batch
   }
   if (tid == 0) {
     uint32_t* meta = p.sel_meta + head * 4;
     meta[0] = tau;
     meta[1] = need;
     meta[2] = settled ? 1u : 0u;
+  }
+}
+
+// ------------------------------------------------------ sliced selection ---
+constexpr int kSliceReplicas = 4;  // histogram copies (8 keys per thread: less contention)
+static_assert(kSliceKeys == 2 * kSlab, "a slice is two slabs: 8 keys per thread");
+
+struct alignas(16) SliceSmem {
+  uint32_t rep[kSliceReplicas * kRepStride];
+  uint32_t rowtot[kWaves];
+  uint32_t sh_bin, sh_need, sh_count;
+};
+
+// The threshold as far as `digits` radix digits, from the head's global
+// histograms hist (digit 1: 2048 bins, digit 2: 2048 bins at +2048, digit
+// 3: 1024 bins at +4096): the resolved high bits `prefix`, the number of
+// bits below them `low`, the keys of the final bin still needed, and whether
+// every key of that bin is kept. Uniform over the workgroup.
+struct Threshold {
+  uint32_t prefix, need;
+  int low;
+  bool settled;
+};
+
+template <typename Smem>
+__device__ __forceinline__ Threshold resolve_digits(const uint32_t* hist, int digits, uint32_t m,
+                                                    Smem& sm) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  Threshold t{0u, m, 32, false};
+#pragma unroll
+  for (int d = 0; d < 3; ++d) {
+    if (d >= digits || t.settled) break;
+    const int shift = d == 0 ? kTopShift : (d == 1 ? 10 : 0);
+    const int nbins = d == 2 ? 1024 : 2048;
+    const uint32_t* hd = hist + 2048 * d;
+    find_bin(
+        [&] {
+          const int i = 256 * wave + 4 * lane;
+          return i < nbins ? *reinterpret_cast<const u32x4*>(hd + i) : u32x4{0u, 0u, 0u, 0u};
+        },
+        t.need, sm);
+    t.prefix |= sm.sh_bin << shift;
+    t.need = sm.sh_need;
+    t.settled = t.need == sm.sh_count;
+    t.low = shift;
+  }
+  return t;
+}
+
+// Keys of positions s0 .. s0 + kSliceKeys - 1 for this thread: slab g holds
+// s0 + g * kSlab + 4t .. +3; 0 past P.
+__device__ __forceinline__ void load_slice_keys(uint32_t (&key)[2][4], const float* src, int P,
+                                                int s0) {
+  const int last = (P - 1) & ~3;
+  float4 v[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+    v[g] = *reinterpret_cast<const float4*>(src + min(s0 + g * kSlab + 4 * (int)threadIdx.x, last));
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int j = s0 + g * kSlab + 4 * (int)threadIdx.x;
+    key[g][0] = j < P ? order_key(v[g].x) : 0u;
+    key[g][1] = j + 1 < P ? order_key(v[g].y) : 0u;
+    key[g][2] = j + 2 < P ? order_key(v[g].z) : 0u;
+    key[g][3] = j + 3 < P ? order_key(v[g].w) : 0u;
+  }
+}
+
+// Digit DIGIT (2: 11 bits at bit 10, 3: 10 bits at bit 0) of the slice's
+// keys that match the threshold's resolved prefix, added to the head's
+// histogram of that digit. Nothing to do once the threshold is settled.
+template <int DIGIT>
+__device__ __forceinline__ void select_digit_slice(const PathParams& p, SliceSmem& sm, int b,
+                                                   int h, int sl) {
+  static_assert(DIGIT == 2 || DIGIT == 3, "digits 2 and 3");
+  constexpr int kShift = DIGIT == 2 ? 10 : 0;
+  constexpr int kBinsHere = DIGIT == 2 ? 2048 : 1024;
+  const int P = p.tab.len[b] - p.window;
+  const int s0 = sl * kSliceKeys;
+  if (s0 >= P) return;
+  const size_t head = (size_t)(b * p.hkv + h);
+  uint32_t* hist = p.top_hist + head * kSelHistWords;
+  const int tid = threadIdx.x;
+  uint32_t key[2][4];
+  load_slice_keys(key, p.pooled + head * p.pooled_stride, P, s0);
+  u32x4* r4 = reinterpret_cast<u32x4*>(sm.rep);
+  for (int i = tid; i < kSliceReplicas * kRepStride / 4; i += kThreads)
+    r4[i] = u32x4{0u, 0u, 0u, 0u};
+  // (the search's barriers also order the clearing before the counting)
+  const Threshold t = resolve_digits(hist, DIGIT - 1, (uint32_t)(p.budget - p.window), sm);
+  if (t.settled) return;
+  uint32_t* hrep = sm.rep + (tid % kSliceReplicas) * kRepStride;
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if ((key[g][e] >> t.low) == (t.prefix >> t.low))
+        atomicAdd(&hrep[(key[g][e] >> kShift) & (kBinsHere - 1)], 1u);
+  __syncthreads();
+  uint32_t* dst = hist + (DIGIT == 2 ? 2048 : 4096);
+  for (int i = tid; i < kBinsHere; i += kThreads) {
+    uint32_t n = 0;
+#pragma unroll
+    for (int r = 0; r < kSliceReplicas; ++r) n += sm.rep[r * kRepStride + i];
+    if (n != 0u) atomicAdd(&dst[i], n);
+  }
+}
+
+// Count table entries of the slice's segments (the same counts as the
+// one-workgroup selection writes) and, from the first slice, the threshold.
+__device__ __forceinline__ void select_count_slice(const PathParams& p, SliceSmem& sm, int b,
+                                                   int h, int sl) {
+  const int P = p.tab.len[b] - p.window;
+  const int s0 = sl * kSliceKeys;
+  if (s0 >= P) return;
+  const size_t head = (size_t)(b * p.hkv + h);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t key[2][4];
+  load_slice_keys(key, p.pooled + head * p.pooled_stride, P, s0);
+  const Threshold t = resolve_digits(p.top_hist + head * kSelHistWords, 3,
+                                     (uint32_t)(p.budget - p.window), sm);
+  const uint32_t tau = t.prefix;  // settled: keep keys >= prefix; else > tau, and `need` == tau
+  const int nseg = (P + kSegment - 1) / kSegment;
+  uint32_t* table = p.sel_table + head * (size_t)p.table_stride * 2;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t u = key[g][e];
+      c += (t.settled ? u >= tau : u > tau) ? 1u : 0u;
+      c += (!t.settled && u == tau) ? 0x10000u : 0u;
+    }
+    const uint32_t tot = wave_total(wave_incl_scan(c));
+    const int seg = (s0 + g * kSlab) / kSegment + wave;
+    if (lane == 0 && seg < nseg) {
+      table[2 * seg] = tot & 0xFFFFu;
+      table[2 * seg + 1] = tot >> 16;
+    }
+  }
+  if (sl == 0 && tid == 0) {
+    uint32_t* meta = p.sel_meta + head * 4;
+    meta[0] = tau;
+    meta[1] = t.need;
+    meta[2] = t.settled ? 1u : 0u;
   }
 }
 

@@ -5,7 +5,7 @@ edge cases: prompts at, just over and under the budget, shorter than the
 window, a one-token prefix, no pooling, kernels wider than the prefix, MHA,
 head_dim 64, window rows that are not a multiple of 32, the 512-row maximum,
 ragged batches mixing kept-whole and compressed prompts, and prefixes longer
-than the LDS-resident selection path.
+than the register-resident selection (the sliced selection), with exact ties.
 """
 
 import numpy as np
@@ -78,6 +78,9 @@ EDGE = [
     ([64, 300, 65, 5, 1000], 8, 2, 128, 32, 5, "avg", 96),  # ragged, mixed
     ([1, 1, 2], 4, 4, 128, 16, 5, "max", 32),     # one-token prompts
     ([40000], 8, 2, 128, 16, 7, "max", 2048),     # prefix > register-resident selection
+    # a prefix past the register-resident length sends the whole call through
+    # the sliced selection: short, kept-whole and one-slice prompts beside it
+    ([40000, 3000, 400, 35000, 4100], 8, 2, 128, 16, 5, "avg", 512),
     ([3000, 2500], 16, 4, 128, 64, 5, "avg", 1024),
 ]
 
@@ -100,14 +103,16 @@ def test_no_planting_flat_scores():
 
 
 @needs_gpu
+@pytest.mark.parametrize("lens", [[3000, 2100], [36000, 2100]], ids=["resident", "sliced"])
 @pytest.mark.parametrize("pool", ["max", "avg"])
-def test_exact_ties_go_to_lowest_positions(pool):
+def test_exact_ties_go_to_lowest_positions(pool, lens):
     # zero queries make every logit 0: all prefix votes are equal, so the
     # selection is decided by ties alone (lowest positions first); avg pooling
-    # lowers the first and last r positions through its zero padding
-    x = make_custom([3000, 2100], 16, 4, 128, 32, seed=9)
+    # lowers the first and last r positions through its zero padding. A
+    # prefix past the register-resident length takes the sliced selection.
+    x = make_custom(lens, 16, 4, 128, 32, seed=9)
     x.q_win[:] = 0
-    print(f"[parity] ties {pool}", flush=True)
+    print(f"[parity] ties {pool} {lens}", flush=True)
     out = full_check(x, 32, 5, pool, 512)
     idx = out["res"]["out_idx"]
     m = 512 - 32
