@@ -18,6 +18,12 @@ constexpr float kInf = __builtin_inff();
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxRowTilesPerWave = 2;  // row tiles of 32 window rows per wave
 
+// Index of this thread's wave in the workgroup, as a wave-uniform (scalar)
+// value, so branches on it and on roles derived from it stay scalar.
+__device__ __forceinline__ int wave_index() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 __device__ __forceinline__ float exp2_fast(float x) {
   return __builtin_amdgcn_exp2f(x);  // v_exp_f32
 }
@@ -30,7 +36,8 @@ __device__ __forceinline__ int acc_row(int v, int lane) {
   return ((v >> 2) << 3) + ((lane >> 5) << 2) + (v & 3);
 }
 
-// Merge two (max, sum of 2^(x - max)) pairs.
+// Merge two (reference m, sum of 2^(x - m)) pairs (the reference need not be
+// the maximum; the result takes the larger one).
 __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
   const float mx = fmaxf(m, m2);
   if (mx == -kInf) return;

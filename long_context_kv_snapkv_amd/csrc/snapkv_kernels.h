@@ -45,7 +45,8 @@ struct PathParams {
   float* out_ks;
   uint8_t* out_vq;
   float* out_vs;
-  float2* part;       // [batch, Hkv, nchunk, rows_pad] per-chunk (max, sum) in log2 units
+  float2* part;       // [batch, Hkv, nchunk, rows_pad] per-chunk (reference m, sum of
+                      // 2^(x - m)) in log2 units
   float* pooled;      // [batch, Hkv, pooled_stride] pooled scores c_h[j], j < P
   const float* window_lse;  // [batch, Hq, W] caller's natural-log normaliser of each window
                             // row (snapkv_compress_from_lse), or null

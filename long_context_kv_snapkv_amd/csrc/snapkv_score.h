@@ -12,9 +12,10 @@
 // Every row's normaliser must be known before a column can be summed, so the
 // keys are visited twice, each time as a bf16 MFMA contraction Q_win . K^T
 // with fp32 accumulation (v_mfma_f32_32x32x16_bf16):
-//   stats item (chunk c): per row, the maximum and the sum of 2^(x - max)
-//        over the chunk's visible keys, x = l * log2(e); C = K . Q^T so a lane
-//        owns one row and the statistics are in-lane online reductions;
+//   stats item (chunk c): per row, a reference m (a block maximum, moved up
+//        only when a later logit exceeds it by more than 64) and the sum of
+//        2^(x - m) over the chunk's visible keys, x = l * log2(e); C = K . Q^T
+//        so a lane owns one row and the statistics are in-lane reductions;
 //   vote item (chunk c): combines the partials of all chunks of the head into
 //        lse_r, recomputes its logits as C = Q . K^T so a lane owns one key,
 //        and column-sums 2^(x - lse) over the rows (in-lane over 16 rows, then
@@ -124,7 +125,7 @@ __device__ __forceinline__ void snapkv_score_stats_item(const PathParams& p, Sta
   const int P = L - p.window;
   const int key0 = c * p.chunk;
   const int kend = min(key0 + p.chunk, L);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const WaveRole role = wave_role(p, wave);
 
   bf16x8 qf[RTW][D / 16];
@@ -170,10 +171,16 @@ __device__ __forceinline__ void snapkv_score_stats_item(const PathParams& p, Sta
       mrun[t] = mnew;
     }
   };
-  // the same update for a block every row sees in full, without branches
-  // (an all -inf block leaves the state unchanged), so it can be interleaved
-  // with the MFMA chain of the next block
-  auto update_full = [&](const f32x16& acc, int t) {
+  // A block every row sees in full. The first block of a row sets its
+  // reference to the block maximum; later blocks are summed against the
+  // reference directly, without a maximum: the pair (m, s) stands for
+  // m + log2(s) whichever m it holds, and a term 2^(x - m) stays finite and
+  // exact to rounding as long as x - m <= 64 (checked on the block sum, which
+  // bounds every term). Terms far below the reference are at most what the
+  // first block's own term (exactly 1) leaves below rounding. A block with a
+  // logit more than 64 above the reference, or the first block, takes the
+  // maximum path, which moves the reference up.
+  auto update_max = [&](const f32x16& acc, int t) {
     float mx0 = fmaxf(acc[0], acc[1]), mx1 = fmaxf(acc[2], acc[3]);
 #pragma unroll
     for (int v = 4; v < 16; v += 4) {
@@ -181,7 +188,7 @@ __device__ __forceinline__ void snapkv_score_stats_item(const PathParams& p, Sta
       mx1 = fmaxf(mx1, fmaxf(acc[v + 2], acc[v + 3]));
     }
     const float mnew = fmaxf(mrun[t], fmaxf(mx0, mx1) * scale);
-    const float mref = mnew == -kInf ? 0.f : mnew;
+    const float mref = mnew == -kInf ? 0.f : mnew;  // an all -inf block changes nothing
     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int v = 0; v < 16; v += 2) {
@@ -191,34 +198,78 @@ __device__ __forceinline__ void snapkv_score_stats_item(const PathParams& p, Sta
     srun[t] = fmaf(srun[t], exp2_fast(mrun[t] - mref), s0 + s1);
     mrun[t] = mnew;
   };
+  constexpr float kBlockSumCap = 0x1p64f;
+  // The direct sum is computed unconditionally, so it can interleave with
+  // the MFMA chain of the next block; with no reference yet (m = -inf) it is
+  // +inf or NaN and the block falls to the maximum path.
+  auto update_full = [&](const f32x16& acc, int t) {
+    const float m = mrun[t];
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; v += 2) {
+      s0 += exp2_fast(fmaf(acc[v], scale, -m));
+      s1 += exp2_fast(fmaf(acc[v + 1], scale, -m));
+    }
+    const float sb = s0 + s1;
+    const bool ok = sb <= kBlockSumCap;  // false for +inf and NaN too
+    srun[t] = ok ? srun[t] + sb : srun[t];
+    if (!ok) update_max(acc, t);
+  };
+  // the MFMA chains of one key block for every row tile of this wave
+  auto chain_block = [&](f32x16 (&acc)[RTW], const bf16x8 (&kf)[D / 16]) {
+#pragma unroll
+    for (int t = 0; t < RTW; ++t) {
+      acc[t] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s)
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[t][s], acc[t], 0, 0, 0);
+    }
+  };
   // Software pipeline over this wave's key blocks: the MFMA chains of block
-  // n are issued, then the softmax update of block n - 1 runs while they
-  // execute. Tiles whose keys are all visible to every row take this path;
-  // the tile that reaches the window or the chunk end flushes the pending
-  // block and is processed with masking.
-  f32x16 pacc[RTW];
+  // n are issued, then the update of block n - 1 runs while they execute.
+  // Blocks go in pairs whose accumulators take turns as the pending one, so
+  // nothing is copied between them. Tiles whose keys are all visible to
+  // every row take this path; the tile that reaches the window or the chunk
+  // end flushes the pending block and is processed with masking.
+  f32x16 pacc[RTW];  // pending block (all -inf: nothing pending)
 #pragma unroll
   for (int t = 0; t < RTW; ++t)
 #pragma unroll
     for (int v = 0; v < 16; ++v) pacc[t][v] = -kInf;
   auto compute = [&](const unsigned char* tile, int i) {
     const int tk0 = ks.tile_key(i);
-    if (tk0 + KTile<D>::KEYS <= full_end) {
+    if (RTW > 1 && tk0 + KTile<D>::KEYS <= full_end) {
+      // two row tiles: the block's second chain runs under the first
+      // update, and the block is retired within the iteration (a pending
+      // block would not fit the register budget)
       for (int kb = role.wk; kb < KTile<D>::KEYS / 32; kb += role.nwk) {
+        f32x16 acc[RTW];
         bf16x8 kf[D / 16];
         read_key_frags<D>(kf, tile, kb, lane);
+        chain_block(acc, kf);
+#pragma unroll
+        for (int t = 0; t < RTW; ++t) update_full(acc[t], t);
+      }
+    } else if (tk0 + KTile<D>::KEYS <= full_end) {
+      for (int kb = role.wk; kb < KTile<D>::KEYS / 32; kb += 2 * role.nwk) {
         f32x16 acc[RTW];
-#pragma unroll
-        for (int t = 0; t < RTW; ++t) {
-          acc[t] = f32x16{};
-#pragma unroll
-          for (int s = 0; s < D / 16; ++s)
-            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[t][s], acc[t], 0, 0, 0);
+        {
+          bf16x8 kf[D / 16];
+          read_key_frags<D>(kf, tile, kb, lane);
+          chain_block(acc, kf);
         }
 #pragma unroll
         for (int t = 0; t < RTW; ++t) update_full(pacc[t], t);
+        if (kb + role.nwk < KTile<D>::KEYS / 32) {
+          bf16x8 kf[D / 16];
+          read_key_frags<D>(kf, tile, kb + role.nwk, lane);
+          chain_block(pacc, kf);
 #pragma unroll
-        for (int t = 0; t < RTW; ++t) pacc[t] = acc[t];
+          for (int t = 0; t < RTW; ++t) update_full(acc[t], t);
+        } else {
+#pragma unroll
+          for (int t = 0; t < RTW; ++t) pacc[t] = acc[t];
+        }
       }
     } else {
 #pragma unroll
@@ -291,7 +342,7 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
   // its own positions (identical values: same keys, same operation order)
   const int r = p.kernel >> 1;
   const int kv0 = max(0, key0 - r), kv1 = min(P, kend + r);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const WaveRole role = wave_role(p, wave);
 
   // statistics of row `row`, chunks sub, sub + tpr, ...: the first batch
@@ -394,6 +445,38 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
   auto compute = [&](const unsigned char* tile, int i) {
     const int tk0 = kv0 + i * KEYS;
     float* vr = &sm.vred[i & 1][2 * role.wr + (lane >> 5)][lane & 31];
+    constexpr int GB = KeyGroup<RTW>::G;
+    // A tile inside the voted range, with every row tile of this wave present
+    // and every group whole, takes a path without per-chain conditions (no
+    // accumulators to define for chains that are not run).
+    if (tk0 + KEYS <= kv1 && role.my_nrt == RTW && GB * role.nwk <= KEYS / 32) {
+      for (int kb = role.wk; kb < KEYS / 32; kb += GB * role.nwk) {
+        bf16x8 kf[GB][D / 16];
+        f32x16 acc[GB][RTW];
+#pragma unroll
+        for (int g = 0; g < GB; ++g) read_key_frags<D>(kf[g], tile, kb + g * role.nwk, lane);
+#pragma unroll
+        for (int g = 0; g < GB; ++g) {
+#pragma unroll
+          for (int t = 0; t < RTW; ++t) {
+            acc[g][t] = f32x16{};
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s)
+              acc[g][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[t][s], kf[g][s], acc[g][t], 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < GB; ++g) {
+          float cs = 0.f;
+#pragma unroll
+          for (int t = 0; t < RTW; ++t)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) cs += exp2_fast(fmaf(acc[g][t][v], scale, -lr[t][v]));
+          vr[(kb + g * role.nwk) * 32] = cs;
+        }
+      }
+      return;
+    }
     for (int kb = role.wk; kb < KEYS / 32; kb += KeyGroup<RTW>::G * role.nwk) {
       if (tk0 + kb * 32 >= kv1) break;
       KeyGroup<RTW> grp(kb, role.nwk, tk0, kv1, KEYS);
