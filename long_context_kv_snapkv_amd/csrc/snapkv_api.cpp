@@ -3,9 +3,13 @@
 // before the first HIP call, so a rejected call enqueues nothing.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
+#include <random>
 #include <string>
 
 #include "snapkv.h"
@@ -40,13 +44,14 @@ int largest_pow2_at_most(int x) {
 //   sel_table uint32[batch * H_kv, t_stride, 2]     per-segment counts
 //   sel_meta  uint32[batch * H_kv, 4]               threshold of each head
 //   part      float2[batch, H_kv, nchunk, rows_pad]  per-chunk row statistics
+//   flags     uint64[batch, H_kv, nchunk]       fused score kernel: published items
 //   pooled    float [batch, H_kv, p_stride]      pooled scores, p_stride =
 //                                                max P rounded up to 64
 // Every word is written by a call before that call reads it.
 struct Plan {
   int batch, hq, hkv, d, window, group, rows, rows_pad, nrt, nwr;
   int chunk, nchunk, l_max, p_max, p_stride;
-  size_t off_top, off_table, off_meta, off_part, off_pooled, bytes;
+  size_t off_top, off_table, off_meta, off_part, off_flags, off_pooled, bytes;
   int t_stride;
   snapkv::PromptTable tab;
 };
@@ -118,6 +123,8 @@ int32_t make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const int32
   off = align_up(off + heads * 4 * sizeof(uint32_t), 256);
   pl->off_part = off;
   off = align_up(off + heads * pl->nchunk * pl->rows_pad * sizeof(float2), 256);
+  pl->off_flags = off;
+  off = align_up(off + heads * pl->nchunk * sizeof(uint64_t), 256);
   pl->off_pooled = off;
   off = align_up(off + heads * pl->p_stride * sizeof(float), 256);
   pl->bytes = off;
@@ -150,6 +157,7 @@ snapkv::PathParams path_params(const Plan& pl, const void* q, const void* k, con
   p.sel_meta = reinterpret_cast<uint32_t*>(w + pl.off_meta);
   p.table_stride = pl.t_stride;
   p.part = reinterpret_cast<float2*>(w + pl.off_part);
+  p.flags = reinterpret_cast<uint64_t*>(w + pl.off_flags);
   p.pooled = reinterpret_cast<float*>(w + pl.off_pooled);
   p.pooled_stride = pl.p_stride;
   p.batch = pl.batch;
@@ -181,6 +189,51 @@ snapkv::PathParams path_params(const Plan& pl, const void* q, const void* k, con
                      ? (pl.p_max + snapkv::kSliceKeys - 1) / snapkv::kSliceKeys
                      : 0;
   return p;
+}
+
+// Compute units of the current device (0 if unknown), cached per device.
+int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Publication marks of the fused score kernel: unique per call in this
+// process and started at a random odd value, so neither an earlier call's
+// flags nor stale memory in a fresh workspace can match.
+uint64_t next_epoch() {
+  static std::atomic<uint64_t> counter{[] {
+    std::random_device rd;
+    const uint64_t t = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+    return ((((uint64_t)rd() << 32) ^ (uint64_t)rd() ^ (t * 0x9E3779B97F4A7C15ull)) | 1ull);
+  }()};
+  return counter.fetch_add(2, std::memory_order_relaxed);
+}
+
+// Statistics and vote in one launch: head_dim 128, one row tile per wave, a
+// chunk's keys fit the LDS slots, the halo fits one block, and every item of
+// the grid can be resident at once (one workgroup per CU). SNAPKV_NO_FUSED_SCORE
+// set to a non-empty value other than "0" turns it off (two launches).
+bool use_fused_scoring(const Plan& pl, int32_t kernel) {
+  static const bool disabled = [] {
+    const char* e = std::getenv("SNAPKV_NO_FUSED_SCORE");
+    return e != nullptr && e[0] != '\0' && std::strcmp(e, "0") != 0;
+  }();
+  if (disabled || pl.d != 128 || pl.rows_pad > snapkv::kFusedMaxRows ||
+      pl.chunk > snapkv::kFusedChunk || kernel / 2 > snapkv::kFusedMaxHalo ||
+      pl.nchunk > snapkv::kThreads)
+    return false;
+  const int64_t items = (int64_t)pl.nchunk * pl.hkv * pl.batch;
+  const int cus = device_cus();
+  return cus > 0 && items <= cus;
 }
 
 bool any_scored(const Plan& pl, int32_t budget, bool score_all) {
@@ -274,15 +327,23 @@ int32_t compress_impl(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const v
     skip(1);
     skip(2);
   } else {
-    if (ext_lse) {
-      // the caller's normalisers replace the statistics pass, which would
-      // also have cleared the vote's digit histogram
-      if ((e = snapkv::launch_clear_hist(p, s, events(0))) != hipSuccess)
-        return hip_fail(e, "snapkv_clear_hist launch");
-    } else if ((e = snapkv::launch_score_stats(p, d, s, events(0))) != hipSuccess)
-      return hip_fail(e, "snapkv_score_stats launch");
-    if ((e = snapkv::launch_score_vote(p, d, s, events(1), ext_lse)) != hipSuccess)
-      return hip_fail(e, "snapkv_score_vote launch");
+    if (!ext_lse && use_fused_scoring(pl, kernel)) {
+      // statistics and vote in one launch (stage 0); stage 1 is empty
+      p.epoch = next_epoch();
+      if ((e = snapkv::launch_score_fused(p, d, s, events(0))) != hipSuccess)
+        return hip_fail(e, "snapkv_score_fused launch");
+      skip(1);
+    } else {
+      if (ext_lse) {
+        // the caller's normalisers replace the statistics pass, which would
+        // also have cleared the vote's digit histogram
+        if ((e = snapkv::launch_clear_hist(p, s, events(0))) != hipSuccess)
+          return hip_fail(e, "snapkv_clear_hist launch");
+      } else if ((e = snapkv::launch_score_stats(p, d, s, events(0))) != hipSuccess)
+        return hip_fail(e, "snapkv_score_stats launch");
+      if ((e = snapkv::launch_score_vote(p, d, s, events(1), ext_lse)) != hipSuccess)
+        return hip_fail(e, "snapkv_score_vote launch");
+    }
     if ((e = snapkv::launch_select(p, s, events(2))) != hipSuccess)
       return hip_fail(e, "snapkv_select launch");
   }

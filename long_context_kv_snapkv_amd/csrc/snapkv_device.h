@@ -57,6 +57,22 @@ constexpr int kTopShift = 21;
 constexpr int kTopBins = kTopHistBins;
 static_assert(kTopBins == 1 << (32 - kTopShift), "top digit");
 
+// hist[bin] += 1 for every active lane, one LDS atomic per distinct bin in
+// the wave (lanes with the bin of the lowest pending lane add together): the
+// pooled scores of a chunk fall into very few bins, and same-address LDS
+// atomics serialise.
+__device__ __forceinline__ void lds_count(uint32_t* hist, uint32_t bin) {
+  const int lane = (int)(threadIdx.x & 63);
+  uint64_t todo = __ballot(1);
+  while (todo != 0) {
+    const int leader = __builtin_ctzll(todo);
+    const uint32_t lb = (uint32_t)__shfl((int)bin, leader);
+    const uint64_t same = __ballot(bin == lb) & todo;
+    if (lane == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(same));
+    todo &= ~same;
+  }
+}
+
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
@@ -182,6 +198,10 @@ struct KeyStream {
     load_key_tile<D>(ra, kb, tstride, tile_key(0), kend, threadIdx.x);
   }
 
+  template <typename Compute>
+  __device__ __forceinline__ void run_resident(unsigned char (*slots)[T::BYTES],
+                                               Compute&& compute);
+
   template <typename Compute, typename After>
   __device__ __forceinline__ void run(unsigned char (*ring)[T::BYTES], Compute&& compute,
                                       After&& after_barrier) {
@@ -211,6 +231,36 @@ struct KeyStream {
     }
   }
 };
+
+// The same stream with every tile kept: tile i (in visit order) is stored
+// to slots[i] and stays there after compute(slots[i], i) returns, so a later
+// pass can read the chunk's keys from LDS. The caller provides one slot per
+// tile.
+template <int D>
+template <typename Compute>
+__device__ __forceinline__ void KeyStream<D>::run_resident(unsigned char (*slots)[T::BYTES],
+                                                           Compute&& compute) {
+  const int tid = threadIdx.x;
+  const int ntiles = this->ntiles();
+  auto start = [&](int i) { return tile_key(min(i, ntiles - 1)); };
+  store_key_tile<D>(ra, slots[0], tid);
+  load_key_tile<D>(rb, kb, tstride, start(1), kend, tid);
+  asm volatile("" ::: "memory");  // keep tile 1's loads older than tile 2's
+  load_key_tile<D>(ra, kb, tstride, start(2), kend, tid);
+  lds_barrier();
+  for (int i = 0;; i += 2) {
+    compute(slots[i], i);
+    if (i + 1 >= ntiles) break;
+    store_key_tile<D>(rb, slots[i + 1], tid);
+    load_key_tile<D>(rb, kb, tstride, start(i + 3), kend, tid);
+    lds_barrier();
+    compute(slots[i + 1], i + 1);
+    if (i + 2 >= ntiles) break;
+    store_key_tile<D>(ra, slots[i + 2], tid);
+    load_key_tile<D>(ra, kb, tstride, start(i + 4), kend, tid);
+    lds_barrier();
+  }
+}
 
 // Query fragments of this wave's row tiles (same D-to-k-slot map as the
 // keys), staged through LDS: the group's rows (contiguous in q_win) are read

@@ -22,6 +22,12 @@ constexpr int kSelHistWords = 2048 + 2048 + 1024;
 constexpr int kSliceKeys = 4096;   // prefix positions per sliced-selection work item
 constexpr int kSelectHeldKeys = 64 * kThreads;  // prefix positions one selection workgroup
                                                 // keeps in registers (longer: sliced)
+// fused score kernel (statistics and vote in one launch, key chunk resident
+// in LDS): limits of the shapes it takes
+constexpr int kFusedTiles = 4;                  // resident 128-key tiles per item
+constexpr int kFusedChunk = kFusedTiles * 128;  // keys per item (at most)
+constexpr int kFusedMaxHalo = 16;               // kernel / 2 (at most)
+constexpr int kFusedMaxRows = 256;              // G * W rounded up to 32 (one row tile per wave)
 
 // Per-prompt table passed by value in the kernel arguments.
 struct PromptTable {
@@ -55,6 +61,9 @@ struct PathParams {
   uint32_t* sel_table;  // [batch * Hkv, table_stride, 2] per kSegment positions: keys in the
                         // segment above / equal to the threshold
   uint32_t* sel_meta;   // [batch * Hkv, 4]: threshold key, keys equal to it kept, settled
+  uint64_t* flags;      // [batch, Hkv, nchunk] fused score kernel: `epoch` once an item's
+                        // row statistics are published
+  uint64_t epoch;       // this call's publication mark (unique per call in the process)
   int32_t batch, hq, hkv, window, group;
   int32_t rows, rows_pad;  // G*W and its round-up to 32
   int32_t nwr;             // waves that split the row tiles (power of two)
@@ -89,6 +98,10 @@ hipError_t launch_score_vote(const PathParams& p, int head_dim, hipStream_t stre
 // zeroes top_hist of the scored heads (stands in for the statistics pass,
 // which does it otherwise)
 hipError_t launch_clear_hist(const PathParams& p, hipStream_t stream, StageEvents ev = {});
+// statistics and vote in one launch (head_dim 128 and the kFused* limits;
+// every item of the grid must be able to be resident at once)
+hipError_t launch_score_fused(const PathParams& p, int head_dim, hipStream_t stream,
+                              StageEvents ev = {});
 // one workgroup per head, or (sel_slices > 0) three sliced kernels
 hipError_t launch_select(const PathParams& p, hipStream_t stream, StageEvents ev = {});
 // form 0: bf16 rows; 1: 4-bit, 2: FP8 E4M3 codes with per-row scales, through

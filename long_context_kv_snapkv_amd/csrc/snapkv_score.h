@@ -118,9 +118,17 @@ struct KeyGroup {
 };
 
 // ---------------------------------------------------------------- stats ---
-template <int D, int RTW>
-__device__ __forceinline__ void snapkv_score_stats_item(const PathParams& p, StatsSmem<D>& sm,
-                                                        int b, int h, int c) {
+// The statistics pass of one item. `qbuf` (one tile of LDS) stages the query
+// rows, `wstats` collects the waves' row statistics, and run(ks, compute)
+// streams the chunk's key tiles (through a ring, or into resident slots for
+// the fused kernel). The query fragments are left in `qf`. With COHERENT the
+// statistics and the histogram clearing are written with device-coherent
+// stores (another workgroup of the same kernel reads them).
+template <int D, int RTW, bool COHERENT, typename Run>
+__device__ __forceinline__ void score_stats_body(const PathParams& p, unsigned char* qbuf,
+                                                 float2 (*wstats)[kMaxRowTilesPerWave * 32],
+                                                 bf16x8 (&qf)[RTW][D / 16], Run&& run, int b,
+                                                 int h, int c) {
   const int L = p.tab.len[b];
   const int P = L - p.window;
   const int key0 = c * p.chunk;
@@ -128,14 +136,13 @@ __device__ __forceinline__ void snapkv_score_stats_item(const PathParams& p, Sta
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const WaveRole role = wave_role(p, wave);
 
-  bf16x8 qf[RTW][D / 16];
   // last tile first: the vote item of the same chunk (same workgroup index,
   // so the same XCD) starts with the tiles this item read last, which are
   // then the most likely to still be in that XCD's L2
   KeyStream<D> ks{{}, {}, p.k + ((size_t)p.tab.off[b] * p.hkv + h) * D, (size_t)p.hkv * D,
                   key0, kend, true};
   stage_query_frags<D, RTW>(qf, p.q + (size_t)(b * p.hq + h * p.group) * p.window * D, p.rows,
-                            p.rows_pad, role.wr, role.nwr, role.my_nrt, sm.ring[1],
+                            p.rows_pad, role.wr, role.nwr, role.my_nrt, qbuf,
                             [&] { ks.prefetch(); });
 
   int lim[RTW];  // last key visible to this lane's row
@@ -204,13 +211,10 @@ __device__ __forceinline__ void snapkv_score_stats_item(const PathParams& p, Sta
   // +inf or NaN and the block falls to the maximum path.
   auto update_full = [&](const f32x16& acc, int t) {
     const float m = mrun[t];
-    float s0 = 0.f, s1 = 0.f;
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};  // short dependent add chains
 #pragma unroll
-    for (int v = 0; v < 16; v += 2) {
-      s0 += exp2_fast(fmaf(acc[v], scale, -m));
-      s1 += exp2_fast(fmaf(acc[v + 1], scale, -m));
-    }
-    const float sb = s0 + s1;
+    for (int v = 0; v < 16; ++v) s4[v & 3] += exp2_fast(fmaf(acc[v], scale, -m));
+    const float sb = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     const bool ok = sb <= kBlockSumCap;  // false for +inf and NaN too
     srun[t] = ok ? srun[t] + sb : srun[t];
     if (!ok) update_max(acc, t);
@@ -294,7 +298,7 @@ __device__ __forceinline__ void snapkv_score_stats_item(const PathParams& p, Sta
       }
     }
   };
-  ks.run(sm.ring, compute, [](int) {});
+  run(ks, compute);
 #pragma unroll
   for (int t = 0; t < RTW; ++t) update_full(pacc[t], t);
 
@@ -304,23 +308,42 @@ __device__ __forceinline__ void snapkv_score_stats_item(const PathParams& p, Sta
     const float mo = __shfl_xor(mrun[t], 32);
     const float so = __shfl_xor(srun[t], 32);
     lse_merge(mrun[t], srun[t], mo, so);
-    if (lane < 32 && t < role.my_nrt) sm.wstats[wave][t * 32 + lane] = make_float2(mrun[t], srun[t]);
+    if (lane < 32 && t < role.my_nrt) wstats[wave][t * 32 + lane] = make_float2(mrun[t], srun[t]);
   }
   __syncthreads();
   float2* dst = p.part + ((size_t)(b * p.hkv + h) * p.nchunk + c) * p.rows_pad;
   if (c == 0) {  // the vote items (digit 1) and a sliced selection (digits 2, 3) add to these
     uint32_t* top = p.top_hist + (size_t)(b * p.hkv + h) * kSelHistWords;
-    for (int i = tid; i < kSelHistWords; i += kThreads) top[i] = 0u;
+    for (int i = tid; i < kSelHistWords; i += kThreads) {
+      if constexpr (COHERENT)
+        __hip_atomic_store(&top[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        top[i] = 0u;
+    }
   }
   for (int r = tid; r < p.rows; r += kThreads) {
     const int rt = r >> 5, owner = rt % role.nwr, t = rt / role.nwr;
     float m = -kInf, s = 0.f;
     for (int q = 0; q < role.nwk; ++q) {
-      const float2 e = sm.wstats[owner + role.nwr * q][t * 32 + (r & 31)];
+      const float2 e = wstats[owner + role.nwr * q][t * 32 + (r & 31)];
       lse_merge(m, s, e.x, e.y);
     }
-    dst[r] = make_float2(m, s);
+    if constexpr (COHERENT)
+      __hip_atomic_store(reinterpret_cast<uint64_t*>(&dst[r]),
+                         __builtin_bit_cast(uint64_t, make_float2(m, s)), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    else
+      dst[r] = make_float2(m, s);
   }
+}
+
+template <int D, int RTW>
+__device__ __forceinline__ void snapkv_score_stats_item(const PathParams& p, StatsSmem<D>& sm,
+                                                        int b, int h, int c) {
+  bf16x8 qf[RTW][D / 16];
+  score_stats_body<D, RTW, false>(
+      p, sm.ring[1], sm.wstats, qf,
+      [&](KeyStream<D>& ks, auto&& compute) { ks.run(sm.ring, compute, [](int) {}); }, b, h, c);
 }
 
 // ----------------------------------------------------------------- vote ---
@@ -431,16 +454,18 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
   };
   // column sums over this wave's rows of block kb (keys tk0 + kb*32 + lane%32):
   // lanes l and l + 32 hold different rows of the same key, so each half
-  // writes its own partial
+  // writes its own partial. Four partial sums keep the dependent add chains
+  // short; every key of a wave is summed in this same order on every path,
+  // so equal columns give equal votes.
   auto colsum = [&](const f32x16(&acc)[RTW]) {
-    float cs = 0.f;
+    float c4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < RTW; ++t) {
       if (t >= role.my_nrt) break;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) cs += exp2_fast(fmaf(acc[t][v], scale, -lr[t][v]));
+      for (int v = 0; v < 16; ++v) c4[v & 3] += exp2_fast(fmaf(acc[t][v], scale, -lr[t][v]));
     }
-    return cs;
+    return (c4[0] + c4[1]) + (c4[2] + c4[3]);
   };
   auto compute = [&](const unsigned char* tile, int i) {
     const int tk0 = kv0 + i * KEYS;
@@ -467,12 +492,13 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
         }
 #pragma unroll
         for (int g = 0; g < GB; ++g) {
-          float cs = 0.f;
+          // the order of colsum below
+          float c4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int t = 0; t < RTW; ++t)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) cs += exp2_fast(fmaf(acc[g][t][v], scale, -lr[t][v]));
-          vr[(kb + g * role.nwk) * 32] = cs;
+            for (int v = 0; v < 16; ++v) c4[v & 3] += exp2_fast(fmaf(acc[g][t][v], scale, -lr[t][v]));
+          vr[(kb + g * role.nwk) * 32] = (c4[0] + c4[1]) + (c4[2] + c4[3]);
         }
       }
       return;
@@ -516,7 +542,7 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
     const float c_j = pool_value([&](int u) { return sm.s_chunk[u - kv0]; }, j, P, p.kernel,
                                  p.pool_mode);
     pooled[j] = c_j;
-    if (!p.export_scores) atomicAdd(&sm.top[order_key(c_j) >> kTopShift], 1u);
+    if (!p.export_scores) lds_count(sm.top, order_key(c_j) >> kTopShift);
   }
   if (!p.export_scores) {
     // the selection's first radix digit: this chunk's counts join the head's
@@ -528,6 +554,242 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
       const uint32_t n = sm.top[i];
       if (n != 0u) atomicAdd(&top[i], n);
     }
+  }
+}
+
+// ---------------------------------------------------------------- fused ---
+// Statistics and vote of one chunk in a single launch, for shapes where every
+// item can be resident at once and a chunk's keys fit in LDS. Phase 1 is the
+// statistics pass with the chunk's key tiles kept in LDS; the item publishes
+// its row statistics with device-coherent stores and then a per-item flag
+// (this call's `epoch`). Phase 2 waits for the flags of every chunk of its
+// head, merges the statistics into each row's normaliser, and votes from the
+// resident tiles plus a block of the r halo keys on each side (loaded while
+// it waits), then pools and counts as the vote item does. The arithmetic of
+// every vote, normaliser and pooled value is the vote item's, in the same
+// order, so both paths give identical bits. Every wait is bounded: after
+// kSpinLimit polls the item gives up and writes NaN scores, which the
+// selection and any comparison expose; the host only takes this path when
+// the grid fits the device one workgroup per CU, so the bound is not reached.
+constexpr int kSpinLimit = 1 << 20;
+
+template <int D>
+struct alignas(16) FusedSmem {
+  unsigned char k[kFusedTiles][KTile<D>::BYTES];  // the chunk's key tiles
+  unsigned char halo[32 * KTile<D>::ROWB];       // r keys on each side of the voted range
+  union {
+    float2 wstats[kWaves][kMaxRowTilesPerWave * 32];
+    float2 scratch[kThreads];
+  } u;
+  float lse[kFusedMaxRows];
+  float s_chunk[kFusedChunk + 2 * kFusedMaxHalo];  // votes of keys kv0 ..
+};
+static_assert(sizeof(FusedSmem<128>) <= 160 * 1024, "fused item LDS");
+static_assert(kTopBins * 4 <= KTile<128>::BYTES, "histogram in a key slot");
+
+template <int D>
+__device__ __forceinline__ void snapkv_score_fused_item(const PathParams& p, FusedSmem<D>& sm,
+                                                        int b, int h, int c) {
+  constexpr int RTW = 1;
+  constexpr int KEYS = KTile<D>::KEYS;
+  const int L = p.tab.len[b];
+  const int P = L - p.window;
+  const int key0 = c * p.chunk;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
+  const WaveRole role = wave_role(p, wave);
+  const int nch = (L + p.chunk - 1) / p.chunk;
+  const size_t head = (size_t)(b * p.hkv + h);
+  const uint16_t* kbase = p.k + ((size_t)p.tab.off[b] * p.hkv + h) * D;
+  const size_t tstride = (size_t)p.hkv * D;
+
+  // phase 1: statistics; the query rows are staged through the last slot,
+  // which the stream fills last
+  bf16x8 qf[RTW][D / 16];
+  int nst = 0;  // tiles of the chunk, stored to the slots last tile first
+  score_stats_body<D, RTW, true>(
+      p, sm.k[kFusedTiles - 1], sm.u.wstats, qf,
+      [&](KeyStream<D>& ks, auto&& compute) {
+        nst = ks.ntiles();
+        ks.run_resident(sm.k, compute);
+      },
+      b, h, c);
+  // publish: this thread's coherent stores are complete, then every thread's
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  uint64_t* flags = p.flags + head * p.nchunk;
+  if (tid == 0) __hip_atomic_store(&flags[c], p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (key0 >= P) return;  // a chunk of window keys only: nothing to vote
+
+  // phase 2: the voted positions [key0, kend) and their pooling halo
+  const int kend = min(key0 + p.chunk, P);
+  const int r = p.kernel >> 1;
+  const int kv0 = max(0, key0 - r), kv1 = min(P, kend + r);
+  const int rl = key0 - kv0, rr = kv1 - kend;  // halo keys before and after
+  {
+    // halo row i: key kv0 + i (i < rl), kend + i - rl (i < rl + rr); other
+    // rows repeat key0 and are never folded
+    constexpr int PIECES = KTile<D>::PIECES;
+    for (int pc = tid; pc < 32 * PIECES; pc += kThreads) {
+      const int row = pc / PIECES, col = pc % PIECES;
+      const int j = row < rl ? kv0 + row : (row < rl + rr ? kend + row - rl : key0);
+      const u32x4 x = *reinterpret_cast<const u32x4*>(kbase + (size_t)j * tstride + col * 8);
+      *reinterpret_cast<u32x4*>(sm.halo + row * KTile<D>::ROWB + col * 16) = x;
+    }
+  }
+  // wait for the statistics of every chunk of this head (bounded)
+  int timed_out = 0;
+  if (tid < nch) {
+    int spins = 0;
+    while (__hip_atomic_load(&flags[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != p.epoch) {
+      if (++spins > kSpinLimit) {
+        timed_out = 1;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  timed_out = __syncthreads_or(timed_out);
+
+  // lse of every row, exactly as the vote item merges it, from coherent loads
+  const float2* part = p.part + head * p.nchunk * p.rows_pad;
+  int tpr = 1;
+  while (tpr * 2 * p.rows_pad <= kThreads) tpr *= 2;
+  const int span = kThreads / tpr;  // rows per round (>= rows_pad)
+  const int row = tid % span, sub = tid / span;
+  const bool row_ok = row < p.rows;
+  const int row_c = min(row, p.rows - 1);
+  auto load_part = [&](int cc) {
+    uint64_t* a = const_cast<uint64_t*>(
+        reinterpret_cast<const uint64_t*>(&part[(size_t)cc * p.rows_pad + row_c]));
+    return __builtin_bit_cast(float2,
+                              __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  };
+  float2 pe[kPartBatch];
+#pragma unroll
+  for (int u = 0; u < kPartBatch; ++u) pe[u] = load_part(min(sub + u * tpr, nch - 1));
+  {
+    float m = -kInf, s = 0.f;
+#pragma unroll
+    for (int u = 0; u < kPartBatch; ++u)
+      if (sub + u * tpr < nch) m = fmaxf(m, pe[u].x);
+    if (m != -kInf) {
+#pragma unroll
+      for (int u = 0; u < kPartBatch; ++u)
+        if (sub + u * tpr < nch) s += pe[u].y * exp2_fast(pe[u].x - m);
+    }
+    for (int cc = sub + kPartBatch * tpr; cc < nch; cc += tpr) {
+      const float2 e = load_part(cc);
+      lse_merge(m, s, e.x, e.y);
+    }
+    sm.u.scratch[tid] = row_ok ? make_float2(m, s) : make_float2(-kInf, 0.f);
+    lds_barrier();
+    if (tid < p.rows_pad) {
+      float mm = -kInf, ss = 0.f;
+      for (int q = 0; q < tpr; ++q) {
+        const float2 e = sm.u.scratch[q * span + tid];
+        lse_merge(mm, ss, e.x, e.y);
+      }
+      sm.lse[tid] = tid < p.rows ? mm + log2f(ss) : kInf;  // padded rows add 0
+    }
+    __syncthreads();
+  }
+  float lr[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) lr[v] = sm.lse[min(role.wr * 32 + acc_row(v, lane), kFusedMaxRows - 1)];
+  const float scale = p.scale_log2;
+
+  // the vote item's per-key arithmetic: the block's logits by one MFMA
+  // chain, then the column sum over this wave's rows in colsum's order
+  auto chain = [&](const unsigned char* tile, int kb) {
+    bf16x8 kf[D / 16];
+    read_key_frags<D>(kf, tile, kb, lane);
+    f32x16 acc = {};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][s], kf[s], acc, 0, 0, 0);
+    return acc;
+  };
+  auto colsum = [&](const f32x16& acc) {
+    float c4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int v = 0; v < 16; ++v) c4[v & 3] += exp2_fast(fmaf(acc[v], scale, -lr[v]));
+    return (c4[0] + c4[1]) + (c4[2] + c4[3]);
+  };
+  const int nparts = 2 * role.nwr;  // (row-tile wave, lane half) partial sums per key
+  // Every block this wave votes (its blocks of each resident tile, and the
+  // halo block for the waves of key group 0) is computed first, with the
+  // column sums kept in registers, so the waves run through the MFMA and
+  // exp work without meeting at barriers. The key tiles are then dead: the
+  // partial sums of every voted key go to an array in their place and are
+  // folded in one pass, in the fixed order of the vote item.
+  const int nvt = (kend - key0 + KEYS - 1) / KEYS;  // tiles holding voted keys
+  auto has = [&](int tt, int q) {
+    const int kb = role.wk + q * role.nwk;
+    return tt < nvt && kb < KEYS / 32 && key0 + tt * KEYS + kb * 32 < kend;
+  };
+  const bool halo = rl + rr > 0;
+  float ph = 0.f;
+  if (halo && role.wk == 0) ph = colsum(chain(sm.halo, 0));
+  float pv[kFusedTiles][4] = {};
+#pragma unroll
+  for (int tt = 0; tt < kFusedTiles; ++tt) {
+    const unsigned char* tile = sm.k[max(nst - 1 - tt, 0)];
+#pragma unroll
+    for (int q = 0; q < 4; q += 2) {
+      const int kb0 = role.wk + q * role.nwk, kb1 = kb0 + role.nwk;
+      if (has(tt, q + 1)) {  // two chains in flight before either column sum
+        const f32x16 a0 = chain(tile, kb0);
+        const f32x16 a1 = chain(tile, kb1);
+        pv[tt][q] = colsum(a0);
+        pv[tt][q + 1] = colsum(a1);
+      } else if (has(tt, q)) {
+        pv[tt][q] = colsum(chain(tile, kb0));
+      }
+    }
+  }
+  constexpr int kVotedMax = kFusedChunk + 2 * kFusedMaxHalo;
+  static_assert(2 * kWaves * kVotedMax * 4 <= 2 * KTile<D>::BYTES, "partials in two key slots");
+  float (*vall)[kVotedMax] = reinterpret_cast<float (*)[kVotedMax]>(&sm.k[0][0]);
+  __syncthreads();  // every wave is done with the key tiles
+  {
+    const int col = lane & 31;
+    float* mine = vall[2 * role.wr + (lane >> 5)];  // this (row-tile wave, lane half)
+    if (halo && role.wk == 0 && col < rl + rr)
+      mine[col < rl ? col : kend - kv0 + col - rl] = ph;
+#pragma unroll
+    for (int tt = 0; tt < kFusedTiles; ++tt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int key = key0 + tt * KEYS + (role.wk + q * role.nwk) * 32 + col;
+        if (has(tt, q) && key < kend) mine[key - kv0] = pv[tt][q];
+      }
+  }
+  __syncthreads();
+  for (int kk = tid; kk < kv1 - kv0; kk += kThreads) {
+    float s = 0.f;
+    for (int q = 0; q < nparts; ++q) s += vall[q][kk];
+    sm.s_chunk[kk] = s;
+  }
+  __syncthreads();
+
+  // snapkv_pool and the first radix digit, as in the vote item; the
+  // histogram lives in a key slot no longer read
+  uint32_t* top = reinterpret_cast<uint32_t*>(sm.k[2]);
+  for (int i = tid; i < kTopBins; i += kThreads) top[i] = 0u;
+  lds_barrier();
+  float* pooled = p.pooled + head * p.pooled_stride;
+  for (int j = key0 + tid; j < kend; j += kThreads) {
+    float c_j = pool_value([&](int u) { return sm.s_chunk[u - kv0]; }, j, P, p.kernel,
+                           p.pool_mode);
+    if (timed_out) c_j = __builtin_nanf("");
+    pooled[j] = c_j;
+    lds_count(top, order_key(c_j) >> kTopShift);
+  }
+  lds_barrier();
+  uint32_t* gtop = p.top_hist + head * kSelHistWords;
+  for (int i = tid; i < kTopBins; i += kThreads) {
+    const uint32_t n = top[i];
+    if (n != 0u) atomicAdd(&gtop[i], n);
   }
 }
 
