@@ -3,7 +3,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one snapkv_compress call (vote statistics, vote with pooling,
-selection, gather: four kernels) on one layer of synthetic, seeded input
+selection, gather: four kernels, or three when statistics and vote run as
+the fused score kernel) on one layer of synthetic, seeded input
 already resident in HBM. Inputs and outputs rotate over enough buffer sets to
 exceed the 256 MB Infinity Cache, so every step streams its K from HBM.
 Prints one JSON line: value = prompt tokens compressed per second per layer;
@@ -47,16 +48,18 @@ def algorithmic_bytes(w, seq_lens):
 
 def stage_bytes(w, seq_lens):
     """Algorithmic bytes of each stage kernel for one call (per launch):
-    stats reads Q and all L keys; vote reads Q and the P prefix keys; select
-    reads the P pooled scores and writes the index list; gather moves the
-    kept rows (the gather term of algorithmic_bytes)."""
+    stats reads Q and all L keys; vote reads Q and the P prefix keys; the
+    fused score kernel (both in one launch) reads Q and all L keys once;
+    select reads the P pooled scores and writes the index list; gather moves
+    the kept rows (the gather term of algorithmic_bytes)."""
     d, q_bytes = w.head_dim, w.h_q * w.window * w.head_dim * 2
-    out = {"snapkv_score_stats": 0, "snapkv_score_vote": 0, "snapkv_select": 0,
-           "snapkv_gather": algorithmic_bytes(w, seq_lens)[1]}
+    out = {"snapkv_score_stats": 0, "snapkv_score_vote": 0, "snapkv_score_fused": 0,
+           "snapkv_select": 0, "snapkv_gather": algorithmic_bytes(w, seq_lens)[1]}
     for L in seq_lens:
         if L > w.budget:
             P = L - w.window
             out["snapkv_score_stats"] += q_bytes + w.h_kv * L * d * 2
+            out["snapkv_score_fused"] += q_bytes + w.h_kv * L * d * 2
             out["snapkv_score_vote"] += q_bytes + w.h_kv * P * d * 2
             out["snapkv_select"] += w.h_kv * (P * 4 + w.budget * 4)
     return out
@@ -217,10 +220,15 @@ def main():
     for i in range(nprof):
         step(i, staged=True, events=evs[i])
     torch.cuda.synchronize()
+    # with the fused score kernel, stage 0 is that kernel and stage 1 is empty
+    fused = skv.snapkv_score_kernels(w.h_q, hkv, d, lens, w.window, w.kernel) == 1
     stage_ms = {}
     for s_ in range(nst):
+        if fused and s_ == 1:
+            continue
         vals = [row[2 * s_].elapsed_time(row[2 * s_ + 1]) for row in evs]
-        stage_ms[skv.snapkv_stage_name(s_)] = float(np.mean(vals))
+        name = "snapkv_score_fused" if fused and s_ == 0 else skv.snapkv_stage_name(s_)
+        stage_ms[name] = float(np.mean(vals))
 
     # the same compression when the caller's prefill attention hands over
     # each window row's log-sum-exp (snapkv_compress_from_lse): the
@@ -330,7 +338,8 @@ def main():
     score_b, gather_b = algorithmic_bytes(w, lens)
     total_b = score_b + gather_b
     flops = score_flops(w, lens)
-    score_ms = stage_ms["snapkv_score_stats"] + stage_ms["snapkv_score_vote"]
+    score_ms = (stage_ms["snapkv_score_fused"] if fused else
+                stage_ms["snapkv_score_stats"] + stage_ms["snapkv_score_vote"])
     tokens = sum(lens)
     value = tokens / (ms_step * 1e-3)
     roofline = {
@@ -356,6 +365,7 @@ def main():
                                                        BF16_PEAK_TFLOPS, 4),
                             "issued_2pass": round(2 * flops / (score_ms * 1e-3) / 1e12 /
                                                   BF16_PEAK_TFLOPS, 4)},
+        "score_kernels": 1 if fused else 2,
         "stage_kernels": {k: {"ms": round(v, 5), "alg_bytes": sbytes[k],
                               "gbps": round(sbytes[k] / (v * 1e-3) / 1e9, 1)}
                           for k, v in stage_ms.items()},

@@ -423,6 +423,19 @@ int32_t make_decode_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t d, int3
 
 extern "C" {
 
+int32_t snapkv_score_kernels(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, const int32_t* seq_lens, int32_t window,
+                             int32_t kernel_size, int32_t* kernels) {
+  if (kernels == nullptr) return fail(SNAPKV_ERR_INVALID_ARGUMENT, "kernels is NULL");
+  Plan pl;
+  int32_t st = make_plan(batch, num_q_heads, num_kv_heads, head_dim, seq_lens, window, &pl);
+  if (st != SNAPKV_OK) return st;
+  st = check_pool(kernel_size, SNAPKV_POOL_AVG);
+  if (st != SNAPKV_OK) return st;
+  *kernels = use_fused_scoring(pl, kernel_size) ? 1 : 2;
+  return SNAPKV_OK;
+}
+
 int32_t snapkv_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t head_dim, const int32_t* seq_lens, int32_t window,
                               size_t* bytes) {

@@ -96,6 +96,8 @@ def load_library():
     lib.snapkv_status_string.restype = ctypes.c_char_p
     lib.snapkv_last_error.argtypes = []
     lib.snapkv_last_error.restype = ctypes.c_char_p
+    lib.snapkv_score_kernels.argtypes = [_i32, _i32, _i32, _i32, _pi32, _i32, _i32, _pi32]
+    lib.snapkv_score_kernels.restype = _i32
     lib.snapkv_stage_name.argtypes = [_i32]
     lib.snapkv_stage_name.restype = ctypes.c_char_p
     _lib = lib
@@ -429,6 +431,17 @@ def snapkv_status_string(status: int) -> str:
 
 def snapkv_last_error() -> str:
     return load_library().snapkv_last_error().decode()
+
+
+def snapkv_score_kernels(num_q_heads: int, num_kv_heads: int, head_dim: int,
+                         seq_lens: Iterable[int], window: int, kernel_size: int) -> int:
+    """1 when snapkv_compress runs the vote statistics and the vote as one
+    kernel (snapkv_score_fused) for this shape on the current device, else 2."""
+    arr, vals = _lens(seq_lens)
+    n = ctypes.c_int32(0)
+    _check(load_library().snapkv_score_kernels(len(vals), num_q_heads, num_kv_heads, head_dim,
+                                               arr, window, kernel_size, ctypes.byref(n)))
+    return n.value
 
 
 def snapkv_stage_name(stage: int) -> Optional[str]:

@@ -22,7 +22,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = skv.header_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     assert "snapkv_compress_staged" in names
     assert "snapkv_compress_from_lse" in names
     for name in names:
@@ -172,3 +172,17 @@ def test_decode_validation_and_workspace(lib):
     st = lib.snapkv_decode_attention(1, 32, 8, 128, FAKE, FAKE, FAKE, 0, 128, lens, FAKE,
                                      FAKE, 1, None)
     assert st == 3
+
+
+def test_score_kernels_host_logic(lib):
+    # no device here: the fused score kernel needs the device's CU count, so
+    # the two-kernel path is reported; shape errors follow snapkv_compress
+    assert skv.snapkv_score_kernels(32, 8, 128, [16384], 32, 7) in (1, 2)
+    with pytest.raises(skv.SnapKVError):
+        skv.snapkv_score_kernels(32, 8, 96, [16384], 32, 7)
+    with pytest.raises(skv.SnapKVError):
+        skv.snapkv_score_kernels(32, 8, 128, [16384], 32, 4)
+    n = ctypes.c_int32(0)
+    lens = (ctypes.c_int32 * 1)(16384)
+    assert lib.snapkv_score_kernels(1, 32, 8, 128, lens, 32, 7, None) == skv.SNAPKV_ERR_INVALID_ARGUMENT
+    assert lib.snapkv_score_kernels(1, 32, 8, 128, lens, 32, 7, ctypes.byref(n)) == skv.SNAPKV_OK

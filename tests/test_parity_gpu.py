@@ -238,3 +238,20 @@ def test_caller_stream_is_used():
     for a, b in zip(out, ref):
         assert torch.equal(a, b)
     assert torch.equal(dec, dec_ref)
+
+
+@needs_gpu
+def test_score_kernel_count_by_shape():
+    # the 16K layer (8 heads x 32 chunks of 512 keys, one item per CU) runs
+    # statistics and vote as one kernel; longer prompts, head_dim 64, wide
+    # pooling and more items than CUs take the two kernels. The parity cases
+    # above cover both paths, and the score export (always two kernels)
+    # reproduces the fused path's selection exactly in full_check.
+    w = WORKLOADS["llama3_8b_16k"]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    fused = skv.snapkv_score_kernels(w.h_q, w.h_kv, w.head_dim, [16384], w.window, w.kernel)
+    assert fused == (1 if cus >= 256 else 2)
+    assert skv.snapkv_score_kernels(32, 8, 128, [32768], 32, 5) == 2
+    assert skv.snapkv_score_kernels(32, 8, 64, [16384], 32, 7) == 2
+    assert skv.snapkv_score_kernels(32, 8, 128, [16384], 32, 35) == 2
+    assert skv.snapkv_score_kernels(8, 8, 128, [1000], 32, 33) == 1
