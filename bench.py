@@ -3,8 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one snapkv_compress call (vote statistics, vote with pooling,
-selection, gather: four kernels, or three when statistics and vote run as
-the fused score kernel) on one layer of synthetic, seeded input
+selection, gather: four kernels, or fewer when statistics and vote run as
+the fused score kernel and the selection runs inside the gather) on one
+layer of synthetic, seeded input
 already resident in HBM. Inputs and outputs rotate over enough buffer sets to
 exceed the 256 MB Infinity Cache, so every step streams its K from HBM.
 Prints one JSON line: value = prompt tokens compressed per second per layer;
@@ -53,8 +54,9 @@ def stage_bytes(w, seq_lens):
     select reads the P pooled scores and writes the index list; gather moves
     the kept rows (the gather term of algorithmic_bytes)."""
     d, q_bytes = w.head_dim, w.h_q * w.window * w.head_dim * 2
+    gather = algorithmic_bytes(w, seq_lens)[1]
     out = {"snapkv_score_stats": 0, "snapkv_score_vote": 0, "snapkv_score_fused": 0,
-           "snapkv_select": 0, "snapkv_gather": algorithmic_bytes(w, seq_lens)[1]}
+           "snapkv_select": 0, "snapkv_gather": gather, "snapkv_gather_select": gather}
     for L in seq_lens:
         if L > w.budget:
             P = L - w.window
@@ -62,6 +64,7 @@ def stage_bytes(w, seq_lens):
             out["snapkv_score_fused"] += q_bytes + w.h_kv * L * d * 2
             out["snapkv_score_vote"] += q_bytes + w.h_kv * P * d * 2
             out["snapkv_select"] += w.h_kv * (P * 4 + w.budget * 4)
+            out["snapkv_gather_select"] += w.h_kv * P * 4  # the pooled scores, read once
     return out
 
 
@@ -221,13 +224,20 @@ def main():
         step(i, staged=True, events=evs[i])
     torch.cuda.synchronize()
     # with the fused score kernel, stage 0 is that kernel and stage 1 is empty
+    # and with the selection inside the gather, stage 3 is that kernel and
+    # stage 2 is empty
     fused = skv.snapkv_score_kernels(w.h_q, hkv, d, lens, w.window, w.kernel) == 1
+    sel_in_gather = skv.snapkv_gather_selects(w.h_q, hkv, d, lens, w.window, B) == 1
     stage_ms = {}
     for s_ in range(nst):
-        if fused and s_ == 1:
+        if (fused and s_ == 1) or (sel_in_gather and s_ == 2):
             continue
         vals = [row[2 * s_].elapsed_time(row[2 * s_ + 1]) for row in evs]
-        name = "snapkv_score_fused" if fused and s_ == 0 else skv.snapkv_stage_name(s_)
+        name = skv.snapkv_stage_name(s_)
+        if fused and s_ == 0:
+            name = "snapkv_score_fused"
+        if sel_in_gather and s_ == 3:
+            name = "snapkv_gather_select"
         stage_ms[name] = float(np.mean(vals))
 
     # the same compression when the caller's prefill attention hands over
@@ -366,6 +376,7 @@ def main():
                             "issued_2pass": round(2 * flops / (score_ms * 1e-3) / 1e12 /
                                                   BF16_PEAK_TFLOPS, 4)},
         "score_kernels": 1 if fused else 2,
+        "selection_in_gather": sel_in_gather,
         "stage_kernels": {k: {"ms": round(v, 5), "alg_bytes": sbytes[k],
                               "gbps": round(sbytes[k] / (v * 1e-3) / 1e9, 1)}
                           for k, v in stage_ms.items()},

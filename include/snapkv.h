@@ -140,9 +140,9 @@ int32_t snapkv_compress(int32_t batch, int32_t num_q_heads,
  * num_q_heads / num_kv_heads * window <= 256, kernel_size <= 33, and at most
  * one scoring work item of at most 512 keys per compute unit of the device,
  * so that every item can be resident at once), else 2 (snapkv_score_stats,
- * snapkv_score_vote). With the environment variable SNAPKV_NO_FUSED_SCORE
- * set to a non-empty value other than "0" when the library is first used,
- * it is always 2. snapkv_compress_from_lse always runs the vote kernel
+ * snapkv_score_vote). While the environment variable SNAPKV_NO_FUSED_SCORE
+ * is set to a non-empty value other than "0" (read at every call), it is
+ * always 2. snapkv_compress_from_lse always runs the vote kernel
  * alone. Writes *kernels and returns SNAPKV_OK, or an error status under the
  * shape rules of snapkv_compress (SNAPKV_ERR_INVALID_ARGUMENT also for a
  * NULL `kernels`).
@@ -153,6 +153,25 @@ int32_t snapkv_score_kernels(int32_t batch, int32_t num_q_heads,
                              int32_t kernel_size, int32_t* kernels);
 
 /*
+ * Whether snapkv_compress (and its _staged, _from_lse, _int4 and _fp8
+ * forms) runs the selection inside the gather on this shape, on the current
+ * device: 1 when each gather work item runs its head's selection itself
+ * (snapkv_gather_select: every prefix L - W is at most 32768 positions and
+ * the gather's work items, of 32 or 64 rows, fit the device one per compute
+ * unit), so the selection stage launches nothing; else 0 (snapkv_select,
+ * then snapkv_gather). Results are identical either way. While the
+ * environment variable SNAPKV_NO_FUSED_SELECT is set to a non-empty value
+ * other than "0" (read at every call), it is always 0. Writes *fused
+ * and returns SNAPKV_OK, or an error status under the shape rules of
+ * snapkv_compress (SNAPKV_ERR_INVALID_ARGUMENT also for a NULL `fused` or
+ * budget <= window).
+ */
+int32_t snapkv_gather_selects(int32_t batch, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim,
+                              const int32_t* seq_lens, int32_t window,
+                              int32_t budget, int32_t* fused);
+
+/*
  * snapkv_compress with optional per-stage timing: the same kernels (named by
  * snapkv_stage_name) and identical results. When stage_events is not NULL it
  * points to 2 * SNAPKV_NUM_STAGES caller-owned hipEvent_t: the dispatch of
@@ -160,7 +179,9 @@ int32_t snapkv_score_kernels(int32_t batch, int32_t num_q_heads,
  * stage_events[2*s+1] when it ends (a stage without work records both back
  * to back), so elapsed times are the kernels' own durations. With the fused
  * score kernel (snapkv_score_kernels = 1) stage 0 times that kernel and
- * stage 1 has no work.
+ * stage 1 has no work; with the selection inside the gather
+ * (snapkv_gather_selects = 1) stage 3 times snapkv_gather_select and stage 2
+ * has no work.
  * Errors as for snapkv_compress.
  */
 int32_t snapkv_compress_staged(int32_t batch, int32_t num_q_heads,

@@ -143,6 +143,23 @@ int32_t check_pool(int32_t kernel, int32_t pool_mode) {
   return SNAPKV_OK;
 }
 
+// Gather items and the selection's layout for a budget: half-size gather
+// items (D = 128) when full ones would leave CUs idle (fewer than about two
+// per CU over the call); prefixes longer than one selection workgroup holds
+// in registers are spread over workgroups of kSliceKeys positions.
+void gather_plan(const Plan& pl, int32_t budget, snapkv::PathParams* p) {
+  p->budget = budget;
+  const int full_items =
+      budget > 0 ? pl.batch * pl.hkv * ((budget + snapkv::kGatherRows - 1) / snapkv::kGatherRows)
+                 : 0;
+  p->gather_rows =
+      pl.d == 128 && full_items < 512 ? snapkv::kGatherRows / 2 : snapkv::kGatherRows;
+  p->n_gather_blocks = budget > 0 ? (budget + p->gather_rows - 1) / p->gather_rows : 0;
+  p->sel_slices = pl.p_max > snapkv::kSelectHeldKeys
+                      ? (pl.p_max + snapkv::kSliceKeys - 1) / snapkv::kSliceKeys
+                      : 0;
+}
+
 snapkv::PathParams path_params(const Plan& pl, const void* q, const void* k, const void* v,
                                void* ws, int32_t budget, int32_t kernel, int32_t pool_mode,
                                bool score_all) {
@@ -176,18 +193,7 @@ snapkv::PathParams path_params(const Plan& pl, const void* q, const void* k, con
   p.score_all = score_all ? 1 : 0;
   p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)pl.d));
   p.tab = pl.tab;
-  // half-size gather items (D = 128) when full ones would leave CUs idle:
-  // fewer than about two per CU over the call
-  const int full_items =
-      budget > 0 ? pl.batch * pl.hkv * ((budget + snapkv::kGatherRows - 1) / snapkv::kGatherRows)
-                 : 0;
-  p.gather_rows = pl.d == 128 && full_items < 512 ? snapkv::kGatherRows / 2 : snapkv::kGatherRows;
-  p.n_gather_blocks = budget > 0 ? (budget + p.gather_rows - 1) / p.gather_rows : 0;
-  // prefixes longer than one selection workgroup holds in registers are
-  // spread over workgroups of kSliceKeys positions
-  p.sel_slices = pl.p_max > snapkv::kSelectHeldKeys
-                     ? (pl.p_max + snapkv::kSliceKeys - 1) / snapkv::kSliceKeys
-                     : 0;
+  gather_plan(pl, budget, &p);
   return p;
 }
 
@@ -221,12 +227,17 @@ uint64_t next_epoch() {
 // Statistics and vote in one launch: head_dim 128, one row tile per wave, a
 // chunk's keys fit the LDS slots, the halo fits one block, and every item of
 // the grid can be resident at once (one workgroup per CU). SNAPKV_NO_FUSED_SCORE
-// set to a non-empty value other than "0" turns it off (two launches).
+// set to a non-empty value other than "0" at the call turns it off (two
+// launches).
+// Whether environment variable `name` is set to a non-empty value other
+// than "0" (read at every call, so a process can compare both paths).
+bool env_flag(const char* name) {
+  const char* e = std::getenv(name);
+  return e != nullptr && e[0] != '\0' && std::strcmp(e, "0") != 0;
+}
+
 bool use_fused_scoring(const Plan& pl, int32_t kernel) {
-  static const bool disabled = [] {
-    const char* e = std::getenv("SNAPKV_NO_FUSED_SCORE");
-    return e != nullptr && e[0] != '\0' && std::strcmp(e, "0") != 0;
-  }();
+  const bool disabled = env_flag("SNAPKV_NO_FUSED_SCORE");
   if (disabled || pl.d != 128 || pl.rows_pad > snapkv::kFusedMaxRows ||
       pl.chunk > snapkv::kFusedChunk || kernel / 2 > snapkv::kFusedMaxHalo ||
       pl.nchunk > snapkv::kThreads)
@@ -234,6 +245,27 @@ bool use_fused_scoring(const Plan& pl, int32_t kernel) {
   const int64_t items = (int64_t)pl.nchunk * pl.hkv * pl.batch;
   const int cus = device_cus();
   return cus > 0 && items <= cus;
+}
+
+// The selection inside the gather (snapkv_gather_select): every prefix fits
+// one workgroup's registers and the whole gather grid fits the device at
+// once, with 64-row items if 32-row ones would not. Sets p->gather_rows and
+// p->n_gather_blocks for the chosen items. SNAPKV_NO_FUSED_SELECT set to a
+// non-empty value other than "0" turns it off.
+bool use_select_in_gather(const Plan& pl, snapkv::PathParams* p) {
+  const bool disabled = env_flag("SNAPKV_NO_FUSED_SELECT");
+  if (disabled || p->sel_slices != 0 || p->budget <= 0) return false;
+  const int cus = device_cus();
+  if (cus <= 0) return false;
+  for (int rows : {p->gather_rows, snapkv::kGatherRows}) {
+    const int64_t blocks = (p->budget + rows - 1) / rows;
+    if (blocks * pl.hkv * pl.batch <= cus) {
+      p->gather_rows = rows;
+      p->n_gather_blocks = (int)blocks;
+      return true;
+    }
+  }
+  return false;
 }
 
 bool any_scored(const Plan& pl, int32_t budget, bool score_all) {
@@ -344,11 +376,22 @@ int32_t compress_impl(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const v
       if ((e = snapkv::launch_score_vote(p, d, s, events(1), ext_lse)) != hipSuccess)
         return hip_fail(e, "snapkv_score_vote launch");
     }
+  }
+  // the selection inside the gather (stage 2 then has no work), or its own
+  // kernel before the gather
+  const bool sel_in_gather = scored && use_select_in_gather(pl, &p);
+  if (scored && !sel_in_gather) {
     if ((e = snapkv::launch_select(p, s, events(2))) != hipSuccess)
       return hip_fail(e, "snapkv_select launch");
+  } else if (scored) {
+    skip(2);
   }
-  if ((e = snapkv::launch_gather(p, d, s, events(3), q4 ? q4->form : 0)) != hipSuccess)
+  if (sel_in_gather) {
+    if ((e = snapkv::launch_gather_select(p, d, s, events(3), q4 ? q4->form : 0)) != hipSuccess)
+      return hip_fail(e, "snapkv_gather_select launch");
+  } else if ((e = snapkv::launch_gather(p, d, s, events(3), q4 ? q4->form : 0)) != hipSuccess) {
     return hip_fail(e, "snapkv_gather launch");
+  }
   return SNAPKV_OK;
 }
 
@@ -433,6 +476,21 @@ int32_t snapkv_score_kernels(int32_t batch, int32_t num_q_heads, int32_t num_kv_
   st = check_pool(kernel_size, SNAPKV_POOL_AVG);
   if (st != SNAPKV_OK) return st;
   *kernels = use_fused_scoring(pl, kernel_size) ? 1 : 2;
+  return SNAPKV_OK;
+}
+
+int32_t snapkv_gather_selects(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, const int32_t* seq_lens, int32_t window,
+                              int32_t budget, int32_t* fused) {
+  if (fused == nullptr) return fail(SNAPKV_ERR_INVALID_ARGUMENT, "fused is NULL");
+  Plan pl;
+  const int32_t st = make_plan(batch, num_q_heads, num_kv_heads, head_dim, seq_lens, window, &pl);
+  if (st != SNAPKV_OK) return st;
+  if (budget <= window)
+    return fail(SNAPKV_ERR_INVALID_ARGUMENT, "budget must exceed window (it includes the window)");
+  snapkv::PathParams p{};
+  gather_plan(pl, budget, &p);
+  *fused = any_scored(pl, budget, false) && use_select_in_gather(pl, &p) ? 1 : 0;
   return SNAPKV_OK;
 }
 

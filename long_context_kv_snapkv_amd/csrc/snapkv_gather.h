@@ -34,16 +34,17 @@ struct GatherSmem {
 };
 
 // s.pos[t - lo] = the kept prefix position in slot t, for lo <= t < hi <= m,
-// of prompt b / head h with L > B.
+// of prompt b / head h with L > B, from the selection's count table `tab`
+// and threshold `thr` (global memory, or LDS when the selection ran in this
+// workgroup).
 __device__ __forceinline__ void locate_kept(const PathParams& p, GatherSmem& s, int b, int h,
-                                            int lo, int hi) {
+                                            int lo, int hi, const uint32_t* tab,
+                                            const uint32_t* thr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int P = p.tab.len[b] - p.window;
   const size_t head = (size_t)(b * p.hkv + h);
-  const uint32_t* tab = p.sel_table + head * (size_t)p.table_stride * 2;
-  const uint32_t* meta = p.sel_meta + head * 4;
-  const uint32_t tau = meta[0], need = meta[1];
-  const bool settled = meta[2] != 0u;
+  const uint32_t tau = thr[0], need = thr[1];
+  const bool settled = thr[2] != 0u;
   const int nseg = (P + kSegment - 1) / kSegment;
   if (tid < kGatherRows) s.pos[tid] = -1;
   if (tid == 0) s.nseg = 0u;
@@ -176,9 +177,11 @@ __device__ __forceinline__ uint2 quantize_piece_fp8(const u32x4& w, float& scale
 // Storage forms of the kept rows.
 constexpr int kStoreBf16 = 0, kStoreInt4 = 1, kStoreFp8 = 2;
 
+// The rows of the item's slots t0 .. t0 + RW - 1, once gs.pos holds the kept
+// positions of its slots below m (prompts with L > B).
 template <int D, int FORM, int RW>
-__device__ __forceinline__ void snapkv_gather_item(const PathParams& p, GatherSmem& gs, int b,
-                                                   int h, int rb) {
+__device__ __forceinline__ void gather_rows(const PathParams& p, const GatherSmem& gs, int b,
+                                            int h, int rb) {
   constexpr int PIECES = D / 8;
   constexpr int ROWS_PER_PASS = kThreads / PIECES;
   constexpr int PASSES = RW / ROWS_PER_PASS;  // RW: rows of this item
@@ -188,7 +191,6 @@ __device__ __forceinline__ void snapkv_gather_item(const PathParams& p, GatherSm
   const int B = p.budget;
   const bool whole = L <= B;
   const int P = L - p.window, m = B - p.window;
-  if (!whole && t0 < m) locate_kept(p, gs, b, h, t0, min(t0 + RW, m));
   const int tid = threadIdx.x;
   int32_t* idx = p.out_idx + (size_t)(b * p.hkv + h) * B;
   const size_t tstride = (size_t)p.hkv * D;
@@ -256,6 +258,20 @@ __device__ __forceinline__ void snapkv_gather_item(const PathParams& p, GatherSm
       if (piece == 0) idx[t] = jj[q];
     }
   }
+}
+
+template <int D, int FORM, int RW>
+__device__ __forceinline__ void snapkv_gather_item(const PathParams& p, GatherSmem& gs, int b,
+                                                   int h, int rb) {
+  const int t0 = rb * RW;
+  const int L = p.tab.len[b];
+  const int m = p.budget - p.window;
+  if (L > p.budget && t0 < m) {
+    const size_t head = (size_t)(b * p.hkv + h);
+    locate_kept(p, gs, b, h, t0, min(t0 + RW, m), p.sel_table + head * (size_t)p.table_stride * 2,
+                p.sel_meta + head * 4);
+  }
+  gather_rows<D, FORM, RW>(p, gs, b, h, rb);
 }
 
 }  // namespace snapkv

@@ -108,5 +108,8 @@ hipError_t launch_select(const PathParams& p, hipStream_t stream, StageEvents ev
 // out_kq/out_ks/out_vq/out_vs
 hipError_t launch_gather(const PathParams& p, int head_dim, hipStream_t stream,
                          StageEvents ev = {}, int form = 0);
+// the gather with the selection inside each item (sel_slices == 0 only)
+hipError_t launch_gather_select(const PathParams& p, int head_dim, hipStream_t stream,
+                                StageEvents ev = {}, int form = 0);
 
 }  // namespace snapkv

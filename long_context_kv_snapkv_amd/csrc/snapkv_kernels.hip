@@ -9,6 +9,9 @@
 //     or, for long prefixes, snapkv_select_digit<2>, snapkv_select_digit<3>
 //     and snapkv_select_count over (slice, head, prompt)
 //   snapkv_gather       (row block, head, prompt)  slots -> positions, rows
+//     or, when the prefixes fit one workgroup's registers and the grid fits
+//     the device at once, snapkv_gather_select (row block, head, prompt):
+//     each item runs its head's selection, then places and moves its rows
 //
 //   snapkv_clear_hist   (head, prompt)          zeroes the vote's digit
 //                                               histogram when the caller
@@ -110,6 +113,35 @@ __global__ void __launch_bounds__(kThreads) snapkv_gather(const PathParams p) {
   snapkv_gather_item<D, FORM, RW>(p, sm, blockIdx.z, blockIdx.y, blockIdx.x);
 }
 
+// The gather with the selection inside: every item whose slots hold kept
+// prefix positions runs its head's whole selection (the same integer
+// decisions as snapkv_select, so all items of a head agree) with the count
+// table in LDS, then places and moves its rows. Taken when the prefixes fit
+// one workgroup's registers and the grid fits the device at once, so the
+// repeated selections run side by side instead of after each other; it
+// saves the selection's launch and the table's round trip through memory.
+struct alignas(16) GatherSelectSmem {
+  SelectSmem sel;
+  GatherSmem gs;
+  uint32_t table[2 * (kSelectHeldKeys / kSegment)];
+  uint32_t thr[4];
+};
+
+template <int D, int FORM, int RW>
+__global__ void __launch_bounds__(kThreads) snapkv_gather_select(const PathParams p) {
+  __shared__ GatherSelectSmem sm;
+  const int b = blockIdx.z, h = blockIdx.y, rb = blockIdx.x;
+  const int t0 = rb * RW;
+  const int L = p.tab.len[b];
+  const int m = p.budget - p.window;
+  if (L > p.budget && t0 < m) {
+    select_dispatch(p, sm.sel, b, h, SelectOut{sm.table, sm.thr});
+    __syncthreads();
+    locate_kept(p, sm.gs, b, h, t0, min(t0 + RW, m), sm.table, sm.thr);
+  }
+  gather_rows<D, FORM, RW>(p, sm.gs, b, h, rb);
+}
+
 // Launch with one PathParams argument; with events, through the extended
 // launch that records them at the kernel's own start and end.
 template <typename K>
@@ -205,6 +237,28 @@ hipError_t launch_gather(const PathParams& p, int head_dim, hipStream_t stream,
       if (form == kStoreInt4) return launch(snapkv_gather<D, kStoreInt4, RW>, grid, stream, ev, p);
       if (form == kStoreFp8) return launch(snapkv_gather<D, kStoreFp8, RW>, grid, stream, ev, p);
       return launch(snapkv_gather<D, kStoreBf16, RW>, grid, stream, ev, p);
+    };
+    if constexpr (D == 128) {
+      if (p.gather_rows == kGatherRows / 2)
+        return go(std::integral_constant<int, kGatherRows / 2>());
+    }
+    return go(std::integral_constant<int, kGatherRows>());
+  });
+}
+
+hipError_t launch_gather_select(const PathParams& p, int head_dim, hipStream_t stream,
+                                StageEvents ev, int form) {
+  if (p.sel_slices != 0) return hipErrorInvalidValue;  // prefixes must fit the registers
+  return dispatch_dim(head_dim, [&](auto d) {
+    constexpr int D = decltype(d)::value;
+    const dim3 grid(p.n_gather_blocks, p.hkv, p.batch);
+    auto go = [&](auto rw) {
+      constexpr int RW = decltype(rw)::value;
+      if (form == kStoreInt4)
+        return launch(snapkv_gather_select<D, kStoreInt4, RW>, grid, stream, ev, p);
+      if (form == kStoreFp8)
+        return launch(snapkv_gather_select<D, kStoreFp8, RW>, grid, stream, ev, p);
+      return launch(snapkv_gather_select<D, kStoreBf16, RW>, grid, stream, ev, p);
     };
     if constexpr (D == 128) {
       if (p.gather_rows == kGatherRows / 2)

@@ -59,6 +59,15 @@ struct alignas(16) SelectSmem {
   uint32_t sh_bin, sh_need, sh_count;
 };
 
+// Where a selection puts its result: the global count table and threshold
+// (the gather reads them after the kernel boundary), or, for a selection
+// that runs inside a gather item, a count table in LDS and the threshold
+// in `thr` (tau, need, settled).
+struct SelectOut {
+  uint32_t* table;  // [nseg][2]
+  uint32_t* thr;    // [3]
+};
+
 // Keys of slabs slab0 .. slab0+NS-1 for this thread; 0 past P. Loads are
 // unconditional (clamped to the float4 group holding position P-1, inside
 // the row since rows are padded to 64 floats) so they all issue before the
@@ -135,7 +144,8 @@ __device__ __forceinline__ void find_bin(Counts&& counts, uint32_t need, Smem& s
 // Select for one (prompt, head) with L > budget. NS slabs per batch; with
 // RESIDENT the prefix fits in one batch and is loaded once.
 template <int NS, bool RESIDENT>
-__device__ __forceinline__ void select_head(const PathParams& p, SelectSmem& sm, int b, int h) {
+__device__ __forceinline__ void select_head(const PathParams& p, SelectSmem& sm, int b, int h,
+                                            const SelectOut& out) {
   const int L = p.tab.len[b];
   const int P = L - p.window;
   const uint32_t m = (uint32_t)(p.budget - p.window);  // 1 <= m < P
@@ -208,7 +218,7 @@ __device__ __forceinline__ void select_head(const PathParams& p, SelectSmem& sm,
   // before it) < need and lands at (above before it) + (equal before it).
   static_assert(kSegment == 4 * 64, "a segment is one wave's share of a slab");
   const int nseg = (P + kSegment - 1) / kSegment;
-  uint32_t* table = p.sel_table + head * (size_t)p.table_stride * 2;
+  uint32_t* table = out.table;
   for (int bt = 0; bt < nbatch; ++bt) {
     if (!RESIDENT) load_keys<NS>(key, src, P, bt * NS);
 #pragma unroll
@@ -229,10 +239,9 @@ __device__ __forceinline__ void select_head(const PathParams& p, SelectSmem& sm,
     }
   }
   if (tid == 0) {
-    uint32_t* meta = p.sel_meta + head * 4;
-    meta[0] = tau;
-    meta[1] = need;
-    meta[2] = settled ? 1u : 0u;
+    out.thr[0] = tau;
+    out.thr[1] = need;
+    out.thr[2] = settled ? 1u : 0u;
   }
 }
 
@@ -383,22 +392,29 @@ __device__ __forceinline__ void select_count_slice(const PathParams& p, SliceSme
 
 // Selection of one (prompt, head): the smallest register batch that holds
 // the prefix, or batches of kMaxSlabsHeld slabs re-read for longer prefixes.
-__device__ __forceinline__ void snapkv_select_item(const PathParams& p, SelectSmem& sm, int b,
-                                                   int h) {
+__device__ __forceinline__ void select_dispatch(const PathParams& p, SelectSmem& sm, int b, int h,
+                                                const SelectOut& out) {
   const int P = p.tab.len[b] - p.window;
   const int slabs = (P + kSlab - 1) / kSlab;
   if (slabs <= 1)
-    select_head<1, true>(p, sm, b, h);
+    select_head<1, true>(p, sm, b, h, out);
   else if (slabs <= 2)
-    select_head<2, true>(p, sm, b, h);
+    select_head<2, true>(p, sm, b, h, out);
   else if (slabs <= 4)
-    select_head<4, true>(p, sm, b, h);
+    select_head<4, true>(p, sm, b, h, out);
   else if (slabs <= 8)
-    select_head<8, true>(p, sm, b, h);
+    select_head<8, true>(p, sm, b, h, out);
   else if (slabs <= kMaxSlabsHeld)
-    select_head<kMaxSlabsHeld, true>(p, sm, b, h);
+    select_head<kMaxSlabsHeld, true>(p, sm, b, h, out);
   else
-    select_head<kMaxSlabsHeld, false>(p, sm, b, h);
+    select_head<kMaxSlabsHeld, false>(p, sm, b, h, out);
+}
+
+__device__ __forceinline__ void snapkv_select_item(const PathParams& p, SelectSmem& sm, int b,
+                                                   int h) {
+  const size_t head = (size_t)(b * p.hkv + h);
+  select_dispatch(p, sm, b, h,
+                  SelectOut{p.sel_table + head * (size_t)p.table_stride * 2, p.sel_meta + head * 4});
 }
 
 }  // namespace snapkv

@@ -98,6 +98,8 @@ def load_library():
     lib.snapkv_last_error.restype = ctypes.c_char_p
     lib.snapkv_score_kernels.argtypes = [_i32, _i32, _i32, _i32, _pi32, _i32, _i32, _pi32]
     lib.snapkv_score_kernels.restype = _i32
+    lib.snapkv_gather_selects.argtypes = [_i32, _i32, _i32, _i32, _pi32, _i32, _i32, _pi32]
+    lib.snapkv_gather_selects.restype = _i32
     lib.snapkv_stage_name.argtypes = [_i32]
     lib.snapkv_stage_name.restype = ctypes.c_char_p
     _lib = lib
@@ -441,6 +443,17 @@ def snapkv_score_kernels(num_q_heads: int, num_kv_heads: int, head_dim: int,
     n = ctypes.c_int32(0)
     _check(load_library().snapkv_score_kernels(len(vals), num_q_heads, num_kv_heads, head_dim,
                                                arr, window, kernel_size, ctypes.byref(n)))
+    return n.value
+
+
+def snapkv_gather_selects(num_q_heads: int, num_kv_heads: int, head_dim: int,
+                          seq_lens: Iterable[int], window: int, budget: int) -> int:
+    """1 when snapkv_compress runs the selection inside the gather
+    (snapkv_gather_select) for this shape on the current device, else 0."""
+    arr, vals = _lens(seq_lens)
+    n = ctypes.c_int32(0)
+    _check(load_library().snapkv_gather_selects(len(vals), num_q_heads, num_kv_heads, head_dim,
+                                                arr, window, budget, ctypes.byref(n)))
     return n.value
 
 

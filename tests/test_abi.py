@@ -22,7 +22,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = skv.header_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     assert "snapkv_compress_staged" in names
     assert "snapkv_compress_from_lse" in names
     for name in names:
@@ -186,3 +186,13 @@ def test_score_kernels_host_logic(lib):
     lens = (ctypes.c_int32 * 1)(16384)
     assert lib.snapkv_score_kernels(1, 32, 8, 128, lens, 32, 7, None) == skv.SNAPKV_ERR_INVALID_ARGUMENT
     assert lib.snapkv_score_kernels(1, 32, 8, 128, lens, 32, 7, ctypes.byref(n)) == skv.SNAPKV_OK
+
+
+def test_gather_selects_host_logic(lib):
+    # no device here: the selection inside the gather needs the device's CU
+    # count, so the separate selection kernel is reported off the GPU
+    assert skv.snapkv_gather_selects(32, 8, 128, [16384], 32, 1024) in (0, 1)
+    with pytest.raises(skv.SnapKVError):
+        skv.snapkv_gather_selects(32, 8, 128, [16384], 32, 32)
+    lens = (ctypes.c_int32 * 1)(16384)
+    assert lib.snapkv_gather_selects(1, 32, 8, 128, lens, 32, 1024, None) == skv.SNAPKV_ERR_INVALID_ARGUMENT

@@ -255,3 +255,41 @@ def test_score_kernel_count_by_shape():
     assert skv.snapkv_score_kernels(32, 8, 64, [16384], 32, 7) == 2
     assert skv.snapkv_score_kernels(32, 8, 128, [16384], 32, 35) == 2
     assert skv.snapkv_score_kernels(8, 8, 128, [1000], 32, 33) == 1
+
+
+@needs_gpu
+def test_selection_inside_gather_by_shape():
+    w = WORKLOADS["llama3_8b_16k"]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    got = skv.snapkv_gather_selects(w.h_q, w.h_kv, w.head_dim, [16384], w.window, w.budget)
+    assert got == (1 if cus >= 256 else 0)
+    # 32K layer: 64-row items (32 per head) fit the CUs
+    assert skv.snapkv_gather_selects(32, 8, 128, [32768], 32, 2048) == (1 if cus >= 256 else 0)
+    # a prefix past the register-resident length takes the sliced selection
+    assert skv.snapkv_gather_selects(64, 8, 128, [131072], 64, 1024) == 0
+    # too many gather items for the device at once
+    assert skv.snapkv_gather_selects(32, 8, 128, [20000] * 8, 64, 4096) == 0
+
+
+@needs_gpu
+@pytest.mark.parametrize("name", ["llama3_8b_16k", "llama3_8b_32k_x32"])
+def test_fused_and_separate_paths_give_identical_bits(name, monkeypatch):
+    # the same call with the fused score kernel and the selection inside the
+    # gather, and with both switched off: every output bit equal
+    w = WORKLOADS[name]
+    x = make_layer(w)
+    print(f"[parity] fused vs separate {name}", flush=True)
+    dev = upload(x)
+    q, k, v = dev
+    lens = x.seq_lens.tolist()
+    a = skv.snapkv_compress(q, k, v, lens, w.window, w.kernel, w.pool, w.budget)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("SNAPKV_NO_FUSED_SCORE", "1")
+    monkeypatch.setenv("SNAPKV_NO_FUSED_SELECT", "1")
+    assert skv.snapkv_score_kernels(w.h_q, w.h_kv, w.head_dim, lens, w.window, w.kernel) == 2
+    assert skv.snapkv_gather_selects(w.h_q, w.h_kv, w.head_dim, lens, w.window, w.budget) == 0
+    b = skv.snapkv_compress(q, k, v, lens, w.window, w.kernel, w.pool, w.budget)
+    torch.cuda.synchronize()
+    for ta, tb in zip(a, b):
+        assert torch.equal(ta.view(torch.int16) if ta.dtype == torch.bfloat16 else ta,
+                           tb.view(torch.int16) if tb.dtype == torch.bfloat16 else tb)
