@@ -185,6 +185,7 @@ struct KeyStream {
   size_t tstride;
   int key0, kend;
   bool reverse = false;  // visit the tiles last to first
+  bool deep = false;     // prefetch() requests the first two tiles (run_resident)
 
   __device__ __forceinline__ int ntiles() const { return (kend - key0 + T::KEYS - 1) / T::KEYS; }
   // first key of the i-th tile visited
@@ -196,6 +197,10 @@ struct KeyStream {
   // first tile arrives sooner if it does not compete with deeper prefetch.
   __device__ __forceinline__ void prefetch() {
     load_key_tile<D>(ra, kb, tstride, tile_key(0), kend, threadIdx.x);
+    if (deep) {
+      asm volatile("" ::: "memory");  // tile 0's loads stay older than tile 1's
+      load_key_tile<D>(rb, kb, tstride, tile_key(min(1, ntiles() - 1)), kend, threadIdx.x);
+    }
   }
 
   template <typename Compute>
@@ -244,8 +249,10 @@ __device__ __forceinline__ void KeyStream<D>::run_resident(unsigned char (*slots
   const int ntiles = this->ntiles();
   auto start = [&](int i) { return tile_key(min(i, ntiles - 1)); };
   store_key_tile<D>(ra, slots[0], tid);
-  load_key_tile<D>(rb, kb, tstride, start(1), kend, tid);
-  asm volatile("" ::: "memory");  // keep tile 1's loads older than tile 2's
+  if (!deep) {
+    load_key_tile<D>(rb, kb, tstride, start(1), kend, tid);
+    asm volatile("" ::: "memory");  // keep tile 1's loads older than tile 2's
+  }
   load_key_tile<D>(ra, kb, tstride, start(2), kend, tid);
   lds_barrier();
   for (int i = 0;; i += 2) {

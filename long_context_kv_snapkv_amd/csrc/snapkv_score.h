@@ -124,7 +124,7 @@ struct KeyGroup {
 // the fused kernel). The query fragments are left in `qf`. With COHERENT the
 // statistics and the histogram clearing are written with device-coherent
 // stores (another workgroup of the same kernel reads them).
-template <int D, int RTW, bool COHERENT, typename Run>
+template <int D, int RTW, bool COHERENT, bool DEEP = false, typename Run>
 __device__ __forceinline__ void score_stats_body(const PathParams& p, unsigned char* qbuf,
                                                  float2 (*wstats)[kMaxRowTilesPerWave * 32],
                                                  bf16x8 (&qf)[RTW][D / 16], Run&& run, int b,
@@ -140,7 +140,7 @@ __device__ __forceinline__ void score_stats_body(const PathParams& p, unsigned c
   // so the same XCD) starts with the tiles this item read last, which are
   // then the most likely to still be in that XCD's L2
   KeyStream<D> ks{{}, {}, p.k + ((size_t)p.tab.off[b] * p.hkv + h) * D, (size_t)p.hkv * D,
-                  key0, kend, true};
+                  key0, kend, true, DEEP};
   stage_query_frags<D, RTW>(qf, p.q + (size_t)(b * p.hq + h * p.group) * p.window * D, p.rows,
                             p.rows_pad, role.wr, role.nwr, role.my_nrt, qbuf,
                             [&] { ks.prefetch(); });
@@ -606,7 +606,7 @@ __device__ __forceinline__ void snapkv_score_fused_item(const PathParams& p, Fus
   // which the stream fills last
   bf16x8 qf[RTW][D / 16];
   int nst = 0;  // tiles of the chunk, stored to the slots last tile first
-  score_stats_body<D, RTW, true>(
+  score_stats_body<D, RTW, true, true>(
       p, sm.k[kFusedTiles - 1], sm.u.wstats, qf,
       [&](KeyStream<D>& ks, auto&& compute) {
         nst = ks.ntiles();
