@@ -56,12 +56,13 @@ def stage_bytes(w, seq_lens):
     d, q_bytes = w.head_dim, w.h_q * w.window * w.head_dim * 2
     gather = algorithmic_bytes(w, seq_lens)[1]
     out = {"snapkv_score_stats": 0, "snapkv_score_vote": 0, "snapkv_score_fused": 0,
-           "snapkv_select": 0, "snapkv_gather": gather, "snapkv_gather_select": gather}
+           "snapkv_score_fused_stream": 0, "snapkv_select": 0, "snapkv_gather": gather, "snapkv_gather_select": gather}
     for L in seq_lens:
         if L > w.budget:
             P = L - w.window
             out["snapkv_score_stats"] += q_bytes + w.h_kv * L * d * 2
             out["snapkv_score_fused"] += q_bytes + w.h_kv * L * d * 2
+            out["snapkv_score_fused_stream"] += q_bytes + w.h_kv * L * d * 2
             out["snapkv_score_vote"] += q_bytes + w.h_kv * P * d * 2
             out["snapkv_select"] += w.h_kv * (P * 4 + w.budget * 4)
             out["snapkv_gather_select"] += w.h_kv * P * 4  # the pooled scores, read once
@@ -223,10 +224,12 @@ def main():
     for i in range(nprof):
         step(i, staged=True, events=evs[i])
     torch.cuda.synchronize()
-    # with the fused score kernel, stage 0 is that kernel and stage 1 is empty
+    # with a fused score kernel, stage 0 is that kernel and stage 1 is empty
     # and with the selection inside the gather, stage 3 is that kernel and
     # stage 2 is empty
-    fused = skv.snapkv_score_kernels(w.h_q, hkv, d, lens, w.window, w.kernel) == 1
+    score_kernels = skv.snapkv_score_kernels(w.h_q, hkv, d, lens, w.window, w.kernel)
+    fused = score_kernels != 2
+    fused_name = "snapkv_score_fused" if score_kernels == 1 else "snapkv_score_fused_stream"
     sel_in_gather = skv.snapkv_gather_selects(w.h_q, hkv, d, lens, w.window, B) == 1
     stage_ms = {}
     for s_ in range(nst):
@@ -235,7 +238,7 @@ def main():
         vals = [row[2 * s_].elapsed_time(row[2 * s_ + 1]) for row in evs]
         name = skv.snapkv_stage_name(s_)
         if fused and s_ == 0:
-            name = "snapkv_score_fused"
+            name = fused_name
         if sel_in_gather and s_ == 3:
             name = "snapkv_gather_select"
         stage_ms[name] = float(np.mean(vals))
@@ -348,7 +351,7 @@ def main():
     score_b, gather_b = algorithmic_bytes(w, lens)
     total_b = score_b + gather_b
     flops = score_flops(w, lens)
-    score_ms = (stage_ms["snapkv_score_fused"] if fused else
+    score_ms = (stage_ms[fused_name] if fused else
                 stage_ms["snapkv_score_stats"] + stage_ms["snapkv_score_vote"])
     tokens = sum(lens)
     value = tokens / (ms_step * 1e-3)
@@ -376,6 +379,7 @@ def main():
                             "issued_2pass": round(2 * flops / (score_ms * 1e-3) / 1e12 /
                                                   BF16_PEAK_TFLOPS, 4)},
         "score_kernels": 1 if fused else 2,
+        "score_kernel": fused_name if fused else "snapkv_score_stats + snapkv_score_vote",
         "selection_in_gather": sel_in_gather,
         "stage_kernels": {k: {"ms": round(v, 5), "alg_bytes": sbytes[k],
                               "gbps": round(sbytes[k] / (v * 1e-3) / 1e9, 1)}

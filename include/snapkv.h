@@ -97,10 +97,10 @@ int32_t snapkv_workspace_size(int32_t batch, int32_t num_q_heads,
 /*
  * Compress one layer's prompt KV cache (steps 1-4 above) with
  * SNAPKV_NUM_STAGES consecutive kernels on `stream`: vote statistics, vote
- * with pooling, selection, gather. When snapkv_score_kernels reports 1 for
- * the shape, the first two run as one kernel (snapkv_score_fused) whose work
- * items exchange the row statistics through the workspace and wait, bounded,
- * for each other; its results are bit-identical to the two kernels'.
+ * with pooling, selection, gather. When snapkv_score_kernels reports 1 or 3
+ * for the shape, the first two run as one kernel whose work items exchange
+ * the row statistics through the workspace and wait, bounded, for each
+ * other; its results are bit-identical to the two kernels'.
  *
  *   window       W >= 1, the observation window (pages: 16-64)
  *   kernel_size  odd, 1 <= kernel_size <= SNAPKV_MAX_KERNEL; 1 = no pooling
@@ -134,18 +134,24 @@ int32_t snapkv_compress(int32_t batch, int32_t num_q_heads,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * How many kernels snapkv_compress (and its _staged, _int4 and _fp8 forms)
- * runs for the vote statistics and the vote on this shape, on the current
- * device: 1 when they run as one kernel, snapkv_score_fused (head_dim 128,
- * num_q_heads / num_kv_heads * window <= 256, kernel_size <= 33, and at most
- * one scoring work item of at most 512 keys per compute unit of the device,
- * so that every item can be resident at once), else 2 (snapkv_score_stats,
- * snapkv_score_vote). While the environment variable SNAPKV_NO_FUSED_SCORE
- * is set to a non-empty value other than "0" (read at every call), it is
- * always 2. snapkv_compress_from_lse always runs the vote kernel
- * alone. Writes *kernels and returns SNAPKV_OK, or an error status under the
- * shape rules of snapkv_compress (SNAPKV_ERR_INVALID_ARGUMENT also for a
- * NULL `kernels`).
+ * How snapkv_compress (and its _staged, _int4 and _fp8 forms) runs the vote
+ * statistics and the vote on this shape, on the current device:
+ *   1  one kernel, snapkv_score_fused, whose work items keep their keys in
+ *      LDS between the two (head_dim 128, num_q_heads / num_kv_heads * window
+ *      <= 256, at most 512 keys per work item, kernel_size <= 33);
+ *   3  one kernel, snapkv_score_fused_stream, whose work items read their
+ *      keys twice (other shapes);
+ *   2  two kernels, snapkv_score_stats and snapkv_score_vote.
+ * The one-kernel forms are taken when the call has at most one scoring work
+ * item per compute unit of the device, so that every item can be resident
+ * at once: their items exchange the row statistics through the workspace
+ * and wait, bounded, for each other. All three give identical bits. While
+ * the environment variable SNAPKV_NO_FUSED_SCORE is set to a non-empty value
+ * other than "0" (read at every call), it is always 2.
+ * snapkv_compress_from_lse always runs the vote kernel alone. Writes
+ * *kernels and returns SNAPKV_OK, or an error status under the shape rules
+ * of snapkv_compress (SNAPKV_ERR_INVALID_ARGUMENT also for a NULL
+ * `kernels`).
  */
 int32_t snapkv_score_kernels(int32_t batch, int32_t num_q_heads,
                              int32_t num_kv_heads, int32_t head_dim,
@@ -177,9 +183,9 @@ int32_t snapkv_gather_selects(int32_t batch, int32_t num_q_heads,
  * points to 2 * SNAPKV_NUM_STAGES caller-owned hipEvent_t: the dispatch of
  * stage s records stage_events[2*s] when its kernel starts and
  * stage_events[2*s+1] when it ends (a stage without work records both back
- * to back), so elapsed times are the kernels' own durations. With the fused
- * score kernel (snapkv_score_kernels = 1) stage 0 times that kernel and
- * stage 1 has no work; with the selection inside the gather
+ * to back), so elapsed times are the kernels' own durations. With a fused
+ * score kernel (snapkv_score_kernels = 1 or 3) stage 0 times that kernel
+ * and stage 1 has no work; with the selection inside the gather
  * (snapkv_gather_selects = 1) stage 3 times snapkv_gather_select and stage 2
  * has no work.
  * Errors as for snapkv_compress.

@@ -224,11 +224,8 @@ uint64_t next_epoch() {
   return counter.fetch_add(2, std::memory_order_relaxed);
 }
 
-// Statistics and vote in one launch: head_dim 128, one row tile per wave, a
-// chunk's keys fit the LDS slots, the halo fits one block, and every item of
-// the grid can be resident at once (one workgroup per CU). SNAPKV_NO_FUSED_SCORE
-// set to a non-empty value other than "0" at the call turns it off (two
-// launches).
+// SNAPKV_NO_FUSED_SCORE set to a non-empty value other than "0" at the call
+// turns the one-launch forms off (two kernels).
 // Whether environment variable `name` is set to a non-empty value other
 // than "0" (read at every call, so a process can compare both paths).
 bool env_flag(const char* name) {
@@ -236,15 +233,23 @@ bool env_flag(const char* name) {
   return e != nullptr && e[0] != '\0' && std::strcmp(e, "0") != 0;
 }
 
-bool use_fused_scoring(const Plan& pl, int32_t kernel) {
-  const bool disabled = env_flag("SNAPKV_NO_FUSED_SCORE");
-  if (disabled || pl.d != 128 || pl.rows_pad > snapkv::kFusedMaxRows ||
-      pl.chunk > snapkv::kFusedChunk || kernel / 2 > snapkv::kFusedMaxHalo ||
-      pl.nchunk > snapkv::kThreads)
-    return false;
+// How the statistics and the vote run: two kernels, or one launch whose
+// items exchange the statistics (every item of the grid resident at once,
+// one workgroup per CU), keeping a chunk's keys in LDS when they fit
+// (head_dim 128, one row tile per wave, at most 512 keys, a halo of at most
+// 16 keys) and streaming them twice otherwise.
+enum class Scoring { kTwoKernels, kFusedResident, kFusedStream };
+
+Scoring scoring_plan(const Plan& pl, int32_t kernel) {
+  if (env_flag("SNAPKV_NO_FUSED_SCORE") || pl.nchunk > snapkv::kThreads)
+    return Scoring::kTwoKernels;
   const int64_t items = (int64_t)pl.nchunk * pl.hkv * pl.batch;
   const int cus = device_cus();
-  return cus > 0 && items <= cus;
+  if (cus <= 0 || items > cus) return Scoring::kTwoKernels;
+  if (pl.d == 128 && pl.rows_pad <= snapkv::kFusedMaxRows && pl.chunk <= snapkv::kFusedChunk &&
+      kernel / 2 <= snapkv::kFusedMaxHalo)
+    return Scoring::kFusedResident;
+  return Scoring::kFusedStream;
 }
 
 // The selection inside the gather (snapkv_gather_select): every prefix fits
@@ -359,11 +364,16 @@ int32_t compress_impl(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const v
     skip(1);
     skip(2);
   } else {
-    if (!ext_lse && use_fused_scoring(pl, kernel)) {
+    const Scoring sc = ext_lse ? Scoring::kTwoKernels : scoring_plan(pl, kernel);
+    if (sc != Scoring::kTwoKernels) {
       // statistics and vote in one launch (stage 0); stage 1 is empty
       p.epoch = next_epoch();
-      if ((e = snapkv::launch_score_fused(p, d, s, events(0))) != hipSuccess)
-        return hip_fail(e, "snapkv_score_fused launch");
+      if (sc == Scoring::kFusedResident) {
+        if ((e = snapkv::launch_score_fused(p, d, s, events(0))) != hipSuccess)
+          return hip_fail(e, "snapkv_score_fused launch");
+      } else if ((e = snapkv::launch_score_fused_stream(p, d, s, events(0))) != hipSuccess) {
+        return hip_fail(e, "snapkv_score_fused_stream launch");
+      }
       skip(1);
     } else {
       if (ext_lse) {
@@ -475,7 +485,8 @@ int32_t snapkv_score_kernels(int32_t batch, int32_t num_q_heads, int32_t num_kv_
   if (st != SNAPKV_OK) return st;
   st = check_pool(kernel_size, SNAPKV_POOL_AVG);
   if (st != SNAPKV_OK) return st;
-  *kernels = use_fused_scoring(pl, kernel_size) ? 1 : 2;
+  const Scoring sc = scoring_plan(pl, kernel_size);
+  *kernels = sc == Scoring::kTwoKernels ? 2 : (sc == Scoring::kFusedResident ? 1 : 3);
   return SNAPKV_OK;
 }
 

@@ -102,6 +102,10 @@ hipError_t launch_clear_hist(const PathParams& p, hipStream_t stream, StageEvent
 // every item of the grid must be able to be resident at once)
 hipError_t launch_score_fused(const PathParams& p, int head_dim, hipStream_t stream,
                               StageEvents ev = {});
+// statistics and vote in one launch with the keys streamed twice (any
+// head_dim and row tiling; every item of the grid resident at once)
+hipError_t launch_score_fused_stream(const PathParams& p, int head_dim, hipStream_t stream,
+                                     StageEvents ev = {});
 // one workgroup per head, or (sel_slices > 0) three sliced kernels
 hipError_t launch_select(const PathParams& p, hipStream_t stream, StageEvents ev = {});
 // form 0: bf16 rows; 1: 4-bit, 2: FP8 E4M3 codes with per-row scales, through

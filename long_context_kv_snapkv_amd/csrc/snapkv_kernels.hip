@@ -2,8 +2,9 @@
 //
 //   snapkv_score_stats  (chunk, head, prompt)   per-row softmax statistics
 //   snapkv_score_vote   (chunk, head, prompt)   window vote + pooling
-//     or, when every item fits the device at once with its keys in LDS,
-//   snapkv_score_fused  (chunk, head, prompt)   both in one launch
+//     or, when every item fits the device at once, both in one launch:
+//   snapkv_score_fused  (chunk, head, prompt)   keys kept in LDS between them
+//   snapkv_score_fused_stream (chunk, head, prompt)  keys streamed twice
 //   snapkv_select       (head, prompt)          threshold of the top-(B - W)
 //                                               and its count table
 //     or, for long prefixes, snapkv_select_digit<2>, snapkv_select_digit<3>
@@ -18,8 +19,9 @@
 //                                               supplies the normalisers
 //
 // A compress call runs the four in stream order; the kernel boundaries carry
-// every hand-off between stages, except inside snapkv_score_fused, whose
-// items wait (bounded) for per-item flags of the other items of their head.
+// every hand-off between stages, except inside the fused score kernels,
+// whose items wait (bounded) for per-item flags of the other items of their
+// head.
 // The score export runs stats and vote only, with the caller's buffer as the
 // pooled rows.
 #include <hip/hip_ext.h>
@@ -73,6 +75,16 @@ __global__ void __launch_bounds__(kThreads) snapkv_score_fused(const PathParams 
   const int b = blockIdx.z, h = blockIdx.y, c = blockIdx.x;
   if (!is_scored(p, b) || c >= num_chunks(p, b)) return;
   snapkv_score_fused_item<D>(p, sm, b, h, c);
+}
+
+// Statistics and vote in one launch with the keys streamed twice (every item
+// resident at once; the host checks the grid against the device's CUs).
+template <int D, int RTW>
+__global__ void __launch_bounds__(kThreads) snapkv_score_fused_stream(const PathParams p) {
+  __shared__ FusedStreamSmem<D, RTW> sm;
+  const int b = blockIdx.z, h = blockIdx.y, c = blockIdx.x;
+  if (!is_scored(p, b) || c >= num_chunks(p, b)) return;
+  snapkv_score_fused_stream_item<D, RTW>(p, sm, b, h, c);
 }
 
 // With the caller's row normalisers there is no statistics pass to clear the
@@ -208,6 +220,15 @@ hipError_t launch_score_fused(const PathParams& p, int head_dim, hipStream_t str
       p.kernel / 2 > kFusedMaxHalo || p.nchunk > kThreads)
     return hipErrorInvalidValue;
   return launch(snapkv_score_fused<128>, dim3(p.nchunk, p.hkv, p.batch), stream, ev, p);
+}
+
+hipError_t launch_score_fused_stream(const PathParams& p, int head_dim, hipStream_t stream,
+                                     StageEvents ev) {
+  if (p.nchunk > kThreads) return hipErrorInvalidValue;
+  return dispatch_dim_rtw(head_dim, row_tiles_per_wave(p), [&](auto d, auto rtw) {
+    return launch(snapkv_score_fused_stream<decltype(d)::value, decltype(rtw)::value>,
+                  dim3(p.nchunk, p.hkv, p.batch), stream, ev, p);
+  });
 }
 
 hipError_t launch_clear_hist(const PathParams& p, hipStream_t stream, StageEvents ev) {

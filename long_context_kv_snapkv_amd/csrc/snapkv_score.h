@@ -354,7 +354,19 @@ __device__ __forceinline__ void snapkv_score_stats_item(const PathParams& p, Sta
 // for its own inputs while the rest is still in flight.
 constexpr int kPartBatch = 8;
 
-template <int D, int RTW, bool EXT_LSE>
+// Per-chunk statistics of one row, with a device-coherent load when another
+// workgroup of the same kernel wrote them (COHERENT).
+template <bool COHERENT>
+__device__ __forceinline__ float2 load_part(const float2* a) {
+  if constexpr (COHERENT)
+    return __builtin_bit_cast(
+        float2, __hip_atomic_load(const_cast<uint64_t*>(reinterpret_cast<const uint64_t*>(a)),
+                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  else
+    return *a;
+}
+
+template <int D, int RTW, bool EXT_LSE, bool COHERENT = false>
 __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, VoteSmem<D>& sm,
                                                        int b, int h, int c) {
   const int L = p.tab.len[b];
@@ -385,7 +397,7 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
   } else {
 #pragma unroll
     for (int u = 0; u < kPartBatch; ++u)
-      pe[u] = part[(size_t)min(sub + u * tpr, nch - 1) * p.rows_pad + row_c];
+      pe[u] = load_part<COHERENT>(&part[(size_t)min(sub + u * tpr, nch - 1) * p.rows_pad + row_c]);
   }
   asm volatile("" ::: "memory");  // these loads stay older than the rest
 
@@ -414,7 +426,7 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
         if (sub + u * tpr < nch) s += pe[u].y * exp2_fast(pe[u].x - m);
     }
     for (int cc = sub + kPartBatch * tpr; cc < nch; cc += tpr) {  // long prompts only
-      const float2 e = part[(size_t)cc * p.rows_pad + row_c];
+      const float2 e = load_part<COHERENT>(&part[(size_t)cc * p.rows_pad + row_c]);
       lse_merge(m, s, e.x, e.y);
     }
     float2* scratch = reinterpret_cast<float2*>(&sm.vred[0][0][0]);  // kThreads float2
@@ -587,6 +599,34 @@ struct alignas(16) FusedSmem {
 static_assert(sizeof(FusedSmem<128>) <= 160 * 1024, "fused item LDS");
 static_assert(kTopBins * 4 <= KTile<128>::BYTES, "histogram in a key slot");
 
+// Publish this item's row statistics (device-coherent stores already
+// issued by every thread): each thread's stores complete, then the flag.
+__device__ __forceinline__ void publish_item(const PathParams& p, uint64_t* flags, int c) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&flags[c], p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until the flags of chunks 0 .. nch-1 of a head carry this call's
+// epoch, at most kSpinLimit polls each; returns non-zero (in every thread)
+// if any poll gave up. Ends with a workgroup barrier.
+__device__ __forceinline__ int wait_head(const PathParams& p, const uint64_t* flags, int nch) {
+  int timed_out = 0;
+  if ((int)threadIdx.x < nch) {
+    int spins = 0;
+    uint64_t* f = const_cast<uint64_t*>(&flags[threadIdx.x]);
+    while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != p.epoch) {
+      if (++spins > kSpinLimit) {
+        timed_out = 1;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  return __syncthreads_or(timed_out);
+}
+
 template <int D>
 __device__ __forceinline__ void snapkv_score_fused_item(const PathParams& p, FusedSmem<D>& sm,
                                                         int b, int h, int c) {
@@ -613,11 +653,8 @@ __device__ __forceinline__ void snapkv_score_fused_item(const PathParams& p, Fus
         ks.run_resident(sm.k, compute);
       },
       b, h, c);
-  // publish: this thread's coherent stores are complete, then every thread's
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
   uint64_t* flags = p.flags + head * p.nchunk;
-  if (tid == 0) __hip_atomic_store(&flags[c], p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  publish_item(p, flags, c);
   if (key0 >= P) return;  // a chunk of window keys only: nothing to vote
 
   // phase 2: the voted positions [key0, kend) and their pooling halo
@@ -637,18 +674,7 @@ __device__ __forceinline__ void snapkv_score_fused_item(const PathParams& p, Fus
     }
   }
   // wait for the statistics of every chunk of this head (bounded)
-  int timed_out = 0;
-  if (tid < nch) {
-    int spins = 0;
-    while (__hip_atomic_load(&flags[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != p.epoch) {
-      if (++spins > kSpinLimit) {
-        timed_out = 1;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-  }
-  timed_out = __syncthreads_or(timed_out);
+  const int timed_out = wait_head(p, flags, nch);
 
   // lse of every row, exactly as the vote item merges it, from coherent loads
   const float2* part = p.part + head * p.nchunk * p.rows_pad;
@@ -658,15 +684,10 @@ __device__ __forceinline__ void snapkv_score_fused_item(const PathParams& p, Fus
   const int row = tid % span, sub = tid / span;
   const bool row_ok = row < p.rows;
   const int row_c = min(row, p.rows - 1);
-  auto load_part = [&](int cc) {
-    uint64_t* a = const_cast<uint64_t*>(
-        reinterpret_cast<const uint64_t*>(&part[(size_t)cc * p.rows_pad + row_c]));
-    return __builtin_bit_cast(float2,
-                              __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  };
+  auto part_of = [&](int cc) { return load_part<true>(&part[(size_t)cc * p.rows_pad + row_c]); };
   float2 pe[kPartBatch];
 #pragma unroll
-  for (int u = 0; u < kPartBatch; ++u) pe[u] = load_part(min(sub + u * tpr, nch - 1));
+  for (int u = 0; u < kPartBatch; ++u) pe[u] = part_of(min(sub + u * tpr, nch - 1));
   {
     float m = -kInf, s = 0.f;
 #pragma unroll
@@ -678,7 +699,7 @@ __device__ __forceinline__ void snapkv_score_fused_item(const PathParams& p, Fus
         if (sub + u * tpr < nch) s += pe[u].y * exp2_fast(pe[u].x - m);
     }
     for (int cc = sub + kPartBatch * tpr; cc < nch; cc += tpr) {
-      const float2 e = load_part(cc);
+      const float2 e = part_of(cc);
       lse_merge(m, s, e.x, e.y);
     }
     sm.u.scratch[tid] = row_ok ? make_float2(m, s) : make_float2(-kInf, 0.f);
@@ -790,6 +811,48 @@ __device__ __forceinline__ void snapkv_score_fused_item(const PathParams& p, Fus
   for (int i = tid; i < kTopBins; i += kThreads) {
     const uint32_t n = top[i];
     if (n != 0u) atomicAdd(&gtop[i], n);
+  }
+}
+
+// Statistics and vote in one launch for chunks too long to keep in LDS: the
+// statistics item as in snapkv_score_stats (statistics written with
+// device-coherent stores), the same publication and bounded wait as the
+// fused item, then the vote item as in snapkv_score_vote with coherent loads
+// of the statistics; its keys stream through the ring again (this CU read
+// them moments before, so mostly from the caches). The same code in the same
+// order as the two kernels, so identical bits. On timeout the item's pooled
+// scores are NaN.
+template <int D, int RTW>
+union FusedStreamSmem {
+  StatsSmem<D> st;
+  VoteSmem<D> vt;
+};
+
+template <int D, int RTW>
+__device__ __forceinline__ void snapkv_score_fused_stream_item(const PathParams& p,
+                                                               FusedStreamSmem<D, RTW>& sm,
+                                                               int b, int h, int c) {
+  const int L = p.tab.len[b];
+  const int P = L - p.window;
+  const int nch = (L + p.chunk - 1) / p.chunk;
+  const size_t head = (size_t)(b * p.hkv + h);
+  {
+    bf16x8 qf[RTW][D / 16];
+    score_stats_body<D, RTW, true>(
+        p, sm.st.ring[1], sm.st.wstats, qf,
+        [&](KeyStream<D>& ks, auto&& compute) { ks.run(sm.st.ring, compute, [](int) {}); }, b,
+        h, c);
+  }
+  uint64_t* flags = p.flags + head * p.nchunk;
+  publish_item(p, flags, c);
+  if (c * p.chunk >= P) return;  // a chunk of window keys only: nothing to vote
+  const int timed_out = wait_head(p, flags, nch);  // its barrier also frees the LDS
+  snapkv_score_vote_item<D, RTW, false, true>(p, sm.vt, b, h, c);
+  if (timed_out) {
+    __syncthreads();
+    float* pooled = p.pooled + head * p.pooled_stride;
+    const int key0 = c * p.chunk, kend = min(key0 + p.chunk, P);
+    for (int j = key0 + (int)threadIdx.x; j < kend; j += kThreads) pooled[j] = __builtin_nanf("");
   }
 }
 

@@ -249,12 +249,18 @@ def test_score_kernel_count_by_shape():
     # reproduces the fused path's selection exactly in full_check.
     w = WORKLOADS["llama3_8b_16k"]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
+    one = cus >= 256  # every workload below has at most 256 scoring items
     fused = skv.snapkv_score_kernels(w.h_q, w.h_kv, w.head_dim, [16384], w.window, w.kernel)
-    assert fused == (1 if cus >= 256 else 2)
-    assert skv.snapkv_score_kernels(32, 8, 128, [32768], 32, 5) == 2
-    assert skv.snapkv_score_kernels(32, 8, 64, [16384], 32, 7) == 2
-    assert skv.snapkv_score_kernels(32, 8, 128, [16384], 32, 35) == 2
+    assert fused == (1 if one else 2)
+    # chunks too long for LDS, head_dim 64, or a wide pooling halo: keys
+    # streamed twice in one launch
+    assert skv.snapkv_score_kernels(32, 8, 128, [32768], 32, 5) == (3 if one else 2)
+    assert skv.snapkv_score_kernels(64, 8, 128, [131072], 64, 7) == (3 if one else 2)
+    assert skv.snapkv_score_kernels(32, 8, 64, [16384], 32, 7) == (3 if one else 2)
+    assert skv.snapkv_score_kernels(32, 8, 128, [16384], 32, 35) == (3 if one else 2)
     assert skv.snapkv_score_kernels(8, 8, 128, [1000], 32, 33) == 1
+    # more scoring items than compute units: two kernels
+    assert skv.snapkv_score_kernels(32, 8, 128, [20000] * 8, 64, 13) == 2
 
 
 @needs_gpu
@@ -272,7 +278,7 @@ def test_selection_inside_gather_by_shape():
 
 
 @needs_gpu
-@pytest.mark.parametrize("name", ["llama3_8b_16k", "llama3_8b_32k_x32"])
+@pytest.mark.parametrize("name", ["llama3_8b_16k", "llama3_8b_32k_x32", "tiny_mha_1k"])
 def test_fused_and_separate_paths_give_identical_bits(name, monkeypatch):
     # the same call with the fused score kernel and the selection inside the
     # gather, and with both switched off: every output bit equal
