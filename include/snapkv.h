@@ -148,6 +148,15 @@ int32_t snapkv_compress(int32_t batch, int32_t num_q_heads,
  * and wait, bounded, for each other. All three give identical bits. While
  * the environment variable SNAPKV_NO_FUSED_SCORE is set to a non-empty value
  * other than "0" (read at every call), it is always 2.
+ * Concurrency: the one-kernel forms count on having the device's compute
+ * units to themselves while they run. A process that runs compressions on
+ * several streams of one device at once sets SNAPKV_NO_FUSED_SCORE, or
+ * SNAPKV_COOPERATIVE (read at every call), which launches them as
+ * cooperative kernels so that the runtime guarantees every work item a
+ * compute unit (about 19 us more per call on MI355X). Otherwise concurrent
+ * fused calls can each wait on items the other's hold CUs from; the wait is
+ * bounded (about a second), after which the items give up and their pooled
+ * scores, and so the selection, are not meaningful (NaN scores).
  * snapkv_compress_from_lse always runs the vote kernel alone. Writes
  * *kernels and returns SNAPKV_OK, or an error status under the shape rules
  * of snapkv_compress (SNAPKV_ERR_INVALID_ARGUMENT also for a NULL

@@ -225,7 +225,9 @@ uint64_t next_epoch() {
 }
 
 // SNAPKV_NO_FUSED_SCORE set to a non-empty value other than "0" at the call
-// turns the one-launch forms off (two kernels).
+// turns the one-launch forms off (two kernels); SNAPKV_COOPERATIVE launches
+// them as cooperative kernels (the runtime then guarantees co-residency even
+// with other work on the device, at a cost of about 19 us per call).
 // Whether environment variable `name` is set to a non-empty value other
 // than "0" (read at every call, so a process can compare both paths).
 bool env_flag(const char* name) {
@@ -368,6 +370,7 @@ int32_t compress_impl(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const v
     if (sc != Scoring::kTwoKernels) {
       // statistics and vote in one launch (stage 0); stage 1 is empty
       p.epoch = next_epoch();
+      p.cooperative = env_flag("SNAPKV_COOPERATIVE") ? 1 : 0;
       if (sc == Scoring::kFusedResident) {
         if ((e = snapkv::launch_score_fused(p, d, s, events(0))) != hipSuccess)
           return hip_fail(e, "snapkv_score_fused launch");

@@ -154,7 +154,7 @@ __device__ __forceinline__ void store_key_tile(const typename KTile<D>::Regs& r,
 
 // MFMA fragments of key block kb (32 keys) of a staged tile: lane holds key
 // kb*32 + (lane & 31), D elements 16*s + 8*(lane >> 5) .. +7 for k-step s.
-template <int D>
+template <int D, bool FENCE = true>
 __device__ __forceinline__ void read_key_frags(bf16x8 (&kf)[D / 16], const unsigned char* tile,
                                                int kb, int lane) {
   using T = KTile<D>;
@@ -163,8 +163,9 @@ __device__ __forceinline__ void read_key_frags(bf16x8 (&kf)[D / 16], const unsig
   for (int s = 0; s < D / 16; ++s)
     kf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(row + s * 32));
   // issue every fragment read before the MFMAs that consume them, instead of
-  // one LDS round trip per MFMA
-  __builtin_amdgcn_sched_barrier(0);
+  // one LDS round trip per MFMA (without FENCE the compiler schedules them
+  // freely, e.g. under the previous block's exp2 work)
+  if constexpr (FENCE) __builtin_amdgcn_sched_barrier(0);
 }
 
 // Stream the keys [key0, kend) of one head through two LDS tile buffers,

@@ -64,6 +64,7 @@ struct PathParams {
   uint64_t* flags;      // [batch, Hkv, nchunk] fused score kernel: `epoch` once an item's
                         // row statistics are published
   uint64_t epoch;       // this call's publication mark (unique per call in the process)
+  int32_t cooperative;  // launch the fused score kernels as cooperative launches
   int32_t batch, hq, hkv, window, group;
   int32_t rows, rows_pad;  // G*W and its round-up to 32
   int32_t nwr;             // waves that split the row tiles (power of two)

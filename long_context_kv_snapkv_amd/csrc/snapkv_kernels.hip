@@ -158,7 +158,19 @@ __global__ void __launch_bounds__(kThreads) snapkv_gather_select(const PathParam
 // launch that records them at the kernel's own start and end.
 template <typename K>
 hipError_t launch(K kernel, dim3 grid, hipStream_t stream, const StageEvents& ev,
-                  const PathParams& p) {
+                  const PathParams& p, bool cooperative = false) {
+  if (cooperative) {
+    // the runtime makes every workgroup resident at once (or fails the
+    // launch); events, if any, are recorded on the stream around it
+    void* args[] = {const_cast<PathParams*>(&p)};
+    hipError_t e = hipSuccess;
+    if (ev.start != nullptr) e = hipEventRecord(ev.start, stream);
+    if (e == hipSuccess)
+      e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kernel), grid, dim3(kThreads),
+                                     args, 0, stream);
+    if (e == hipSuccess && ev.stop != nullptr) e = hipEventRecord(ev.stop, stream);
+    return e;
+  }
   if (ev.start != nullptr || ev.stop != nullptr) {
     void* args[] = {const_cast<PathParams*>(&p)};
     return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, dim3(kThreads), args,
@@ -219,7 +231,8 @@ hipError_t launch_score_fused(const PathParams& p, int head_dim, hipStream_t str
   if (head_dim != 128 || p.rows_pad > kFusedMaxRows || p.chunk > kFusedChunk ||
       p.kernel / 2 > kFusedMaxHalo || p.nchunk > kThreads)
     return hipErrorInvalidValue;
-  return launch(snapkv_score_fused<128>, dim3(p.nchunk, p.hkv, p.batch), stream, ev, p);
+  return launch(snapkv_score_fused<128>, dim3(p.nchunk, p.hkv, p.batch), stream, ev, p,
+                p.cooperative != 0);
 }
 
 hipError_t launch_score_fused_stream(const PathParams& p, int head_dim, hipStream_t stream,
@@ -227,7 +240,7 @@ hipError_t launch_score_fused_stream(const PathParams& p, int head_dim, hipStrea
   if (p.nchunk > kThreads) return hipErrorInvalidValue;
   return dispatch_dim_rtw(head_dim, row_tiles_per_wave(p), [&](auto d, auto rtw) {
     return launch(snapkv_score_fused_stream<decltype(d)::value, decltype(rtw)::value>,
-                  dim3(p.nchunk, p.hkv, p.batch), stream, ev, p);
+                  dim3(p.nchunk, p.hkv, p.batch), stream, ev, p, p.cooperative != 0);
   });
 }
 

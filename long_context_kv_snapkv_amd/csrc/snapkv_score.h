@@ -723,7 +723,7 @@ __device__ __forceinline__ void snapkv_score_fused_item(const PathParams& p, Fus
   // chain, then the column sum over this wave's rows in colsum's order
   auto chain = [&](const unsigned char* tile, int kb) {
     bf16x8 kf[D / 16];
-    read_key_frags<D>(kf, tile, kb, lane);
+    read_key_frags<D, false>(kf, tile, kb, lane);
     f32x16 acc = {};
 #pragma unroll
     for (int s = 0; s < D / 16; ++s)

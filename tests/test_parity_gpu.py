@@ -299,3 +299,21 @@ def test_fused_and_separate_paths_give_identical_bits(name, monkeypatch):
     for ta, tb in zip(a, b):
         assert torch.equal(ta.view(torch.int16) if ta.dtype == torch.bfloat16 else ta,
                            tb.view(torch.int16) if tb.dtype == torch.bfloat16 else tb)
+
+
+@needs_gpu
+def test_cooperative_launch_gives_identical_bits(monkeypatch):
+    # the fused score kernels launched cooperatively (runtime-guaranteed
+    # co-residency) give the same bits as the ordinary launch
+    w = WORKLOADS["llama3_8b_16k"]
+    x = make_layer(w)
+    q, k, v = upload(x)
+    lens = x.seq_lens.tolist()
+    print("[parity] cooperative launch 16k", flush=True)
+    a = skv.snapkv_compress(q, k, v, lens, w.window, w.kernel, w.pool, w.budget)
+    monkeypatch.setenv("SNAPKV_COOPERATIVE", "1")
+    b = skv.snapkv_compress(q, k, v, lens, w.window, w.kernel, w.pool, w.budget)
+    torch.cuda.synchronize()
+    for ta, tb in zip(a, b):
+        assert torch.equal(ta.view(torch.int16) if ta.dtype == torch.bfloat16 else ta,
+                           tb.view(torch.int16) if tb.dtype == torch.bfloat16 else tb)
