@@ -155,8 +155,10 @@ int32_t snapkv_compress(int32_t batch, int32_t num_q_heads,
  * cooperative kernels so that the runtime guarantees every work item a
  * compute unit (about 19 us more per call on MI355X). Otherwise concurrent
  * fused calls can each wait on items the other's hold CUs from; the wait is
- * bounded (about a second), after which the items give up and their pooled
- * scores, and so the selection, are not meaningful (NaN scores).
+ * bounded (about a second; SNAPKV_SPIN_LIMIT, read at every call, lowers
+ * the number of polls, e.g. to exercise this path), after which the items
+ * give up and their pooled scores, and so the selection, are not meaningful
+ * (NaN scores); every kernel still exits and the outputs keep their layout.
  * snapkv_compress_from_lse always runs the vote kernel alone. Writes
  * *kernels and returns SNAPKV_OK, or an error status under the shape rules
  * of snapkv_compress (SNAPKV_ERR_INVALID_ARGUMENT also for a NULL

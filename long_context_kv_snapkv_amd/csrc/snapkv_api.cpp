@@ -259,6 +259,18 @@ Scoring scoring_plan(const Plan& pl, int32_t kernel) {
 // once, with 64-row items if 32-row ones would not. Sets p->gather_rows and
 // p->n_gather_blocks for the chosen items. SNAPKV_NO_FUSED_SELECT set to a
 // non-empty value other than "0" turns it off.
+// Polls before a fused score item stops waiting for its head: kSpinLimit
+// (about a second), or SNAPKV_SPIN_LIMIT (read at every call, 0 .. the
+// default) to exercise the give-up path.
+int32_t spin_limit() {
+  const char* e = std::getenv("SNAPKV_SPIN_LIMIT");
+  if (e == nullptr || e[0] == '\0') return snapkv::kSpinLimit;
+  char* end = nullptr;
+  const long v = std::strtol(e, &end, 10);
+  if (end == e || v < 0 || v > snapkv::kSpinLimit) return snapkv::kSpinLimit;
+  return (int32_t)v;
+}
+
 bool use_select_in_gather(const Plan& pl, snapkv::PathParams* p) {
   const bool disabled = env_flag("SNAPKV_NO_FUSED_SELECT");
   if (disabled || p->sel_slices != 0 || p->budget <= 0) return false;
@@ -371,6 +383,7 @@ int32_t compress_impl(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const v
       // statistics and vote in one launch (stage 0); stage 1 is empty
       p.epoch = next_epoch();
       p.cooperative = env_flag("SNAPKV_COOPERATIVE") ? 1 : 0;
+      p.spin_limit = spin_limit();
       if (sc == Scoring::kFusedResident) {
         if ((e = snapkv::launch_score_fused(p, d, s, events(0))) != hipSuccess)
           return hip_fail(e, "snapkv_score_fused launch");

@@ -28,6 +28,7 @@ constexpr int kFusedTiles = 4;                  // resident 128-key tiles per it
 constexpr int kFusedChunk = kFusedTiles * 128;  // keys per item (at most)
 constexpr int kFusedMaxHalo = 16;               // kernel / 2 (at most)
 constexpr int kFusedMaxRows = 256;              // G * W rounded up to 32 (one row tile per wave)
+constexpr int kSpinLimit = 1 << 20;             // polls of a fused item's bounded wait (~1 s)
 
 // Per-prompt table passed by value in the kernel arguments.
 struct PromptTable {
@@ -65,6 +66,7 @@ struct PathParams {
                         // row statistics are published
   uint64_t epoch;       // this call's publication mark (unique per call in the process)
   int32_t cooperative;  // launch the fused score kernels as cooperative launches
+  int32_t spin_limit;   // polls before a fused score item stops waiting (kSpinLimit)
   int32_t batch, hq, hkv, window, group;
   int32_t rows, rows_pad;  // G*W and its round-up to 32
   int32_t nwr;             // waves that split the row tiles (power of two)

@@ -580,10 +580,10 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
 // it waits), then pools and counts as the vote item does. The arithmetic of
 // every vote, normaliser and pooled value is the vote item's, in the same
 // order, so both paths give identical bits. Every wait is bounded: after
-// kSpinLimit polls the item gives up and writes NaN scores, which the
-// selection and any comparison expose; the host only takes this path when
-// the grid fits the device one workgroup per CU, so the bound is not reached.
-constexpr int kSpinLimit = 1 << 20;
+// p.spin_limit polls (kSpinLimit unless the caller lowers it) the item gives
+// up and writes NaN scores, which the selection and any comparison expose;
+// the host only takes this path when the grid fits the device one workgroup
+// per CU, so the default bound is not reached.
 
 template <int D>
 struct alignas(16) FusedSmem {
@@ -609,7 +609,7 @@ __device__ __forceinline__ void publish_item(const PathParams& p, uint64_t* flag
 }
 
 // Wait until the flags of chunks 0 .. nch-1 of a head carry this call's
-// epoch, at most kSpinLimit polls each; returns non-zero (in every thread)
+// epoch, at most p.spin_limit polls each; returns non-zero (in every thread)
 // if any poll gave up. Ends with a workgroup barrier.
 __device__ __forceinline__ int wait_head(const PathParams& p, const uint64_t* flags, int nch) {
   int timed_out = 0;
@@ -617,7 +617,7 @@ __device__ __forceinline__ int wait_head(const PathParams& p, const uint64_t* fl
     int spins = 0;
     uint64_t* f = const_cast<uint64_t*>(&flags[threadIdx.x]);
     while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != p.epoch) {
-      if (++spins > kSpinLimit) {
+      if (++spins > p.spin_limit) {
         timed_out = 1;
         break;
       }

@@ -317,3 +317,25 @@ def test_cooperative_launch_gives_identical_bits(monkeypatch):
     for ta, tb in zip(a, b):
         assert torch.equal(ta.view(torch.int16) if ta.dtype == torch.bfloat16 else ta,
                            tb.view(torch.int16) if tb.dtype == torch.bfloat16 else tb)
+
+
+@needs_gpu
+@pytest.mark.parametrize("name", ["llama3_8b_16k", "llama3_8b_32k_x32"])
+def test_fused_wait_gives_up_and_the_call_completes(name, monkeypatch):
+    # the fused score kernels' wait for the other items of a head is
+    # bounded; with the bound forced to zero polls from the host, items that
+    # find a flag unset give up (their pooled scores become NaN) and every
+    # kernel still exits: the call completes and its output keeps its
+    # structure (ascending kept positions, window last, bit-copied rows)
+    from parity import bits_from_device, check_structure_and_gather
+    w = WORKLOADS[name]
+    x = make_layer(w)
+    q, k, v = upload(x)
+    lens = x.seq_lens.tolist()
+    assert skv.snapkv_score_kernels(w.h_q, w.h_kv, w.head_dim, lens, w.window, w.kernel) != 2
+    monkeypatch.setenv("SNAPKV_SPIN_LIMIT", "0")
+    print(f"[parity] forced give-up {name}", flush=True)
+    ok, ov, oi = skv.snapkv_compress(q, k, v, lens, w.window, w.kernel, w.pool, w.budget)
+    torch.cuda.synchronize()
+    res = dict(out_k=bits_from_device(ok), out_v=bits_from_device(ov), out_idx=oi.cpu().numpy())
+    check_structure_and_gather(res, x, w.window, w.budget)
