@@ -155,11 +155,15 @@ __device__ __forceinline__ void select_head(const PathParams& p, SelectSmem& sm,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nbatch = RESIDENT ? 1 : (P + NS * kSlab - 1) / (NS * kSlab);
 
+  // digit 1: the histogram the vote kernel accumulated. Its row is loaded
+  // before the keys, so the first search waits for it alone while the keys
+  // are still in flight.
+  const u32x4 top4 = *reinterpret_cast<const u32x4*>(top + 256 * wave + 4 * lane);
+  asm volatile("" ::: "memory");  // the histogram loads stay older than the keys'
   uint32_t key[NS][4];
   if (RESIDENT) load_keys<NS>(key, src, P, 0);
   clear_hist(sm.rep[0], 0);
-  // digit 1: the histogram the vote kernel accumulated
-  find_bin([&] { return *reinterpret_cast<const u32x4*>(top + 256 * wave + 4 * lane); }, m, sm);
+  find_bin([&] { return top4; }, m, sm);
   uint32_t prefix = sm.sh_bin << kTopShift;  // resolved high bits of tau
   uint32_t need = sm.sh_need;
   bool settled = need == sm.sh_count;  // the whole threshold bin is kept
