@@ -339,3 +339,26 @@ def test_fused_wait_gives_up_and_the_call_completes(name, monkeypatch):
     torch.cuda.synchronize()
     res = dict(out_k=bits_from_device(ok), out_v=bits_from_device(ov), out_idx=oi.cpu().numpy())
     check_structure_and_gather(res, x, w.window, w.budget)
+
+
+@needs_gpu
+@pytest.mark.parametrize("case", [EDGE[12], EDGE[9], EDGE[8], EDGE[13], EDGE[16], EDGE[10]],
+                         ids=["ragged_mixed", "rows512", "d64_rows72", "one_token", "batch2_w64",
+                              "wide_kernel"])
+def test_fused_paths_identical_on_edge_shapes(case, monkeypatch):
+    # small ragged, row-padded, head_dim-64 and one-token batches take the
+    # fused forms (one-launch scoring, selection inside the gather) by
+    # default; with both switched off every output bit is the same
+    lens, hq, hkv, d, window, kernel, pool, budget = case
+    x = make_custom(lens, hq, hkv, d, window, seed=sum(lens) % 89)
+    q, k, v = upload(x)
+    print(f"[parity] fused vs separate {lens} hq={hq} hkv={hkv} d={d}", flush=True)
+    a = skv.snapkv_compress(q, k, v, lens, window, kernel, pool, budget)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("SNAPKV_NO_FUSED_SCORE", "1")
+    monkeypatch.setenv("SNAPKV_NO_FUSED_SELECT", "1")
+    b = skv.snapkv_compress(q, k, v, lens, window, kernel, pool, budget)
+    torch.cuda.synchronize()
+    for ta, tb in zip(a, b):
+        assert torch.equal(ta.view(torch.int16) if ta.dtype == torch.bfloat16 else ta,
+                           tb.view(torch.int16) if tb.dtype == torch.bfloat16 else tb)
