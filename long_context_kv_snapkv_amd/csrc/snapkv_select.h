@@ -162,7 +162,10 @@ __device__ __forceinline__ void select_head(const PathParams& p, SelectSmem& sm,
   asm volatile("" ::: "memory");  // the histogram loads stay older than the keys'
   uint32_t key[NS][4];
   if (RESIDENT) load_keys<NS>(key, src, P, 0);
+  // both digit histograms are cleared now, while the keys are in flight
+  // (the search's barriers order the clearing before the counting)
   clear_hist(sm.rep[0], 0);
+  clear_hist(sm.rep[1], 0);
   find_bin([&] { return top4; }, m, sm);
   uint32_t prefix = sm.sh_bin << kTopShift;  // resolved high bits of tau
   uint32_t need = sm.sh_need;
@@ -179,8 +182,7 @@ __device__ __forceinline__ void select_head(const PathParams& p, SelectSmem& sm,
     }
   };
   // one more digit of `bits` bits below the resolved prefix, counted into
-  // histogram buffer `buf`; the threshold bin is found, then the other
-  // buffer is cleared for the next digit
+  // histogram buffer `buf` (cleared at the start); the threshold bin is found
   auto digit = [&](int buf, int bits) {
     const int shift = low - bits;
     const uint32_t dmask = (1u << bits) - 1u;
@@ -201,8 +203,6 @@ __device__ __forceinline__ void select_head(const PathParams& p, SelectSmem& sm,
           return acc;
         },
         need, sm);
-    clear_hist(sm.rep[buf ^ 1], 0);  // the other buffer, for the next digit
-    lds_barrier();
     prefix |= sm.sh_bin << shift;
     need = sm.sh_need;
     settled = need == sm.sh_count;
@@ -234,7 +234,7 @@ __device__ __forceinline__ void select_head(const PathParams& p, SelectSmem& sm,
         c += (settled ? u >= tau : u > tau) ? 1u : 0u;
         c += (!settled && u == tau) ? 0x10000u : 0u;
       }
-      const uint32_t tot = wave_total(wave_incl_scan(c));
+      const uint32_t tot = wave_sum(c);
       const int g = (bt * NS + s) * kWaves + wave;  // segment index in the prefix
       if (lane == 0 && g < nseg) {
         table[2 * g] = tot & 0xFFFFu;
