@@ -232,7 +232,11 @@ int32_t snapkv_compress_staged(int32_t batch, int32_t num_q_heads,
  * the workspace and errors as for snapkv_compress; SNAPKV_ERR_INVALID_ARGUMENT
  * also for a null or misaligned window_lse. It runs the kernels of
  * snapkv_compress with the first (the statistics pass) replaced by a small
- * one that clears the vote's histogram in the workspace.
+ * one that clears the vote's histogram in the workspace, or, when every vote
+ * work item can be resident at once (as for the one-kernel scoring forms of
+ * snapkv_score_kernels, with the same concurrency rules and switches), by
+ * nothing: the vote kernel's first item per head clears the histograms and
+ * the others check its flag (bounded wait) before adding to them.
  */
 int32_t snapkv_compress_from_lse(int32_t batch, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim,

@@ -287,6 +287,15 @@ bool use_select_in_gather(const Plan& pl, snapkv::PathParams* p) {
   return false;
 }
 
+// Every scoring item of the call fits the device one workgroup per CU (the
+// vote kernel with the caller's normalisers then clears the histograms
+// itself); SNAPKV_NO_FUSED_SCORE turns that off too.
+bool votes_resident(const Plan& pl) {
+  if (env_flag("SNAPKV_NO_FUSED_SCORE") || pl.nchunk > snapkv::kThreads) return false;
+  const int cus = device_cus();
+  return cus > 0 && (int64_t)pl.nchunk * pl.hkv * pl.batch <= cus;
+}
+
 bool any_scored(const Plan& pl, int32_t budget, bool score_all) {
   for (int b = 0; b < pl.batch; ++b) {
     const int L = pl.tab.len[b];
@@ -392,14 +401,21 @@ int32_t compress_impl(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const v
       }
       skip(1);
     } else {
-      if (ext_lse) {
-        // the caller's normalisers replace the statistics pass, which would
-        // also have cleared the vote's digit histogram
+      // the caller's normalisers replace the statistics pass, which would
+      // also have cleared the vote's digit histograms: a clearing kernel, or
+      // (every vote item resident at once) the vote kernel's item 0 per head
+      const bool zero_first = ext_lse && votes_resident(pl);
+      if (zero_first) {
+        p.epoch = next_epoch();
+        p.spin_limit = spin_limit();
+        skip(0);
+      } else if (ext_lse) {
         if ((e = snapkv::launch_clear_hist(p, s, events(0))) != hipSuccess)
           return hip_fail(e, "snapkv_clear_hist launch");
-      } else if ((e = snapkv::launch_score_stats(p, d, s, events(0))) != hipSuccess)
+      } else if ((e = snapkv::launch_score_stats(p, d, s, events(0))) != hipSuccess) {
         return hip_fail(e, "snapkv_score_stats launch");
-      if ((e = snapkv::launch_score_vote(p, d, s, events(1), ext_lse)) != hipSuccess)
+      }
+      if ((e = snapkv::launch_score_vote(p, d, s, events(1), ext_lse, zero_first)) != hipSuccess)
         return hip_fail(e, "snapkv_score_vote launch");
     }
   }

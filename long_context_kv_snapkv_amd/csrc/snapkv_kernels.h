@@ -95,9 +95,11 @@ struct StageEvents {
 // Stage kernels: grids of work items.
 hipError_t launch_score_stats(const PathParams& p, int head_dim, hipStream_t stream,
                               StageEvents ev = {});
-// with ext_lse the row normalisers come from PathParams::window_lse
+// with ext_lse the row normalisers come from PathParams::window_lse; with
+// zero_first (ext_lse only, every item resident at once) the kernel also
+// clears the selection histograms that snapkv_clear_hist would
 hipError_t launch_score_vote(const PathParams& p, int head_dim, hipStream_t stream,
-                             StageEvents ev = {}, bool ext_lse = false);
+                             StageEvents ev = {}, bool ext_lse = false, bool zero_first = false);
 // zeroes top_hist of the scored heads (stands in for the statistics pass,
 // which does it otherwise)
 hipError_t launch_clear_hist(const PathParams& p, hipStream_t stream, StageEvents ev = {});

@@ -52,7 +52,7 @@ __global__ void __launch_bounds__(kThreads) snapkv_score_stats(const PathParams 
   snapkv_score_stats_item<D, RTW>(p, sm, b, h, c);
 }
 
-template <int D, int RTW, bool EXT_LSE>
+template <int D, int RTW, bool EXT_LSE, bool ZERO_FIRST = false>
 __global__ void __launch_bounds__(kThreads) snapkv_score_vote(const PathParams p) {
   __shared__ VoteSmem<D> sm;
   const int b = blockIdx.z, h = blockIdx.y, c = blockIdx.x;
@@ -64,7 +64,7 @@ __global__ void __launch_bounds__(kThreads) snapkv_score_vote(const PathParams p
     for (int j = max(P, 0) + (int)threadIdx.x; j < p.pooled_stride; j += kThreads) row[j] = 0.f;
   }
   if (!is_scored(p, b) || c >= nvote) return;
-  snapkv_score_vote_item<D, RTW, EXT_LSE>(p, sm, b, h, c);
+  snapkv_score_vote_item<D, RTW, EXT_LSE, false, ZERO_FIRST>(p, sm, b, h, c);
 }
 
 // Statistics and vote in one launch (every item resident at once; the host
@@ -215,9 +215,13 @@ hipError_t launch_score_stats(const PathParams& p, int head_dim, hipStream_t str
 }
 
 hipError_t launch_score_vote(const PathParams& p, int head_dim, hipStream_t stream,
-                             StageEvents ev, bool ext_lse) {
+                             StageEvents ev, bool ext_lse, bool zero_first) {
+  if (zero_first && (!ext_lse || p.nchunk > kThreads)) return hipErrorInvalidValue;
   return dispatch_dim_rtw(head_dim, row_tiles_per_wave(p), [&](auto d, auto rtw) {
     const dim3 grid(p.nchunk, p.hkv, p.batch);
+    if (zero_first)
+      return launch(snapkv_score_vote<decltype(d)::value, decltype(rtw)::value, true, true>, grid,
+                    stream, ev, p);
     if (ext_lse)
       return launch(snapkv_score_vote<decltype(d)::value, decltype(rtw)::value, true>, grid,
                     stream, ev, p);

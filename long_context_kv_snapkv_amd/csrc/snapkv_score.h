@@ -354,6 +354,34 @@ __device__ __forceinline__ void snapkv_score_stats_item(const PathParams& p, Sta
 // for its own inputs while the rest is still in flight.
 constexpr int kPartBatch = 8;
 
+// Publish this item's row statistics (device-coherent stores already
+// issued by every thread): each thread's stores complete, then the flag.
+__device__ __forceinline__ void publish_item(const PathParams& p, uint64_t* flags, int c) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&flags[c], p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until the flags of chunks 0 .. nch-1 of a head carry this call's
+// epoch, at most p.spin_limit polls each; returns non-zero (in every thread)
+// if any poll gave up. Ends with a workgroup barrier.
+__device__ __forceinline__ int wait_head(const PathParams& p, const uint64_t* flags, int nch) {
+  int timed_out = 0;
+  if ((int)threadIdx.x < nch) {
+    int spins = 0;
+    uint64_t* f = const_cast<uint64_t*>(&flags[threadIdx.x]);
+    while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != p.epoch) {
+      if (++spins > p.spin_limit) {
+        timed_out = 1;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  return __syncthreads_or(timed_out);
+}
+
 // Per-chunk statistics of one row, with a device-coherent load when another
 // workgroup of the same kernel wrote them (COHERENT).
 template <bool COHERENT>
@@ -366,7 +394,12 @@ __device__ __forceinline__ float2 load_part(const float2* a) {
     return *a;
 }
 
-template <int D, int RTW, bool EXT_LSE, bool COHERENT = false>
+// With ZERO_FIRST (normalisers from the caller, every item resident at
+// once) the item also stands in for the histogram clearing: item 0 of a head
+// clears the head's selection histograms with device-coherent stores and
+// publishes its flag, and every item checks that flag (bounded wait) before
+// adding its counts.
+template <int D, int RTW, bool EXT_LSE, bool COHERENT = false, bool ZERO_FIRST = false>
 __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, VoteSmem<D>& sm,
                                                        int b, int h, int c) {
   const int L = p.tab.len[b];
@@ -409,6 +442,15 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
                             [&] { ks.prefetch(); });
 
   for (int i = tid; i < kTopBins; i += kThreads) sm.top[i] = 0u;
+  if constexpr (ZERO_FIRST) {
+    if (c == 0) {
+      const size_t head0 = (size_t)(b * p.hkv + h);
+      uint32_t* top = p.top_hist + head0 * kSelHistWords;
+      for (int i = tid; i < kSelHistWords; i += kThreads)
+        __hip_atomic_store(&top[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      publish_item(p, p.flags + head0 * p.nchunk, 0);
+    }
+  }
   if (EXT_LSE) {
     // natural-log normaliser -> log2 units of the scaled logits
     if (tid < p.rows_pad) sm.lse[tid] = tid < p.rows ? ext * 1.4426950408889634f : kInf;
@@ -561,6 +603,12 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
     // histogram (few distinct bins per chunk, so few global atomics); the
     // barrier covers LDS only, the pooled stores need not have landed
     lds_barrier();
+    if constexpr (ZERO_FIRST) {
+      if (wait_head(p, p.flags + head * p.nchunk, 1)) {
+        // item 0 never published: the histograms are not to be trusted
+        for (int j = key0 + tid; j < kend; j += kThreads) pooled[j] = __builtin_nanf("");
+      }
+    }
     uint32_t* top = p.top_hist + head * kSelHistWords;
     for (int i = tid; i < kTopBins; i += kThreads) {
       const uint32_t n = sm.top[i];
@@ -598,34 +646,6 @@ struct alignas(16) FusedSmem {
 };
 static_assert(sizeof(FusedSmem<128>) <= 160 * 1024, "fused item LDS");
 static_assert(kTopBins * 4 <= KTile<128>::BYTES, "histogram in a key slot");
-
-// Publish this item's row statistics (device-coherent stores already
-// issued by every thread): each thread's stores complete, then the flag.
-__device__ __forceinline__ void publish_item(const PathParams& p, uint64_t* flags, int c) {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (threadIdx.x == 0)
-    __hip_atomic_store(&flags[c], p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Wait until the flags of chunks 0 .. nch-1 of a head carry this call's
-// epoch, at most p.spin_limit polls each; returns non-zero (in every thread)
-// if any poll gave up. Ends with a workgroup barrier.
-__device__ __forceinline__ int wait_head(const PathParams& p, const uint64_t* flags, int nch) {
-  int timed_out = 0;
-  if ((int)threadIdx.x < nch) {
-    int spins = 0;
-    uint64_t* f = const_cast<uint64_t*>(&flags[threadIdx.x]);
-    while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != p.epoch) {
-      if (++spins > p.spin_limit) {
-        timed_out = 1;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-  }
-  return __syncthreads_or(timed_out);
-}
 
 template <int D>
 __device__ __forceinline__ void snapkv_score_fused_item(const PathParams& p, FusedSmem<D>& sm,

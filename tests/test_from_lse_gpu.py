@@ -149,3 +149,29 @@ def test_llama3_70b_128k_with_device_normalisers():
     ref = oracle.compress(x.q_win, x.k, x.v, lens, w.window, w.kernel, w.pool, w.budget)
     check_structure_and_gather(res, x, w.window, w.budget)
     check_index_sets(res["out_idx"], ref.pooled, lens, w.window, w.budget)
+
+
+@needs_gpu
+@pytest.mark.parametrize("lens,hq,hkv,d,window,kernel,pool,budget", [
+    ([3000], 32, 8, 128, 32, 7, "max", 512),
+    ([64, 300, 65, 5, 1000], 8, 2, 128, 32, 5, "avg", 96),
+])
+def test_vote_clears_histograms_itself_identically(lens, hq, hkv, d, window, kernel, pool, budget,
+                                                   monkeypatch):
+    # with every vote item resident, the vote kernel's item 0 per head clears
+    # the selection histograms (no clearing launch); with the one-launch forms
+    # switched off a separate kernel clears them: every output bit the same
+    import long_context_kv_snapkv_amd as skv
+    from parity import upload
+    x = make_custom(lens, hq, hkv, d, window, seed=sum(lens) % 83)
+    lse = torch.from_numpy(_oracle_lse_f32(x, window, budget)).cuda()
+    q, k, v = upload(x)
+    print(f"[from_lse] clearing in the vote kernel {lens}", flush=True)
+    a = skv.snapkv_compress_from_lse(q, k, v, lens, window, lse, kernel, pool, budget)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("SNAPKV_NO_FUSED_SCORE", "1")
+    b = skv.snapkv_compress_from_lse(q, k, v, lens, window, lse, kernel, pool, budget)
+    torch.cuda.synchronize()
+    for ta, tb in zip(a, b):
+        assert torch.equal(ta.view(torch.int16) if ta.dtype == torch.bfloat16 else ta,
+                           tb.view(torch.int16) if tb.dtype == torch.bfloat16 else tb)
