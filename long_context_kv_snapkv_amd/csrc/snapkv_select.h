@@ -49,7 +49,7 @@ constexpr int kSlab = 4 * kThreads;  // positions per slab
 constexpr int kMaxSlabsHeld = 16;    // slabs per thread batch: 64 keys in VGPRs
 static_assert(kMaxSlabsHeld * kSlab == kSelectHeldKeys, "resident prefix length");
 constexpr int kBins = kTopBins;      // bins per digit (the last digit uses 1024)
-constexpr int kReplicas = 8;         // histogram copies
+constexpr int kReplicas = 4;         // histogram copies
 constexpr int kRepStride = kBins + 4;  // words between copies: 16-byte aligned, 4 banks apart
 constexpr int kHistWords = kReplicas * kRepStride;
 
