@@ -196,9 +196,11 @@ __device__ __forceinline__ void score_stats_body(const PathParams& p, unsigned c
     }
     const float mnew = fmaxf(mrun[t], fmaxf(mx0, mx1) * scale);
     const float mref = mnew == -kInf ? 0.f : mnew;  // an all -inf block changes nothing
-    float s0 = 0.f, s1 = 0.f;
+    // the first terms start the sums (0 + e is e exactly for every value
+    // exp2 returns, so no add of zero is issued)
+    float s0 = exp2_fast(fmaf(acc[0], scale, -mref)), s1 = exp2_fast(fmaf(acc[1], scale, -mref));
 #pragma unroll
-    for (int v = 0; v < 16; v += 2) {
+    for (int v = 2; v < 16; v += 2) {
       s0 += exp2_fast(fmaf(acc[v], scale, -mref));
       s1 += exp2_fast(fmaf(acc[v + 1], scale, -mref));
     }
@@ -211,9 +213,11 @@ __device__ __forceinline__ void score_stats_body(const PathParams& p, unsigned c
   // +inf or NaN and the block falls to the maximum path.
   auto update_full = [&](const f32x16& acc, int t) {
     const float m = mrun[t];
-    float s4[4] = {0.f, 0.f, 0.f, 0.f};  // short dependent add chains
+    float s4[4];  // short dependent add chains, started by their first terms
 #pragma unroll
-    for (int v = 0; v < 16; ++v) s4[v & 3] += exp2_fast(fmaf(acc[v], scale, -m));
+    for (int v = 0; v < 4; ++v) s4[v] = exp2_fast(fmaf(acc[v], scale, -m));
+#pragma unroll
+    for (int v = 4; v < 16; ++v) s4[v & 3] += exp2_fast(fmaf(acc[v], scale, -m));
     const float sb = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     const bool ok = sb <= kBlockSumCap;  // false for +inf and NaN too
     srun[t] = ok ? srun[t] + sb : srun[t];
@@ -511,10 +515,17 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
   // writes its own partial. Four partial sums keep the dependent add chains
   // short; every key of a wave is summed in this same order on every path,
   // so equal columns give equal votes.
+  // The first four terms start the partial sums: 0 + e is e exactly for
+  // every value exp2 returns, so this equals summing into zeros.
   auto colsum = [&](const f32x16(&acc)[RTW]) {
-    float c4[4] = {0.f, 0.f, 0.f, 0.f};
+    if (role.my_nrt < 1) return 0.f;
+    float c4[4];
 #pragma unroll
-    for (int t = 0; t < RTW; ++t) {
+    for (int v = 0; v < 4; ++v) c4[v] = exp2_fast(fmaf(acc[0][v], scale, -lr[0][v]));
+#pragma unroll
+    for (int v = 4; v < 16; ++v) c4[v & 3] += exp2_fast(fmaf(acc[0][v], scale, -lr[0][v]));
+#pragma unroll
+    for (int t = 1; t < RTW; ++t) {
       if (t >= role.my_nrt) break;
 #pragma unroll
       for (int v = 0; v < 16; ++v) c4[v & 3] += exp2_fast(fmaf(acc[t][v], scale, -lr[t][v]));
@@ -547,9 +558,13 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
 #pragma unroll
         for (int g = 0; g < GB; ++g) {
           // the order of colsum below
-          float c4[4] = {0.f, 0.f, 0.f, 0.f};
+          float c4[4];
 #pragma unroll
-          for (int t = 0; t < RTW; ++t)
+          for (int v = 0; v < 4; ++v) c4[v] = exp2_fast(fmaf(acc[g][0][v], scale, -lr[0][v]));
+#pragma unroll
+          for (int v = 4; v < 16; ++v) c4[v & 3] += exp2_fast(fmaf(acc[g][0][v], scale, -lr[0][v]));
+#pragma unroll
+          for (int t = 1; t < RTW; ++t)
 #pragma unroll
             for (int v = 0; v < 16; ++v) c4[v & 3] += exp2_fast(fmaf(acc[g][t][v], scale, -lr[t][v]));
           vr[(kb + g * role.nwk) * 32] = (c4[0] + c4[1]) + (c4[2] + c4[3]);
@@ -751,9 +766,11 @@ __device__ __forceinline__ void snapkv_score_fused_item(const PathParams& p, Fus
     return acc;
   };
   auto colsum = [&](const f32x16& acc) {
-    float c4[4] = {0.f, 0.f, 0.f, 0.f};
+    float c4[4];  // started by the first terms, as in the vote item
 #pragma unroll
-    for (int v = 0; v < 16; ++v) c4[v & 3] += exp2_fast(fmaf(acc[v], scale, -lr[v]));
+    for (int v = 0; v < 4; ++v) c4[v] = exp2_fast(fmaf(acc[v], scale, -lr[v]));
+#pragma unroll
+    for (int v = 4; v < 16; ++v) c4[v & 3] += exp2_fast(fmaf(acc[v], scale, -lr[v]));
     return (c4[0] + c4[1]) + (c4[2] + c4[3]);
   };
   const int nparts = 2 * role.nwr;  // (row-tile wave, lane half) partial sums per key
