@@ -157,7 +157,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the compression path runs on a single "
-              "MI355X and this build launches no multi-GPU work (--gpus must be 1).",
+              "MI355X and launches no multi-GPU work (--gpus must be 1).",
               file=sys.stderr)
         sys.exit(2)
 

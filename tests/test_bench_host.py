@@ -1,0 +1,75 @@
+"""Host-side logic of bench.py that runs without a GPU: the one-GPU guard,
+the algorithmic byte counts its roofline is priced with, and the rule that
+counter-derived HBM traffic is reported only for the kernel sources it was
+measured on."""
+
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from synth import WORKLOADS  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""  # no JSON line
+
+
+def test_stage_bytes_of_the_16k_layer():
+    # Q_win [32 heads, 32 rows, 128] and K [16384 keys, 8 heads, 128] in bf16,
+    # K read once by the fused score kernel; the vote reads the P = L - W prefix
+    w = WORKLOADS["llama3_8b_16k"]
+    lens = [16384]
+    sb = bench.stage_bytes(w, lens)
+    q = 32 * 32 * 128 * 2
+    assert sb["snapkv_score_fused"] == q + 8 * 16384 * 128 * 2 == 33816576
+    assert sb["snapkv_score_stats"] == sb["snapkv_score_fused"]
+    assert sb["snapkv_score_vote"] == q + 8 * (16384 - 32) * 128 * 2
+    # kept rows: 1024 per head, K and V read and written, plus the index list
+    gather = 4 * 8 * 1024 * 128 * 2 + 4 * 8 * 1024
+    assert sb["snapkv_gather"] == gather
+    assert sb["snapkv_gather_select"] == gather + 8 * (16384 - 32) * 4
+    score, g = bench.algorithmic_bytes(w, lens)
+    assert (score, g) == (sb["snapkv_score_fused"], gather)
+
+
+def test_prompts_within_the_budget_move_only_their_rows():
+    # a prompt of L <= B is kept whole: no scoring bytes, its L rows copied
+    w = WORKLOADS["llama3_8b_16k"]
+    score, g = bench.algorithmic_bytes(w, [w.budget, 100])
+    assert score == 0
+    assert g == sum(4 * w.h_kv * n * w.head_dim * 2 + 4 * w.h_kv * n for n in (w.budget, 100))
+    assert bench.score_flops(w, [w.budget, 100]) == 0
+
+
+def test_traffic_is_reported_only_for_the_measured_sources(monkeypatch, tmp_path):
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    rec = {"snapkv_score_fused": {"source_hash": "abc", "hbm_bytes_per_launch": 123}}
+    (prof / "traffic.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "_source_hash", lambda names: "abc")
+    assert bench._traffic("snapkv_score_fused") == 123
+    assert bench._traffic("snapkv_gather") is None
+    monkeypatch.setattr(bench, "_source_hash", lambda names: "changed")
+    assert bench._traffic("snapkv_score_fused") is None
+    (prof / "traffic.json").unlink()
+    assert bench._traffic("snapkv_score_fused") is None
+
+
+def test_source_hash_covers_every_kernel_source():
+    csrc = os.path.join(ROOT, "long_context_kv_snapkv_amd", "csrc")
+    device_sources = {f for f in os.listdir(csrc) if f.startswith("snapkv_")
+                      and f.endswith((".h", ".hip", ".cpp")) and "decode" not in f}
+    missing = device_sources - set(bench.KERNEL_SOURCES)
+    assert not missing, missing
