@@ -223,16 +223,23 @@ __device__ __forceinline__ void select_head(const PathParams& p, SelectSmem& sm,
   static_assert(kSegment == 4 * 64, "a segment is one wave's share of a slab");
   const int nseg = (P + kSegment - 1) / kSegment;
   uint32_t* table = out.table;
+  // `settled` is the same in every thread (read from LDS after a barrier);
+  // taken as a scalar, each key costs one or two compares, not both forms
+  const bool settled_s = __builtin_amdgcn_readfirstlane(settled ? 1 : 0) != 0;
   for (int bt = 0; bt < nbatch; ++bt) {
     if (!RESIDENT) load_keys<NS>(key, src, P, bt * NS);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       uint32_t c = 0;  // above | equal << 16 (a wave sums at most 256 of each)
+      if (settled_s) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t u = key[s][e];
-        c += (settled ? u >= tau : u > tau) ? 1u : 0u;
-        c += (!settled && u == tau) ? 0x10000u : 0u;
+        for (int e = 0; e < 4; ++e) c += key[s][e] >= tau ? 1u : 0u;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          c += key[s][e] > tau ? 1u : 0u;
+          c += key[s][e] == tau ? 0x10000u : 0u;
+        }
       }
       const uint32_t tot = wave_sum(c);
       const int g = (bt * NS + s) * kWaves + wave;  // segment index in the prefix
