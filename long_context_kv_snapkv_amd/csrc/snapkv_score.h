@@ -809,6 +809,10 @@ __device__ __forceinline__ void snapkv_score_fused_item(const PathParams& p, Fus
   static_assert(2 * kWaves * kVotedMax * 4 <= 2 * KTile<D>::BYTES, "partials in two key slots");
   float (*vall)[kVotedMax] = reinterpret_cast<float (*)[kVotedMax]>(&sm.k[0][0]);
   __syncthreads();  // every wave is done with the key tiles
+  // the first digit's histogram lives in a key slot no longer read; cleared
+  // here, it is ordered before the counting below by the fold's barriers
+  uint32_t* top = reinterpret_cast<uint32_t*>(sm.k[2]);
+  for (int i = tid; i < kTopBins; i += kThreads) top[i] = 0u;
   {
     const int col = lane & 31;
     float* mine = vall[2 * role.wr + (lane >> 5)];  // this (row-tile wave, lane half)
@@ -830,11 +834,7 @@ __device__ __forceinline__ void snapkv_score_fused_item(const PathParams& p, Fus
   }
   __syncthreads();
 
-  // snapkv_pool and the first radix digit, as in the vote item; the
-  // histogram lives in a key slot no longer read
-  uint32_t* top = reinterpret_cast<uint32_t*>(sm.k[2]);
-  for (int i = tid; i < kTopBins; i += kThreads) top[i] = 0u;
-  lds_barrier();
+  // snapkv_pool and the first radix digit, as in the vote item
   float* pooled = p.pooled + head * p.pooled_stride;
   for (int j = key0 + tid; j < kend; j += kThreads) {
     float c_j = pool_value([&](int u) { return sm.s_chunk[u - kv0]; }, j, P, p.kernel,
