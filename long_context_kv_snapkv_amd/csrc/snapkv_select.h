@@ -18,12 +18,14 @@
 //     whole selection; longer prefixes are re-read in batches of that size;
 //   * radix select, digits of 11, 11 and 10 bits, most significant first.
 //     The first digit's histogram was accumulated by the vote kernel. Each
-//     later digit counts the keys that match the known prefix into kReplicas
-//     LDS copies (lane l adds to copy l % kReplicas, copies 4 banks apart):
-//     scores concentrate in few bins and lanes that hit one address
-//     serialise, so the copies bound that to 64 / kReplicas lanes. Each wave
-//     sums the copies of one histogram row and the bin holding the m-th
-//     largest key is found from the row totals. When every key of that bin
+//     later digit counts the keys that match the known prefix into an LDS
+//     histogram with atomic adds (kReplicas copies are supported, lane l
+//     adding to copy l % kReplicas, copies 4 banks apart, to spread lanes
+//     that hit one address; one copy measured fastest: only the keys of the
+//     threshold bin are counted, and clearing and summing copies costs more
+//     than the adds they spread). Each wave sums the copies of one histogram
+//     row and the bin holding the m-th largest key is found from the row
+//     totals. When every key of that bin
 //     is needed the threshold is settled at that digit: the kept keys are
 //     exactly those >= the bin's lowest key;
 //   * count table: for every kSegment positions, how many of its keys lie
@@ -49,7 +51,7 @@ constexpr int kSlab = 4 * kThreads;  // positions per slab
 constexpr int kMaxSlabsHeld = 16;    // slabs per thread batch: 64 keys in VGPRs
 static_assert(kMaxSlabsHeld * kSlab == kSelectHeldKeys, "resident prefix length");
 constexpr int kBins = kTopBins;      // bins per digit (the last digit uses 1024)
-constexpr int kReplicas = 4;         // histogram copies
+constexpr int kReplicas = 1;         // histogram copies
 constexpr int kRepStride = kBins + 4;  // words between copies: 16-byte aligned, 4 banks apart
 constexpr int kHistWords = kReplicas * kRepStride;
 
