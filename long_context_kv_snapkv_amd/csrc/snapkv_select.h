@@ -259,7 +259,7 @@ __device__ __forceinline__ void select_head(const PathParams& p, SelectSmem& sm,
 }
 
 // ------------------------------------------------------ sliced selection ---
-constexpr int kSliceReplicas = 4;  // histogram copies (8 keys per thread: less contention)
+constexpr int kSliceReplicas = 1;  // histogram copies (one measured fastest, as for kReplicas)
 static_assert(kSliceKeys == 2 * kSlab, "a slice is two slabs: 8 keys per thread");
 
 struct alignas(16) SliceSmem {
