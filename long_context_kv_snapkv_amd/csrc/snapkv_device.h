@@ -184,8 +184,9 @@ __device__ __forceinline__ void read_key_frags(bf16x8 (&kf)[D / 16], const unsig
 
 // Stream the keys [key0, kend) of one head through two LDS tile buffers,
 // with two more tiles in flight in registers. KeyStream::prefetch issues the
-// loads of tile 0 (the caller may do other work while they fly, as long as
-// it does not wait on global loads issued after them); run() then stores
+// loads of tile 0, and of tile 1 when deep (the caller may do other work
+// while they fly, as long as it does not wait on global loads issued after
+// them); run() then stores
 // tile i to LDS, loads tile i + 2 into the freed registers, and after
 // a barrier that makes tile i visible (and guarantees every wave is done with
 // tile i - 1) calls after_barrier(i) and compute(tile, i). Global loads stay
@@ -200,7 +201,7 @@ struct KeyStream {
   size_t tstride;
   int key0, kend;
   bool reverse = false;  // visit the tiles last to first
-  bool deep = false;     // prefetch() requests the first two tiles (run_resident)
+  bool deep = false;     // prefetch() requests the first two tiles
 
   __device__ __forceinline__ int ntiles() const { return (kend - key0 + T::KEYS - 1) / T::KEYS; }
   // first key of the i-th tile visited
@@ -208,8 +209,11 @@ struct KeyStream {
     return key0 + (reverse ? ntiles() - 1 - i : i) * T::KEYS;
   }
 
-  // Only tile 0 is requested up front: when every CU starts at once, the
-  // first tile arrives sooner if it does not compete with deeper prefetch.
+  // The two-kernel statistics pass requests only tile 0 up front: when
+  // every CU starts at once, the first tile arrives sooner if it does not
+  // compete with deeper prefetch. The fused score kernels (deep) request
+  // tiles 0 and 1 while their query rows are staged, which measured faster
+  // there (the 128K layer's streaming kernel about 1%).
   __device__ __forceinline__ void prefetch() {
     load_key_tile<D>(ra, kb, tstride, tile_key(0), kend, threadIdx.x);
     if (deep) {
@@ -230,8 +234,10 @@ struct KeyStream {
     // tiles past the end (visited indices >= ntiles) re-read a valid tile
     auto start = [&](int i) { return tile_key(min(i, ntiles - 1)); };
     store_key_tile<D>(ra, ring[0], tid);
-    load_key_tile<D>(rb, kb, tstride, start(1), kend, tid);
-    asm volatile("" ::: "memory");  // keep tile 1's loads older than tile 2's
+    if (!deep) {  // else tile 1 is already in flight
+      load_key_tile<D>(rb, kb, tstride, start(1), kend, tid);
+      asm volatile("" ::: "memory");  // keep tile 1's loads older than tile 2's
+    }
     load_key_tile<D>(ra, kb, tstride, start(2), kend, tid);
     lds_barrier();
     after_barrier(0);

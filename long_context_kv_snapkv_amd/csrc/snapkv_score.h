@@ -875,7 +875,7 @@ __device__ __forceinline__ void snapkv_score_fused_stream_item(const PathParams&
   const size_t head = (size_t)(b * p.hkv + h);
   {
     bf16x8 qf[RTW][D / 16];
-    score_stats_body<D, RTW, true>(
+    score_stats_body<D, RTW, true, true>(
         p, sm.st.ring[1], sm.st.wstats, qf,
         [&](KeyStream<D>& ks, auto&& compute) { ks.run(sm.st.ring, compute, [](int) {}); }, b,
         h, c);
