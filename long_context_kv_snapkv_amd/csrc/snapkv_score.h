@@ -345,7 +345,7 @@ template <int D, int RTW>
 __device__ __forceinline__ void snapkv_score_stats_item(const PathParams& p, StatsSmem<D>& sm,
                                                         int b, int h, int c) {
   bf16x8 qf[RTW][D / 16];
-  score_stats_body<D, RTW, false>(
+  score_stats_body<D, RTW, false, true>(
       p, sm.ring[1], sm.wstats, qf,
       [&](KeyStream<D>& ks, auto&& compute) { ks.run(sm.ring, compute, [](int) {}); }, b, h, c);
 }
