@@ -209,11 +209,10 @@ struct KeyStream {
     return key0 + (reverse ? ntiles() - 1 - i : i) * T::KEYS;
   }
 
-  // The two-kernel statistics pass requests only tile 0 up front: when
-  // every CU starts at once, the first tile arrives sooner if it does not
-  // compete with deeper prefetch. The fused score kernels (deep) request
-  // tiles 0 and 1 while their query rows are staged, which measured faster
-  // there (the 128K layer's streaming kernel about 1%).
+  // The vote item requests only tile 0 up front (two measured slower
+  // there). Every statistics pass (deep) requests tiles 0 and 1 while its
+  // query rows are staged, which measured faster: the 128K layer's
+  // streaming kernel and the ragged batch's statistics kernel by about 1%.
   __device__ __forceinline__ void prefetch() {
     load_key_tile<D>(ra, kb, tstride, tile_key(0), kend, threadIdx.x);
     if (deep) {
