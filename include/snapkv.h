@@ -149,16 +149,18 @@ int32_t snapkv_compress(int32_t batch, int32_t num_q_heads,
  * the environment variable SNAPKV_NO_FUSED_SCORE is set to a non-empty value
  * other than "0" (read at every call), it is always 2.
  * Concurrency: the one-kernel forms count on having the device's compute
- * units to themselves while they run. A process that runs compressions on
- * several streams of one device at once sets SNAPKV_NO_FUSED_SCORE, or
- * SNAPKV_COOPERATIVE (read at every call), which launches them as
- * cooperative kernels so that the runtime guarantees every work item a
- * compute unit (about 19 us more per call on MI355X). Otherwise concurrent
- * fused calls can each wait on items the other's hold CUs from; the wait is
- * bounded (about a second; SNAPKV_SPIN_LIMIT, read at every call, lowers
- * the number of polls, e.g. to exercise this path), after which the items
- * give up and their pooled scores, and so the selection, are not meaningful
- * (NaN scores); every kernel still exits and the outputs keep their layout.
+ * units to themselves while they run; the results never depend on it. Each
+ * wait is bounded (about a second of polling; SNAPKV_SPIN_LIMIT, read at
+ * every call, lowers the number of polls, e.g. to exercise this path): an
+ * item that stops waiting computes the statistics it did not receive itself,
+ * with the same arithmetic, and the selection recounts its first radix digit
+ * when a histogram may have missed its clearing, so the outputs are the same
+ * bits as with no wait given up; only the time grows. A process that runs
+ * compressions on several streams of one device at once may set
+ * SNAPKV_NO_FUSED_SCORE, or SNAPKV_COOPERATIVE (read at every call), which
+ * launches them as cooperative kernels so that the runtime guarantees every
+ * work item a compute unit (about 19 us more per call on MI355X), to avoid
+ * those slow calls.
  * snapkv_compress_from_lse always runs the vote kernel alone. Writes
  * *kernels and returns SNAPKV_OK, or an error status under the shape rules
  * of snapkv_compress (SNAPKV_ERR_INVALID_ARGUMENT also for a NULL
@@ -187,6 +189,36 @@ int32_t snapkv_gather_selects(int32_t batch, int32_t num_q_heads,
                               int32_t num_kv_heads, int32_t head_dim,
                               const int32_t* seq_lens, int32_t window,
                               int32_t budget, int32_t* fused);
+
+/*
+ * snapkv_compress (window_lse NULL) or snapkv_compress_from_lse (window_lse
+ * as there) that also hands out the pooled scores its selection read, for
+ * checking the path's scores against a reference (the scores of step 2 above
+ * as they come out of whichever scoring kernels snapkv_score_kernels names
+ * for the shape):
+ *
+ *   out_scores  device float32 [batch, H_kv, scores_len], 16-byte aligned;
+ *               entry j < P_b of prompt b with L_b > budget holds c_h[j],
+ *               every other entry (prompts kept whole, positions past P_b)
+ *               is written as 0.
+ *   scores_len  >= max_b(L_b - W) and >= 1.
+ *
+ * The compressed cache is identical to snapkv_compress's (or
+ * snapkv_compress_from_lse's); one more kernel copies the scores out of the
+ * workspace after the gather. Errors as for those calls;
+ * SNAPKV_ERR_INVALID_ARGUMENT also for a null or misaligned out_scores or a
+ * scores_len that is too small.
+ */
+int32_t snapkv_compress_with_scores(int32_t batch, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim,
+                                    const void* q_win, const void* k,
+                                    const void* v, const int32_t* seq_lens,
+                                    int32_t window, const float* window_lse,
+                                    int32_t kernel_size, int32_t pool_mode,
+                                    int32_t budget, void* out_k, void* out_v,
+                                    int32_t* out_idx, float* out_scores,
+                                    int32_t scores_len, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 /*
  * snapkv_compress with optional per-stage timing: the same kernels (named by

@@ -28,6 +28,7 @@ from .snapkv import (  # noqa: F401
     snapkv_compress_fp8,
     snapkv_compress_from_lse,
     snapkv_compress_int4,
+    snapkv_compress_with_scores,
     snapkv_decode_attention,
     snapkv_decode_workspace_size,
     snapkv_last_error,

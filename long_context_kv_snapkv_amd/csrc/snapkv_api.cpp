@@ -45,13 +45,15 @@ int largest_pow2_at_most(int x) {
 //   sel_meta  uint32[batch * H_kv, 4]               threshold of each head
 //   part      float2[batch, H_kv, nchunk, rows_pad]  per-chunk row statistics
 //   flags     uint64[batch, H_kv, nchunk]       fused score kernel: published items
+//   hist_bad  uint64[batch * H_kv]               call whose first-digit counts are untrusted
 //   pooled    float [batch, H_kv, p_stride]      pooled scores, p_stride =
 //                                                max P rounded up to 64
-// Every word is written by a call before that call reads it.
+// Every word is written by a call before that call reads it, except flags
+// and hist_bad, which only count when they hold the call's own epoch.
 struct Plan {
   int batch, hq, hkv, d, window, group, rows, rows_pad, nrt, nwr;
   int chunk, nchunk, l_max, p_max, p_stride;
-  size_t off_top, off_table, off_meta, off_part, off_flags, off_pooled, bytes;
+  size_t off_top, off_table, off_meta, off_part, off_flags, off_bad, off_pooled, bytes;
   int t_stride;
   snapkv::PromptTable tab;
 };
@@ -125,6 +127,8 @@ int32_t make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const int32
   off = align_up(off + heads * pl->nchunk * pl->rows_pad * sizeof(float2), 256);
   pl->off_flags = off;
   off = align_up(off + heads * pl->nchunk * sizeof(uint64_t), 256);
+  pl->off_bad = off;
+  off = align_up(off + heads * sizeof(uint64_t), 256);
   pl->off_pooled = off;
   off = align_up(off + heads * pl->p_stride * sizeof(float), 256);
   pl->bytes = off;
@@ -175,6 +179,7 @@ snapkv::PathParams path_params(const Plan& pl, const void* q, const void* k, con
   p.table_stride = pl.t_stride;
   p.part = reinterpret_cast<float2*>(w + pl.off_part);
   p.flags = reinterpret_cast<uint64_t*>(w + pl.off_flags);
+  p.hist_bad = reinterpret_cast<uint64_t*>(w + pl.off_bad);
   p.pooled = reinterpret_cast<float*>(w + pl.off_pooled);
   p.pooled_stride = pl.p_stride;
   p.batch = pl.batch;
@@ -212,9 +217,10 @@ int device_cus() {
   return n;
 }
 
-// Publication marks of the fused score kernel: unique per call in this
-// process and started at a random odd value, so neither an earlier call's
-// flags nor stale memory in a fresh workspace can match.
+// Marks of a call (the fused score kernels' publication flags, the
+// untrusted-histogram word): unique per call in this process and started at
+// a random odd value, so neither an earlier call's marks nor stale memory in
+// a fresh workspace can match.
 uint64_t next_epoch() {
   static std::atomic<uint64_t> counter{[] {
     std::random_device rd;
@@ -327,12 +333,18 @@ struct QuantOut {
   int form;  // 1: 4-bit, 2: FP8 E4M3
 };
 
+// Export of the pooled rows the selection read (snapkv_compress_with_scores).
+struct ScoresOut {
+  float* scores;
+  int32_t len;
+};
+
 int32_t compress_impl(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const void* q_win,
                       const void* k, const void* v, const int32_t* seq_lens, int32_t window,
                       int32_t kernel, int32_t pool_mode, int32_t budget, void* out_k,
                       void* out_v, int32_t* out_idx, void* workspace, size_t workspace_bytes,
                       void* stream, void* const* stage_events, const float* window_lse,
-                      const QuantOut* q4 = nullptr) {
+                      const QuantOut* q4 = nullptr, const ScoresOut* so = nullptr) {
   int32_t st = q4 ? check_tensors(q_win, k, v, q4->kq, q4->vq, out_idx)
                   : check_tensors(q_win, k, v, out_k, out_v, out_idx);
   if (st != SNAPKV_OK) return st;
@@ -345,6 +357,13 @@ int32_t compress_impl(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const v
     return fail(SNAPKV_ERR_INVALID_ARGUMENT, "budget must exceed window (it includes the window)");
   st = check_pool(kernel, pool_mode);
   if (st != SNAPKV_OK) return st;
+  if (so != nullptr) {
+    if (so->scores == nullptr || misaligned(so->scores))
+      return fail(SNAPKV_ERR_INVALID_ARGUMENT, "out_scores must be non-null and 16-byte aligned");
+    if (so->len < pl.p_max)
+      return fail(SNAPKV_ERR_INVALID_ARGUMENT,
+                  "scores_len must be >= max(seq_len) - window = " + std::to_string(pl.p_max));
+  }
   if (workspace == nullptr || workspace_bytes < pl.bytes || misaligned(workspace))
     return fail(SNAPKV_ERR_WORKSPACE, "workspace must be 16-byte aligned and hold " +
                                           std::to_string(pl.bytes) + " bytes");
@@ -361,6 +380,8 @@ int32_t compress_impl(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const v
   }
   p.out_idx = out_idx;
   p.window_lse = window_lse;
+  p.epoch = next_epoch();
+  p.spin_limit = spin_limit();
   const bool ext_lse = window_lse != nullptr;
   hipError_t e;
   // optional caller events, recorded by each stage's dispatch at the
@@ -390,9 +411,7 @@ int32_t compress_impl(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const v
     const Scoring sc = ext_lse ? Scoring::kTwoKernels : scoring_plan(pl, kernel);
     if (sc != Scoring::kTwoKernels) {
       // statistics and vote in one launch (stage 0); stage 1 is empty
-      p.epoch = next_epoch();
       p.cooperative = env_flag("SNAPKV_COOPERATIVE") ? 1 : 0;
-      p.spin_limit = spin_limit();
       if (sc == Scoring::kFusedResident) {
         if ((e = snapkv::launch_score_fused(p, d, s, events(0))) != hipSuccess)
           return hip_fail(e, "snapkv_score_fused launch");
@@ -406,8 +425,6 @@ int32_t compress_impl(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const v
       // (every vote item resident at once) the vote kernel's item 0 per head
       const bool zero_first = ext_lse && votes_resident(pl);
       if (zero_first) {
-        p.epoch = next_epoch();
-        p.spin_limit = spin_limit();
         skip(0);
       } else if (ext_lse) {
         if ((e = snapkv::launch_clear_hist(p, s, events(0))) != hipSuccess)
@@ -433,6 +450,12 @@ int32_t compress_impl(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const v
       return hip_fail(e, "snapkv_gather_select launch");
   } else if ((e = snapkv::launch_gather(p, d, s, events(3), q4 ? q4->form : 0)) != hipSuccess) {
     return hip_fail(e, "snapkv_gather launch");
+  }
+  if (so != nullptr) {
+    p.scores_out = so->scores;
+    p.scores_len = so->len;
+    if ((e = snapkv::launch_export_pooled(p, s)) != hipSuccess)
+      return hip_fail(e, "snapkv_export_pooled launch");
   }
   return SNAPKV_OK;
 }
@@ -572,6 +595,21 @@ int32_t snapkv_compress_from_lse(int32_t batch, int32_t num_q_heads, int32_t num
   return compress_impl(batch, num_q_heads, num_kv_heads, head_dim, q_win, k, v, seq_lens, window,
                        kernel_size, pool_mode, budget, out_k, out_v, out_idx, workspace,
                        workspace_bytes, stream, nullptr, window_lse);
+}
+
+int32_t snapkv_compress_with_scores(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, const void* q_win, const void* k,
+                                    const void* v, const int32_t* seq_lens, int32_t window,
+                                    const float* window_lse, int32_t kernel_size,
+                                    int32_t pool_mode, int32_t budget, void* out_k, void* out_v,
+                                    int32_t* out_idx, float* out_scores, int32_t scores_len,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (window_lse != nullptr && (reinterpret_cast<uintptr_t>(window_lse) & 3u) != 0)
+    return fail(SNAPKV_ERR_INVALID_ARGUMENT, "window_lse must be 4-byte aligned");
+  const ScoresOut so{out_scores, scores_len};
+  return compress_impl(batch, num_q_heads, num_kv_heads, head_dim, q_win, k, v, seq_lens, window,
+                       kernel_size, pool_mode, budget, out_k, out_v, out_idx, workspace,
+                       workspace_bytes, stream, nullptr, window_lse, nullptr, &so);
 }
 
 int32_t snapkv_compress_staged(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

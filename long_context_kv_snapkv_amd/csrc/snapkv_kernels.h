@@ -17,8 +17,12 @@ constexpr int kGatherRows = 64;    // compressed rows per gather work item (at m
 constexpr int kTopHistBins = 2048; // bins of the selection's first radix digit
 constexpr int kSegment = 256;      // positions per selection count-table entry
 // per head: the selection's radix histograms of digits 1, 2 and 3 (2048,
-// 2048 and 1024 bins), adjacent
-constexpr int kSelHistWords = 2048 + 2048 + 1024;
+// 2048 and 1024 bins), adjacent, then a first-digit histogram that the sliced
+// selection recounts from the pooled scores when the score kernel's counts
+// are not to be trusted (see PathParams::hist_bad)
+constexpr int kHistD1 = 0, kHistD2 = 2048, kHistD3 = 4096, kHistFix = 5120;
+constexpr int kHistCleared = kHistFix;  // words zeroed before each call's counting
+constexpr int kSelHistWords = kHistFix + 2048;
 constexpr int kSliceKeys = 4096;   // prefix positions per sliced-selection work item
 constexpr int kSelectHeldKeys = 64 * kThreads;  // prefix positions one selection workgroup
                                                 // keeps in registers (longer: sliced)
@@ -64,7 +68,10 @@ struct PathParams {
   uint32_t* sel_meta;   // [batch * Hkv, 4]: threshold key, keys equal to it kept, settled
   uint64_t* flags;      // [batch, Hkv, nchunk] fused score kernel: `epoch` once an item's
                         // row statistics are published
-  uint64_t epoch;       // this call's publication mark (unique per call in the process)
+  uint64_t* hist_bad;   // [batch * Hkv] `epoch` when an item of the head added its counts to
+                        // the first-digit histogram without having seen it cleared (a bounded
+                        // wait gave up): the selection then recounts that digit itself
+  uint64_t epoch;       // this call's mark (unique per call in the process)
   int32_t cooperative;  // launch the fused score kernels as cooperative launches
   int32_t spin_limit;   // polls before a fused score item stops waiting (kSpinLimit)
   int32_t batch, hq, hkv, window, group;
@@ -82,6 +89,8 @@ struct PathParams {
                            // there are few items (D = 128 only)
   int32_t sel_slices;      // 0: one selection workgroup per head; else kSliceKeys-position
                            // slices per head of the sliced selection
+  float* scores_out;       // snapkv_compress_with_scores: [batch, Hkv, scores_len] copy of
+  int32_t scores_len;      // the pooled rows the selection read (0 where not compressed)
   float scale_log2;        // log2(e) / sqrt(D)
   PromptTable tab;
 };
@@ -120,5 +129,7 @@ hipError_t launch_gather(const PathParams& p, int head_dim, hipStream_t stream,
 // the gather with the selection inside each item (sel_slices == 0 only)
 hipError_t launch_gather_select(const PathParams& p, int head_dim, hipStream_t stream,
                                 StageEvents ev = {}, int form = 0);
+// copy of the pooled rows of compressed prompts to p.scores_out (zeros elsewhere)
+hipError_t launch_export_pooled(const PathParams& p, hipStream_t stream);
 
 }  // namespace snapkv

@@ -93,7 +93,7 @@ __global__ void __launch_bounds__(kThreads) snapkv_clear_hist(const PathParams p
   const int h = blockIdx.x, b = blockIdx.y;
   if (!is_scored(p, b)) return;
   uint4* top = reinterpret_cast<uint4*>(p.top_hist + (size_t)(b * p.hkv + h) * kSelHistWords);
-  for (int i = threadIdx.x; i < kSelHistWords / 4; i += kThreads) top[i] = make_uint4(0u, 0u, 0u, 0u);
+  for (int i = threadIdx.x; i < kHistCleared / 4; i += kThreads) top[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 __global__ void __launch_bounds__(kThreads) snapkv_select(const PathParams p) {
@@ -152,6 +152,19 @@ __global__ void __launch_bounds__(kThreads) snapkv_gather_select(const PathParam
     locate_kept(p, sm.gs, b, h, t0, min(t0 + RW, m), sm.table, sm.thr);
   }
   gather_rows<D, FORM, RW>(p, sm.gs, b, h, rb);
+}
+
+// The pooled rows a compress call selected from, copied out of the
+// workspace after the call's own kernels (stream order): entry j < P of each
+// compressed prompt (L > budget), zero everywhere else.
+__global__ void __launch_bounds__(kThreads) snapkv_export_pooled(const PathParams p) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  const size_t head = (size_t)(b * p.hkv + h);
+  const int L = p.tab.len[b];
+  const int P = L > p.budget ? L - p.window : 0;
+  const float* src = p.pooled + head * p.pooled_stride;
+  float* dst = p.scores_out + head * p.scores_len;
+  for (int j = threadIdx.x; j < p.scores_len; j += kThreads) dst[j] = j < P ? src[j] : 0.f;
 }
 
 // Launch with one PathParams argument; with events, through the extended
@@ -246,6 +259,10 @@ hipError_t launch_score_fused_stream(const PathParams& p, int head_dim, hipStrea
     return launch(snapkv_score_fused_stream<decltype(d)::value, decltype(rtw)::value>,
                   dim3(p.nchunk, p.hkv, p.batch), stream, ev, p, p.cooperative != 0);
   });
+}
+
+hipError_t launch_export_pooled(const PathParams& p, hipStream_t stream) {
+  return launch(snapkv_export_pooled, dim3(p.hkv, p.batch), stream, StageEvents{}, p);
 }
 
 hipError_t launch_clear_hist(const PathParams& p, hipStream_t stream, StageEvents ev) {

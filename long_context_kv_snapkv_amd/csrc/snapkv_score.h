@@ -123,8 +123,10 @@ struct KeyGroup {
 // streams the chunk's key tiles (through a ring, or into resident slots for
 // the fused kernel). The query fragments are left in `qf`. With COHERENT the
 // statistics and the histogram clearing are written with device-coherent
-// stores (another workgroup of the same kernel reads them).
-template <int D, int RTW, bool COHERENT, bool DEEP = false, typename Run>
+// stores (another workgroup of the same kernel reads them). Item 0 of a head
+// clears the head's selection histograms unless CLEAR is false (an item
+// recomputing another item's statistics leaves that to the owner).
+template <int D, int RTW, bool COHERENT, bool DEEP = false, bool CLEAR = true, typename Run>
 __device__ __forceinline__ void score_stats_body(const PathParams& p, unsigned char* qbuf,
                                                  float2 (*wstats)[kMaxRowTilesPerWave * 32],
                                                  bf16x8 (&qf)[RTW][D / 16], Run&& run, int b,
@@ -316,9 +318,9 @@ __device__ __forceinline__ void score_stats_body(const PathParams& p, unsigned c
   }
   __syncthreads();
   float2* dst = p.part + ((size_t)(b * p.hkv + h) * p.nchunk + c) * p.rows_pad;
-  if (c == 0) {  // the vote items (digit 1) and a sliced selection (digits 2, 3) add to these
+  if (CLEAR && c == 0) {  // the vote items (digit 1) and a sliced selection (digits 2, 3) add to these
     uint32_t* top = p.top_hist + (size_t)(b * p.hkv + h) * kSelHistWords;
-    for (int i = tid; i < kSelHistWords; i += kThreads) {
+    for (int i = tid; i < kHistCleared; i += kThreads) {
       if constexpr (COHERENT)
         __hip_atomic_store(&top[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       else
@@ -369,8 +371,21 @@ __device__ __forceinline__ void publish_item(const PathParams& p, uint64_t* flag
 
 // Wait until the flags of chunks 0 .. nch-1 of a head carry this call's
 // epoch, at most p.spin_limit polls each; returns non-zero (in every thread)
-// if any poll gave up. Ends with a workgroup barrier.
-__device__ __forceinline__ int wait_head(const PathParams& p, const uint64_t* flags, int nch) {
+// if any poll gave up, and with `missing` (LDS, nch entries) records which
+// chunks' flags were still unset. Ends with a workgroup barrier.
+//
+// Ordering: the publishing item writes its words with device-coherent stores
+// (agent-scope relaxed atomics: performed at the device's coherence point,
+// not held in one XCD's L2), waits until every one of its threads has had
+// them acknowledged (s_waitcnt vmcnt(0), then a workgroup barrier), and only
+// then stores its flag the same way. A waiting thread polls the flag with
+// device-coherent loads and issues the loads of the published words only
+// after it has seen the flag (the loop exit depends on the loaded value),
+// again device-coherent, so they are served from the coherence point, which
+// already holds the words. No cache write-back or invalidation is needed
+// for these words; nothing else is exchanged between items of one launch.
+__device__ __forceinline__ int wait_head(const PathParams& p, const uint64_t* flags, int nch,
+                                         uint8_t* missing = nullptr) {
   int timed_out = 0;
   if ((int)threadIdx.x < nch) {
     int spins = 0;
@@ -382,8 +397,18 @@ __device__ __forceinline__ int wait_head(const PathParams& p, const uint64_t* fl
       }
       __builtin_amdgcn_s_sleep(1);
     }
+    if (missing != nullptr) missing[threadIdx.x] = (uint8_t)timed_out;
   }
-  return __syncthreads_or(timed_out);
+  // the same in every thread; returned as a scalar
+  return __builtin_amdgcn_readfirstlane(__syncthreads_or(timed_out));
+}
+
+// The head's first-digit histogram may hold counts added before item 0 of
+// the head cleared it (an item gave up waiting for item 0's flag): the
+// selection of this call recounts that digit itself (plain store; the
+// selection runs after a kernel boundary).
+__device__ __forceinline__ void mark_hist_bad(const PathParams& p, size_t head) {
+  if (threadIdx.x == 0) p.hist_bad[head] = p.epoch;
 }
 
 // Per-chunk statistics of one row, with a device-coherent load when another
@@ -450,7 +475,7 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
     if (c == 0) {
       const size_t head0 = (size_t)(b * p.hkv + h);
       uint32_t* top = p.top_hist + head0 * kSelHistWords;
-      for (int i = tid; i < kSelHistWords; i += kThreads)
+      for (int i = tid; i < kHistCleared; i += kThreads)
         __hip_atomic_store(&top[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       publish_item(p, p.flags + head0 * p.nchunk, 0);
     }
@@ -620,8 +645,11 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
     lds_barrier();
     if constexpr (ZERO_FIRST) {
       if (wait_head(p, p.flags + head * p.nchunk, 1)) {
-        // item 0 never published: the histograms are not to be trusted
-        for (int j = key0 + tid; j < kend; j += kThreads) pooled[j] = __builtin_nanf("");
+        // item 0 has not published that it cleared the histograms: adding
+        // now could be undone by its clearing, so this item adds nothing and
+        // the selection recounts the first digit from the pooled scores
+        mark_hist_bad(p, head);
+        return;
       }
     }
     uint32_t* top = p.top_hist + head * kSelHistWords;
@@ -643,10 +671,13 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
 // it waits), then pools and counts as the vote item does. The arithmetic of
 // every vote, normaliser and pooled value is the vote item's, in the same
 // order, so both paths give identical bits. Every wait is bounded: after
-// p.spin_limit polls (kSpinLimit unless the caller lowers it) the item gives
-// up and writes NaN scores, which the selection and any comparison expose;
-// the host only takes this path when the grid fits the device one workgroup
-// per CU, so the default bound is not reached.
+// p.spin_limit polls (kSpinLimit unless the caller lowers it) the item stops
+// waiting and computes the statistics of the chunks whose flags were still
+// unset itself, with the same code (so the same bits as their own items
+// write); the result does not depend on whether a wait gave up. The host
+// takes this path only when the grid fits the device one workgroup per CU,
+// so normally no wait gives up; when other work holds CUs the items still
+// finish, more slowly.
 
 template <int D>
 struct alignas(16) FusedSmem {
@@ -658,8 +689,39 @@ struct alignas(16) FusedSmem {
   } u;
   float lse[kFusedMaxRows];
   float s_chunk[kFusedChunk + 2 * kFusedMaxHalo];  // votes of keys kv0 ..
+  uint8_t missing[kThreads];                       // chunks whose flags a wait gave up on
 };
 static_assert(sizeof(FusedSmem<128>) <= 160 * 1024, "fused item LDS");
+
+// After a wait gave up: the statistics of every chunk in `missing` (LDS,
+// read after a barrier, so the same in every thread), computed with the
+// statistics pass's own code and written to that chunk's words with
+// device-coherent stores (identical bits to what the chunk's item writes,
+// so it does not matter which store lands last). `run` streams the keys
+// through two LDS tiles and `qbuf` stages the query rows. Ends when every
+// thread's stores are acknowledged and a barrier has passed, so the merge
+// that follows reads them.
+template <int D, int RTW, typename Run>
+__device__ __forceinline__ void recompute_missing_stats(const PathParams& p, const uint8_t* missing,
+                                                        int nch, unsigned char* qbuf,
+                                                        float2 (*wstats)[kMaxRowTilesPerWave * 32],
+                                                        Run&& run, int b, int h) {
+  for (int cc = 0; cc < nch; ++cc) {
+    // the same value in every thread: taken as a scalar, so the statistics
+    // code below keeps its uniform values in scalar registers
+    if (__builtin_amdgcn_readfirstlane((int)missing[cc]) == 0) continue;
+    // opaque copies of the indices, renewed every iteration: nothing derived
+    // from them is hoisted out of the loop or shared with the item's own
+    // statistics pass (either would keep registers live across the body)
+    int bb = b, hh = h;
+    asm volatile("" : "+s"(bb), "+s"(hh));
+    bf16x8 qf[RTW][D / 16];
+    score_stats_body<D, RTW, true, true, false>(p, qbuf, wstats, qf, run, bb, hh, cc);
+    __syncthreads();  // the tiles and wstats are reused by the next chunk
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
 static_assert(kTopBins * 4 <= KTile<128>::BYTES, "histogram in a key slot");
 
 template <int D>
@@ -709,7 +771,24 @@ __device__ __forceinline__ void snapkv_score_fused_item(const PathParams& p, Fus
     }
   }
   // wait for the statistics of every chunk of this head (bounded)
-  const int timed_out = wait_head(p, flags, nch);
+  if (wait_head(p, flags, nch, sm.missing)) {
+    // Some items have not published: their statistics are computed here.
+    // The stream needs two tile slots and the query slot, so this chunk's
+    // own tiles are reloaded into their slots afterwards (the halo block
+    // and the query fragments are unaffected).
+    if (__builtin_amdgcn_readfirstlane((int)sm.missing[0])) mark_hist_bad(p, head);
+    recompute_missing_stats<D, RTW>(
+        p, sm.missing, nch, sm.k[kFusedTiles - 1], sm.u.wstats,
+        [&](KeyStream<D>& ks, auto&& compute) {
+          ks.run(reinterpret_cast<unsigned char(*)[KTile<D>::BYTES]>(&sm.k[0][0]), compute,
+                 [](int) {});
+        },
+        b, h);
+    KeyStream<D> own{{}, {}, kbase, tstride, key0, min(key0 + p.chunk, L), true, true};
+    own.prefetch();
+    own.run_resident(sm.k, [](const unsigned char*, int) {});
+    __syncthreads();
+  }
 
   // lse of every row, exactly as the vote item merges it, from coherent loads
   const float2* part = p.part + head * p.nchunk * p.rows_pad;
@@ -837,9 +916,8 @@ __device__ __forceinline__ void snapkv_score_fused_item(const PathParams& p, Fus
   // snapkv_pool and the first radix digit, as in the vote item
   float* pooled = p.pooled + head * p.pooled_stride;
   for (int j = key0 + tid; j < kend; j += kThreads) {
-    float c_j = pool_value([&](int u) { return sm.s_chunk[u - kv0]; }, j, P, p.kernel,
-                           p.pool_mode);
-    if (timed_out) c_j = __builtin_nanf("");
+    const float c_j = pool_value([&](int u) { return sm.s_chunk[u - kv0]; }, j, P, p.kernel,
+                                 p.pool_mode);
     pooled[j] = c_j;
     lds_count(top, order_key(c_j) >> kTopShift);
   }
@@ -857,12 +935,15 @@ __device__ __forceinline__ void snapkv_score_fused_item(const PathParams& p, Fus
 // fused item, then the vote item as in snapkv_score_vote with coherent loads
 // of the statistics; its keys stream through the ring again (this CU read
 // them moments before, so mostly from the caches). The same code in the same
-// order as the two kernels, so identical bits. On timeout the item's pooled
-// scores are NaN.
+// order as the two kernels, so identical bits. When the wait gives up, the
+// item computes the missing chunks' statistics itself, as the fused item does.
 template <int D, int RTW>
-union FusedStreamSmem {
-  StatsSmem<D> st;
-  VoteSmem<D> vt;
+struct FusedStreamSmem {
+  union {
+    StatsSmem<D> st;
+    VoteSmem<D> vt;
+  };
+  uint8_t missing[kThreads];  // chunks whose flags the wait gave up on
 };
 
 template <int D, int RTW>
@@ -883,14 +964,14 @@ __device__ __forceinline__ void snapkv_score_fused_stream_item(const PathParams&
   uint64_t* flags = p.flags + head * p.nchunk;
   publish_item(p, flags, c);
   if (c * p.chunk >= P) return;  // a chunk of window keys only: nothing to vote
-  const int timed_out = wait_head(p, flags, nch);  // its barrier also frees the LDS
-  snapkv_score_vote_item<D, RTW, false, true>(p, sm.vt, b, h, c);
-  if (timed_out) {
-    __syncthreads();
-    float* pooled = p.pooled + head * p.pooled_stride;
-    const int key0 = c * p.chunk, kend = min(key0 + p.chunk, P);
-    for (int j = key0 + (int)threadIdx.x; j < kend; j += kThreads) pooled[j] = __builtin_nanf("");
+  if (wait_head(p, flags, nch, sm.missing)) {  // its barrier also frees the LDS
+    if (__builtin_amdgcn_readfirstlane((int)sm.missing[0])) mark_hist_bad(p, head);
+    recompute_missing_stats<D, RTW>(
+        p, sm.missing, nch, sm.st.ring[1], sm.st.wstats,
+        [&](KeyStream<D>& ks, auto&& compute) { ks.run(sm.st.ring, compute, [](int) {}); }, b,
+        h);
   }
+  snapkv_score_vote_item<D, RTW, false, true>(p, sm.vt, b, h, c);
 }
 
 }  // namespace snapkv

@@ -59,15 +59,17 @@ struct alignas(16) SelectSmem {
   uint32_t rep[2][kHistWords];  // replicated histograms of digits 2 and 3
   uint32_t rowtot[kWaves];                   // histogram row totals (find)
   uint32_t sh_bin, sh_need, sh_count;
+  uint32_t sh_lost;  // a search found no bin holding the threshold
 };
 
 // Where a selection puts its result: the global count table and threshold
 // (the gather reads them after the kernel boundary), or, for a selection
 // that runs inside a gather item, a count table in LDS and the threshold
-// in `thr` (tau, need, settled).
+// in `thr` (tau, need, settled, lost: 1 when a radix search found no bin
+// holding the threshold, which a consistent histogram never causes).
 struct SelectOut {
   uint32_t* table;  // [nseg][2]
-  uint32_t* thr;    // [3]
+  uint32_t* thr;    // [4]
 };
 
 // Keys of slabs slab0 .. slab0+NS-1 for this thread; 0 past P. Loads are
@@ -108,6 +110,9 @@ __device__ __forceinline__ void clear_hist(uint32_t* h, int first) {
 // .. +3. Row totals are exchanged through LDS; the wave holding the
 // threshold then finds it with its lane scan. Requires 1 <= need <= total.
 // Contains two barriers; the result is valid after the second.
+// When no bin holds it (need outside [1, total]: an inconsistent histogram)
+// the result is bin 0 with need 1 and count 0, and sm.sh_lost is set; a
+// consistent histogram leaves sm.sh_lost as it was.
 template <typename Counts, typename Smem>
 __device__ __forceinline__ void find_bin(Counts&& counts, uint32_t need, Smem& sm) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -117,7 +122,17 @@ __device__ __forceinline__ void find_bin(Counts&& counts, uint32_t need, Smem& s
   const uint32_t incl = wave_incl_scan(local);  // lanes <= lane of this row
   const uint32_t total = wave_total(incl);
   if (lane == 0) sm.rowtot[wave] = total;
+  if (threadIdx.x == 0) {  // overwritten below by the thread that finds the bin
+    sm.sh_bin = 0u;
+    sm.sh_need = 1u;
+    sm.sh_count = 0u;
+  }
   __syncthreads();
+  {
+    uint32_t all = 0;
+    for (int w = 0; w < kWaves; ++w) all += sm.rowtot[w];
+    if (threadIdx.x == 0 && (need < 1u || need > all)) sm.sh_lost = 1u;
+  }
   uint32_t above = 0;  // keys in the rows above this one
   for (int w = kWaves - 1; w > wave; --w) above += sm.rowtot[w];
   if (above < need && need <= above + total) {  // the threshold is in this row
@@ -159,8 +174,11 @@ __device__ __forceinline__ void select_head(const PathParams& p, SelectSmem& sm,
 
   // digit 1: the histogram the vote kernel accumulated. Its row is loaded
   // before the keys, so the first search waits for it alone while the keys
-  // are still in flight.
-  const u32x4 top4 = *reinterpret_cast<const u32x4*>(top + 256 * wave + 4 * lane);
+  // are still in flight. When the score kernel marked it untrustworthy for
+  // this call (hist_bad), the digit is recounted here from the keys.
+  const bool recount = p.hist_bad[head] == p.epoch;
+  u32x4 top4 = u32x4{0u, 0u, 0u, 0u};
+  if (!recount) top4 = *reinterpret_cast<const u32x4*>(top + 256 * wave + 4 * lane);
   asm volatile("" ::: "memory");  // the histogram loads stay older than the keys'
   uint32_t key[NS][4];
   if (RESIDENT) load_keys<NS>(key, src, P, 0);
@@ -168,11 +186,7 @@ __device__ __forceinline__ void select_head(const PathParams& p, SelectSmem& sm,
   // (the search's barriers order the clearing before the counting)
   clear_hist(sm.rep[0], 0);
   clear_hist(sm.rep[1], 0);
-  find_bin([&] { return top4; }, m, sm);
-  uint32_t prefix = sm.sh_bin << kTopShift;  // resolved high bits of tau
-  uint32_t need = sm.sh_need;
-  bool settled = need == sm.sh_count;  // the whole threshold bin is kept
-  int low = kTopShift;                 // bits below the resolved prefix
+  if (tid == 0) sm.sh_lost = 0u;
 
   // f(jb, keys) over every float4 group of every batch, in batch order:
   // keys[e] is position jb + e
@@ -183,6 +197,23 @@ __device__ __forceinline__ void select_head(const PathParams& p, SelectSmem& sm,
       for (int s = 0; s < NS; ++s) f((bt * NS + s) * kSlab + 4 * tid, key[s]);
     }
   };
+  if (recount) {
+    __syncthreads();  // the clearing is done
+    visit_groups([&](int jb, const uint32_t(&k4)[4]) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (jb + e < P) lds_count(sm.rep[1], k4[e] >> kTopShift);
+    });
+    __syncthreads();
+    top4 = *reinterpret_cast<const u32x4*>(sm.rep[1] + 256 * wave + 4 * lane);
+    __syncthreads();  // every row is read before the buffer is cleared again
+    clear_hist(sm.rep[1], 0);  // for digit 3; ordered by the search's barriers
+  }
+  find_bin([&] { return top4; }, m, sm);
+  uint32_t prefix = sm.sh_bin << kTopShift;  // resolved high bits of tau
+  uint32_t need = sm.sh_need;
+  bool settled = need == sm.sh_count;  // the whole threshold bin is kept
+  int low = kTopShift;                 // bits below the resolved prefix
   // one more digit of `bits` bits below the resolved prefix, counted into
   // histogram buffer `buf` (cleared at the start); the threshold bin is found
   auto digit = [&](int buf, int bits) {
@@ -255,6 +286,7 @@ __device__ __forceinline__ void select_head(const PathParams& p, SelectSmem& sm,
     out.thr[0] = tau;
     out.thr[1] = need;
     out.thr[2] = settled ? 1u : 0u;
+    out.thr[3] = sm.sh_lost;
   }
 }
 
@@ -266,6 +298,7 @@ struct alignas(16) SliceSmem {
   uint32_t rep[kSliceReplicas * kRepStride];
   uint32_t rowtot[kWaves];
   uint32_t sh_bin, sh_need, sh_count;
+  uint32_t sh_lost;
 };
 
 // The threshold as far as `digits` radix digits, from the head's global
@@ -279,9 +312,10 @@ struct Threshold {
   bool settled;
 };
 
+// `d1` is the first digit's histogram (the head's, in global memory or LDS).
 template <typename Smem>
-__device__ __forceinline__ Threshold resolve_digits(const uint32_t* hist, int digits, uint32_t m,
-                                                    Smem& sm) {
+__device__ __forceinline__ Threshold resolve_digits(const uint32_t* hist, const uint32_t* d1,
+                                                    int digits, uint32_t m, Smem& sm) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   Threshold t{0u, m, 32, false};
 #pragma unroll
@@ -289,7 +323,7 @@ __device__ __forceinline__ Threshold resolve_digits(const uint32_t* hist, int di
     if (d >= digits || t.settled) break;
     const int shift = d == 0 ? kTopShift : (d == 1 ? 10 : 0);
     const int nbins = d == 2 ? 1024 : 2048;
-    const uint32_t* hd = hist + 2048 * d;
+    const uint32_t* hd = d == 0 ? d1 : hist + (d == 1 ? kHistD2 : kHistD3);
     find_bin(
         [&] {
           const int i = 256 * wave + 4 * lane;
@@ -338,14 +372,44 @@ __device__ __forceinline__ void select_digit_slice(const PathParams& p, SliceSme
   const size_t head = (size_t)(b * p.hkv + h);
   uint32_t* hist = p.top_hist + head * kSelHistWords;
   const int tid = threadIdx.x;
+  const float* src = p.pooled + head * p.pooled_stride;
+  const bool recount = p.hist_bad[head] == p.epoch;
   uint32_t key[2][4];
-  load_slice_keys(key, p.pooled + head * p.pooled_stride, P, s0);
+  load_slice_keys(key, src, P, s0);
   u32x4* r4 = reinterpret_cast<u32x4*>(sm.rep);
-  for (int i = tid; i < kSliceReplicas * kRepStride / 4; i += kThreads)
-    r4[i] = u32x4{0u, 0u, 0u, 0u};
+  auto clear = [&] {
+    for (int i = tid; i < kSliceReplicas * kRepStride / 4; i += kThreads)
+      r4[i] = u32x4{0u, 0u, 0u, 0u};
+  };
+  clear();
+  if (tid == 0) sm.sh_lost = 0u;
+  const uint32_t* d1 = hist + (recount && DIGIT == 3 ? kHistFix : kHistD1);
+  if (DIGIT == 2 && recount) {
+    // the score kernel's first-digit counts are not to be trusted for this
+    // call: every slice recounts that digit over the whole prefix, and
+    // slice 0 leaves it for the later passes
+    __syncthreads();
+    for (int a = 0; a < P; a += kSliceKeys) {
+      uint32_t k2[2][4];
+      load_slice_keys(k2, src, P, a);
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (a + g * kSlab + 4 * tid + e < P) lds_count(sm.rep, k2[g][e] >> kTopShift);
+    }
+    __syncthreads();
+    if (sl == 0)
+      for (int i = tid; i < kTopBins; i += kThreads) hist[kHistFix + i] = sm.rep[i];
+    d1 = sm.rep;
+  }
   // (the search's barriers also order the clearing before the counting)
-  const Threshold t = resolve_digits(hist, DIGIT - 1, (uint32_t)(p.budget - p.window), sm);
+  const Threshold t = resolve_digits(hist, d1, DIGIT - 1, (uint32_t)(p.budget - p.window), sm);
   if (t.settled) return;
+  if (DIGIT == 2 && recount) {
+    clear();  // after the search's reads of the recount; its barrier orders this
+    __syncthreads();
+  }
   uint32_t* hrep = sm.rep + (tid % kSliceReplicas) * kRepStride;
 #pragma unroll
   for (int g = 0; g < 2; ++g)
@@ -374,7 +438,10 @@ __device__ __forceinline__ void select_count_slice(const PathParams& p, SliceSme
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t key[2][4];
   load_slice_keys(key, p.pooled + head * p.pooled_stride, P, s0);
-  const Threshold t = resolve_digits(p.top_hist + head * kSelHistWords, 3,
+  const uint32_t* hist = p.top_hist + head * kSelHistWords;
+  const bool recount = p.hist_bad[head] == p.epoch;
+  if (tid == 0) sm.sh_lost = 0u;
+  const Threshold t = resolve_digits(hist, hist + (recount ? kHistFix : kHistD1), 3,
                                      (uint32_t)(p.budget - p.window), sm);
   const uint32_t tau = t.prefix;  // settled: keep keys >= prefix; else > tau, and `need` == tau
   const int nseg = (P + kSegment - 1) / kSegment;
@@ -400,6 +467,7 @@ __device__ __forceinline__ void select_count_slice(const PathParams& p, SliceSme
     meta[0] = tau;
     meta[1] = t.need;
     meta[2] = t.settled ? 1u : 0u;
+    meta[3] = sm.sh_lost;
   }
 }
 

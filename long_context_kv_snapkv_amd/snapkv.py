@@ -77,6 +77,10 @@ def load_library():
     lib.snapkv_compress_from_lse.argtypes = [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _pi32, _i32,
                                              _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
     lib.snapkv_compress_from_lse.restype = _i32
+    lib.snapkv_compress_with_scores.argtypes = [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _pi32,
+                                                _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
+                                                _i32, _vp, _sz, _vp]
+    lib.snapkv_compress_with_scores.restype = _i32
     lib.snapkv_compress_int4.argtypes = [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _pi32, _i32, _vp,
                                          _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                          _vp]
@@ -271,6 +275,52 @@ def snapkv_compress_from_lse(q_win: torch.Tensor, k: torch.Tensor, v: torch.Tens
         kernel_size, pool_mode_code(pool_mode), budget, _ptr(out_k), _ptr(out_v), _ptr(out_idx),
         _ptr(workspace), workspace.numel(), _stream(stream, dev)))
     return out_k, out_v, out_idx
+
+
+def snapkv_compress_with_scores(q_win: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                seq_lens: Sequence[int], window: int, kernel_size: int,
+                                pool_mode, budget: int, *,
+                                window_lse: Optional[torch.Tensor] = None,
+                                out_k: Optional[torch.Tensor] = None,
+                                out_v: Optional[torch.Tensor] = None,
+                                out_idx: Optional[torch.Tensor] = None,
+                                out_scores: Optional[torch.Tensor] = None,
+                                workspace: Optional[torch.Tensor] = None, stream=None):
+    """snapkv_compress (or, with window_lse, snapkv_compress_from_lse) that
+    also returns the pooled scores its selection read: (out_k, out_v,
+    out_idx, scores), scores float32 [batch, H_kv, scores_len] with zeros for
+    prompts kept whole; see include/snapkv.h."""
+    lib = load_library()
+    _check_tensor("q_win", q_win, 4)
+    _check_tensor("k", k, 3)
+    _check_tensor("v", v, 3)
+    arr, vals = _lens(seq_lens)
+    batch, hq, hkv, d, w = _shapes(q_win, k, vals)
+    if v.shape != k.shape:
+        raise ValueError("k and v shapes differ")
+    if w != window:
+        raise ValueError(f"q_win holds {w} window rows but window={window}")
+    if window_lse is not None:
+        _check_tensor("window_lse", window_lse, 3, torch.float32)
+        if tuple(window_lse.shape) != (batch, hq, window):
+            raise ValueError("window_lse must be [batch, H_q, W]")
+    dev = q_win.device
+    out_k, out_v, out_idx = _outputs(batch, hkv, budget, d, dev, out_k, out_v, out_idx)
+    if out_scores is None:
+        out_scores = torch.empty((batch, hkv, max(1, max(vals) - window)), dtype=torch.float32,
+                                 device=dev)
+    _check_tensor("out_scores", out_scores, 3, torch.float32)
+    if tuple(out_scores.shape[:2]) != (batch, hkv):
+        raise ValueError("out_scores must be [batch, H_kv, scores_len]")
+    if workspace is None:
+        workspace = new_workspace(hq, hkv, d, vals, window, dev)
+    _check(lib.snapkv_compress_with_scores(
+        batch, hq, hkv, d, _ptr(q_win), _ptr(k), _ptr(v), arr, window,
+        _ptr(window_lse) if window_lse is not None else None, kernel_size,
+        pool_mode_code(pool_mode), budget, _ptr(out_k), _ptr(out_v), _ptr(out_idx),
+        _ptr(out_scores), out_scores.shape[2], _ptr(workspace), workspace.numel(),
+        _stream(stream, dev)))
+    return out_k, out_v, out_idx, out_scores
 
 
 def snapkv_compress_int4(q_win: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

@@ -2,7 +2,10 @@
 and compare with the oracle under the acceptance rules.
 
 Acceptance (all per prompt b and KV head h):
-  scores   |g_j - o_j| <= 1e-3 * |o_j| + 1e-6 * max_j o_j        (pooled scores)
+  scores   |g_j - o_j| <= 1e-3 * |o_j| + 1e-6 * max_j o_j        (pooled scores),
+           for the scores the compression itself selected from (exported by
+           snapkv_compress_with_scores from whichever scoring kernels the
+           shape takes) and for the two-kernel export snapkv_window_scores
   indices  with o sorted descending, tau = o_(m), tau' = o_(m+1),
            tol = 1e-3 * tau + 1e-6 * max o: every j with o_j > tau' + tol is
            kept and every j with o_j < tau - tol is not; when tau - tau' > tol
@@ -38,24 +41,34 @@ def upload(x):
     return bits_to_device(x.q_win), bits_to_device(x.k), bits_to_device(x.v)
 
 
+def _same(a, b):
+    """Bitwise equality of two device tensors."""
+    if a.dtype == torch.bfloat16:
+        a, b = a.view(torch.int16), b.view(torch.int16)
+    return torch.equal(a, b)
+
+
 def run_gpu(x, window, kernel, pool, budget, dev_inputs=None, workspace=None):
-    """snapkv_compress, snapkv_compress_staged on the same inputs, and the
-    exported scores. The two compress calls must agree bit for bit."""
+    """snapkv_compress_with_scores (the compression plus the pooled scores it
+    selected from), snapkv_compress and snapkv_compress_staged on the same
+    inputs (all three must agree bit for bit), and the two-kernel score
+    export snapkv_window_scores."""
     q, k, v = dev_inputs if dev_inputs is not None else upload(x)
     lens = x.seq_lens.tolist()
     hq, hkv, d = q.shape[1], k.shape[1], k.shape[2]
     ws = workspace if workspace is not None else skv.new_workspace(hq, hkv, d, lens, window)
-    out_k, out_v, out_idx = skv.snapkv_compress(q, k, v, lens, window, kernel, pool, budget,
-                                                workspace=ws)
+    out_k, out_v, out_idx, sel = skv.snapkv_compress_with_scores(
+        q, k, v, lens, window, kernel, pool, budget, workspace=ws)
+    pk, pv, pi = skv.snapkv_compress(q, k, v, lens, window, kernel, pool, budget, workspace=ws)
     sk, sv, si = skv.snapkv_compress(q, k, v, lens, window, kernel, pool, budget, staged=True)
     scores = skv.snapkv_window_scores(q, k, lens, window, kernel, pool)
     torch.cuda.synchronize()
-    res = dict(out_k=bits_from_device(out_k), out_v=bits_from_device(out_v),
-               out_idx=out_idx.cpu().numpy(), scores=scores.cpu().numpy().astype(np.float64))
-    np.testing.assert_array_equal(res["out_idx"], si.cpu().numpy())
-    np.testing.assert_array_equal(res["out_k"], bits_from_device(sk))
-    np.testing.assert_array_equal(res["out_v"], bits_from_device(sv))
-    return res
+    for a, b in ((out_k, pk), (out_v, pv), (out_idx, pi), (out_k, sk), (out_v, sv),
+                 (out_idx, si)):
+        assert _same(a, b), "compress entry points disagree"
+    return dict(out_k=bits_from_device(out_k), out_v=bits_from_device(out_v),
+                out_idx=out_idx.cpu().numpy(), scores=scores.cpu().numpy().astype(np.float64),
+                sel_scores=sel.cpu().numpy().astype(np.float64))
 
 
 def check_scores(gpu_scores, ref_pooled, seq_lens, window):
@@ -75,6 +88,29 @@ def check_scores(gpu_scores, ref_pooled, seq_lens, window):
             f"prompt {b}: {bad.sum()} scores out of tolerance, e.g. head/pos "
             f"{np.argwhere(bad)[:3].tolist()} gpu={g[bad][:3]} oracle={o[bad][:3]}")
         assert (gpu_scores[b, :, p:] == 0).all()
+    return worst
+
+
+def check_selected_scores(sel_scores, ref_pooled, seq_lens, window, budget):
+    """The scores the compression selected from (snapkv_compress_with_scores):
+    within tolerance of the oracle's pooled scores for every compressed
+    prompt, zero for prompts kept whole and past P."""
+    worst = 0.0
+    for b, length in enumerate(seq_lens):
+        if length <= budget:
+            assert (sel_scores[b] == 0).all(), f"prompt {b} kept whole but has scores"
+            continue
+        p = length - window
+        o = ref_pooled[b]
+        g = sel_scores[b, :, :p]
+        bound = REL_TOL * np.abs(o) + ABS_FRAC * o.max(axis=1, keepdims=True)
+        err = np.abs(g - o)
+        worst = max(worst, float((err / np.maximum(bound, 1e-300)).max()))
+        bad = err > bound
+        assert not bad.any(), (
+            f"prompt {b}: {bad.sum()} selected-from scores out of tolerance, e.g. head/pos "
+            f"{np.argwhere(bad)[:3].tolist()} gpu={g[bad][:3]} oracle={o[bad][:3]}")
+        assert (sel_scores[b, :, p:] == 0).all()
     return worst
 
 
@@ -123,13 +159,15 @@ def check_structure_and_gather(res, x, window, budget):
 
 
 def check_topk_exact(res, seq_lens, window, budget):
+    """The oracle's selection rule applied to the scores the compression
+    selected from reproduces its index list exactly."""
     m = budget - window
     for b, length in enumerate(seq_lens):
         if length <= budget:
             continue
         p = length - window
         for h in range(res["out_idx"].shape[1]):
-            sel = oracle.select_prefix(res["scores"][b, h, :p], m)
+            sel = oracle.select_prefix(res["sel_scores"][b, h, :p], m)
             np.testing.assert_array_equal(res["out_idx"][b, h, :m], sel)
 
 
@@ -142,6 +180,12 @@ def full_check(x, window, kernel, pool, budget, ref=None, res=None):
         ref = oracle.compress(x.q_win, x.k, x.v, lens, window, kernel, pool, budget)
     pooled = [p for p in ref.pooled]
     worst = check_scores(res["scores"], pooled, lens, window)
+    worst = max(worst, check_selected_scores(res["sel_scores"], pooled, lens, window, budget))
+    # the scoring forms (one launch or two kernels) give the same bits
+    for b, length in enumerate(lens):
+        if length > budget:
+            np.testing.assert_array_equal(res["sel_scores"][b, :, :length - window],
+                                          res["scores"][b, :, :length - window])
     check_structure_and_gather(res, x, window, budget)
     check_topk_exact(res, lens, window, budget)
     exact = check_index_sets(res["out_idx"], pooled, lens, window, budget)
@@ -177,13 +221,18 @@ def torch_window_lse(q, k, seq_lens, window):
 
 
 def run_gpu_from_lse(x, window, kernel, pool, budget, lse):
-    """snapkv_compress_from_lse on x with normalisers lse (float32 numpy or
-    device tensor), as numpy outputs."""
+    """snapkv_compress_with_scores with normalisers lse (float32 numpy or
+    device tensor) and snapkv_compress_from_lse on the same inputs (they
+    must agree bit for bit), as numpy outputs with the selected-from scores."""
     q, k, v = upload(x)
     t = lse if isinstance(lse, torch.Tensor) else torch.from_numpy(
         np.ascontiguousarray(lse, dtype=np.float32)).cuda()
-    out_k, out_v, out_idx = skv.snapkv_compress_from_lse(
-        q, k, v, x.seq_lens.tolist(), window, t, kernel, pool, budget)
+    lens = x.seq_lens.tolist()
+    out_k, out_v, out_idx, sel = skv.snapkv_compress_with_scores(
+        q, k, v, lens, window, kernel, pool, budget, window_lse=t)
+    pk, pv, pi = skv.snapkv_compress_from_lse(q, k, v, lens, window, t, kernel, pool, budget)
     torch.cuda.synchronize()
+    for a, b in ((out_k, pk), (out_v, pv), (out_idx, pi)):
+        assert _same(a, b), "compress entry points disagree"
     return dict(out_k=bits_from_device(out_k), out_v=bits_from_device(out_v),
-                out_idx=out_idx.cpu().numpy())
+                out_idx=out_idx.cpu().numpy(), sel_scores=sel.cpu().numpy().astype(np.float64))

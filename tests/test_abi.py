@@ -22,8 +22,9 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = skv.header_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     assert "snapkv_compress_staged" in names
+    assert "snapkv_compress_with_scores" in names
     assert "snapkv_compress_from_lse" in names
     for name in names:
         assert hasattr(lib, name), name
@@ -125,6 +126,23 @@ def test_compress_from_lse_validation(lib):
     assert call(FAKE, kernel=4) == 1
     # a 4-byte aligned normaliser buffer passes; the undersized workspace stops the call
     assert call(FAKE + 4) == 3
+
+
+def test_compress_with_scores_validation(lib):
+    lens = (ctypes.c_int32 * 1)(100)
+
+    def call(sc=FAKE, slen=92, lse=None, ws_bytes=1):
+        return lib.snapkv_compress_with_scores(1, 4, 2, 128, FAKE, FAKE, FAKE, lens, 8, lse, 5,
+                                               0, 32, FAKE, FAKE, FAKE, sc, slen, FAKE,
+                                               ws_bytes, None)
+
+    assert call(sc=None) == 1 and "out_scores" in skv.snapkv_last_error()
+    assert call(sc=FAKE + 4) == 1 and "out_scores" in skv.snapkv_last_error()
+    assert call(slen=91) == 1 and "scores_len" in skv.snapkv_last_error()
+    assert call(lse=FAKE + 2) == 1 and "window_lse" in skv.snapkv_last_error()
+    # valid arguments: the undersized workspace stops the call
+    assert call() == 3
+    assert call(lse=FAKE + 4) == 3
 
 
 def test_compress_int4_validation(lib):

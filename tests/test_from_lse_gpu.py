@@ -14,8 +14,8 @@ import pytest
 import torch
 
 import oracle
-from parity import (check_index_sets, check_structure_and_gather, run_gpu,
-                    run_gpu_from_lse, torch_window_lse, upload)
+from parity import (check_index_sets, check_selected_scores, check_structure_and_gather,
+                    check_topk_exact, run_gpu, run_gpu_from_lse, torch_window_lse, upload)
 from synth import WORKLOADS, make_custom, make_layer
 
 pytestmark = pytest.mark.gpu
@@ -47,8 +47,11 @@ def _check(x, window, kernel, pool, budget, lse32):
     res = run_gpu_from_lse(x, window, kernel, pool, budget, lse32)
     ref = oracle.compress(x.q_win, x.k, x.v, x.seq_lens.tolist(), window, kernel, pool,
                           budget, lse=lse32.astype(np.float64))
+    lens = x.seq_lens.tolist()
     check_structure_and_gather(res, x, window, budget)
-    exact = check_index_sets(res["out_idx"], ref.pooled, x.seq_lens.tolist(), window, budget)
+    check_selected_scores(res["sel_scores"], ref.pooled, lens, window, budget)
+    check_topk_exact(res, lens, window, budget)
+    exact = check_index_sets(res["out_idx"], ref.pooled, lens, window, budget)
     return res, ref, exact
 
 
@@ -99,6 +102,10 @@ def test_llama3_8b_16k_with_device_normalisers():
     res = run_gpu_from_lse(x, w.window, w.kernel, w.pool, w.budget, lse)
     ref = oracle.compress(x.q_win, x.k, x.v, lens, w.window, w.kernel, w.pool, w.budget)
     check_structure_and_gather(res, x, w.window, w.budget)
+    # the device normalisers are float32 roundings of the exact ones, far
+    # inside the score tolerance
+    check_selected_scores(res["sel_scores"], ref.pooled, lens, w.window, w.budget)
+    check_topk_exact(res, lens, w.window, w.budget)
     # max pooling leaves plateaus: ties at the threshold are common, and the
     # band rule decides every position outside them
     check_index_sets(res["out_idx"], ref.pooled, lens, w.window, w.budget)
@@ -148,6 +155,8 @@ def test_llama3_70b_128k_with_device_normalisers():
     res = run_gpu_from_lse(x, w.window, w.kernel, w.pool, w.budget, lse)
     ref = oracle.compress(x.q_win, x.k, x.v, lens, w.window, w.kernel, w.pool, w.budget)
     check_structure_and_gather(res, x, w.window, w.budget)
+    check_selected_scores(res["sel_scores"], ref.pooled, lens, w.window, w.budget)
+    check_topk_exact(res, lens, w.window, w.budget)
     check_index_sets(res["out_idx"], ref.pooled, lens, w.window, w.budget)
 
 
@@ -175,3 +184,25 @@ def test_vote_clears_histograms_itself_identically(lens, hq, hkv, d, window, ker
     for ta, tb in zip(a, b):
         assert torch.equal(ta.view(torch.int16) if ta.dtype == torch.bfloat16 else ta,
                            tb.view(torch.int16) if tb.dtype == torch.bfloat16 else tb)
+
+
+@needs_gpu
+@pytest.mark.parametrize("lens,hq,hkv,d,window,kernel,pool,budget", [
+    ([3000], 32, 8, 128, 32, 7, "max", 512),
+    ([64, 300, 65, 5, 1000], 8, 2, 128, 32, 5, "avg", 96),
+    ([40000], 8, 2, 128, 16, 7, "max", 2048),
+])
+def test_vote_gives_up_on_the_clearing_with_identical_results(lens, hq, hkv, d, window, kernel,
+                                                               pool, budget, monkeypatch):
+    # with the vote kernel clearing the histograms itself, an item that gives
+    # up waiting for item 0's flag adds no counts and marks the head for a
+    # recount of the first digit in the selection: forced from the host with
+    # a zero poll bound, every output bit equals the normal call
+    x = make_custom(lens, hq, hkv, d, window, seed=sum(lens) % 79)
+    lse32 = _oracle_lse_f32(x, window, budget)
+    print(f"[from_lse] forced give-up {lens}", flush=True)
+    a = run_gpu_from_lse(x, window, kernel, pool, budget, lse32)
+    monkeypatch.setenv("SNAPKV_SPIN_LIMIT", "0")
+    b, ref, _ = _check(x, window, kernel, pool, budget, lse32)
+    for key in a:
+        np.testing.assert_array_equal(a[key], b[key])

@@ -321,26 +321,46 @@ def test_cooperative_launch_gives_identical_bits(monkeypatch):
                            tb.view(torch.int16) if tb.dtype == torch.bfloat16 else tb)
 
 
+GIVE_UP = [
+    # (workload name or custom shape): fused resident scoring with the
+    # selection in the gather (16K), fused streaming scoring (32K), and
+    # prefixes past the register-resident selection, whose sliced selection
+    # then recounts the first digit over the whole prefix
+    "llama3_8b_16k",
+    "llama3_8b_32k_x32",
+    ([40000], 8, 2, 128, 16, 7, "max", 2048),
+    ([70000], 8, 2, 128, 16, 5, "avg", 1024),
+]
+
+
 @needs_gpu
-@pytest.mark.parametrize("name", ["llama3_8b_16k", "llama3_8b_32k_x32"])
-def test_fused_wait_gives_up_and_the_call_completes(name, monkeypatch):
-    # the fused score kernels' wait for the other items of a head is
-    # bounded; with the bound forced to zero polls from the host, items that
-    # find a flag unset give up (their pooled scores become NaN) and every
-    # kernel still exits: the call completes and its output keeps its
-    # structure (ascending kept positions, window last, bit-copied rows)
-    from parity import bits_from_device, check_structure_and_gather
-    w = WORKLOADS[name]
-    x = make_layer(w)
-    q, k, v = upload(x)
+@pytest.mark.parametrize("case", GIVE_UP, ids=["16k", "32k", "resident_sliced", "stream_sliced"])
+def test_fused_wait_gives_up_with_identical_results(case, monkeypatch):
+    # the fused score kernels' wait for the other items of a head is bounded;
+    # with the bound forced to zero polls from the host, an item gives up at
+    # its first look at an unset flag, computes those chunks' statistics
+    # itself, and marks the head's first-digit histogram for a recount when
+    # item 0's clearing was not seen. Every output bit, the selected-from
+    # scores included, must equal the call in which nobody gave up, and the
+    # whole result must pass the oracle comparison.
+    if isinstance(case, str):
+        w = WORKLOADS[case]
+        x = make_layer(w)
+        window, kernel, pool, budget = w.window, w.kernel, w.pool, w.budget
+        hq, hkv, d = w.h_q, w.h_kv, w.head_dim
+    else:
+        lens, hq, hkv, d, window, kernel, pool, budget = case
+        x = make_custom(lens, hq, hkv, d, window, seed=sum(lens) % 71)
     lens = x.seq_lens.tolist()
-    assert skv.snapkv_score_kernels(w.h_q, w.h_kv, w.head_dim, lens, w.window, w.kernel) != 2
+    assert skv.snapkv_score_kernels(hq, hkv, d, lens, window, kernel) != 2
+    dev = upload(x)
+    print(f"[parity] forced give-up {lens}", flush=True)
+    a = run_gpu(x, window, kernel, pool, budget, dev)
     monkeypatch.setenv("SNAPKV_SPIN_LIMIT", "0")
-    print(f"[parity] forced give-up {name}", flush=True)
-    ok, ov, oi = skv.snapkv_compress(q, k, v, lens, w.window, w.kernel, w.pool, w.budget)
-    torch.cuda.synchronize()
-    res = dict(out_k=bits_from_device(ok), out_v=bits_from_device(ov), out_idx=oi.cpu().numpy())
-    check_structure_and_gather(res, x, w.window, w.budget)
+    b = run_gpu(x, window, kernel, pool, budget, dev)
+    for key in a:
+        np.testing.assert_array_equal(a[key], b[key])
+    full_check(x, window, kernel, pool, budget, res=b)
 
 
 @needs_gpu
