@@ -191,6 +191,36 @@ int32_t snapkv_gather_selects(int32_t batch, int32_t num_q_heads,
                               int32_t budget, int32_t* fused);
 
 /*
+ * snapkv_compress for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * no workspace argument; the intermediates go to a fixed scratch area of
+ * SNAPKV_STATIC_SCRATCH_BYTES inside the library, one per device, held from
+ * the first call on that device until the process ends. The call allocates
+ * nothing (no hipMalloc, no allocating library routine); the caller still
+ * passes the inputs and outputs, as for snapkv_compress. Results are
+ * identical to snapkv_compress's. The area needs no clearing: every word a
+ * call reads is written by that call first, or only counts when it carries
+ * the call's own mark.
+ * All calls on one device share its area: calls that overlap in time on one
+ * device (two streams, two threads) race and give undefined results; the
+ * caller serialises them.
+ * Errors as for snapkv_compress; SNAPKV_ERR_WORKSPACE when the shape needs
+ * more scratch than SNAPKV_STATIC_SCRATCH_BYTES (snapkv_workspace_size gives
+ * the need; e.g. 5.3 MB for one 70B-shaped layer at 131072 tokens, 11 MB for
+ * eight 8B-shaped prompts of up to 32768 tokens), checked before any HIP
+ * call; SNAPKV_ERR_HIP when the area's address cannot be looked up.
+ */
+#define SNAPKV_STATIC_SCRATCH_BYTES (32u << 20)
+
+int32_t snapkv_compress_static(int32_t batch, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim,
+                               const void* q_win, const void* k, const void* v,
+                               const int32_t* seq_lens, int32_t window,
+                               int32_t kernel_size, int32_t pool_mode,
+                               int32_t budget, void* out_k, void* out_v,
+                               int32_t* out_idx, void* stream);
+
+/*
  * snapkv_compress (window_lse NULL) or snapkv_compress_from_lse (window_lse
  * as there) that also hands out the pooled scores its selection read, for
  * checking the path's scores against a reference (the scores of step 2 above

@@ -17,6 +17,7 @@ from .snapkv import (  # noqa: F401
     SNAPKV_OK,
     SNAPKV_POOL_AVG,
     SNAPKV_POOL_MAX,
+    SNAPKV_STATIC_SCRATCH_BYTES,
     SnapKVError,
     SnapKVLibraryMissing,
     compress,
@@ -28,6 +29,7 @@ from .snapkv import (  # noqa: F401
     snapkv_compress_fp8,
     snapkv_compress_from_lse,
     snapkv_compress_int4,
+    snapkv_compress_static,
     snapkv_compress_with_scores,
     snapkv_decode_attention,
     snapkv_decode_workspace_size,

@@ -16,6 +16,9 @@
 #include "snapkv_decode.h"
 #include "snapkv_kernels.h"
 
+static_assert(SNAPKV_STATIC_SCRATCH_BYTES == snapkv::kStaticScratchBytes,
+              "static scratch size in the header and the library");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -595,6 +598,33 @@ int32_t snapkv_compress_from_lse(int32_t batch, int32_t num_q_heads, int32_t num
   return compress_impl(batch, num_q_heads, num_kv_heads, head_dim, q_win, k, v, seq_lens, window,
                        kernel_size, pool_mode, budget, out_k, out_v, out_idx, workspace,
                        workspace_bytes, stream, nullptr, window_lse);
+}
+
+int32_t snapkv_compress_static(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, const void* q_win, const void* k, const void* v,
+                               const int32_t* seq_lens, int32_t window, int32_t kernel_size,
+                               int32_t pool_mode, int32_t budget, void* out_k, void* out_v,
+                               int32_t* out_idx, void* stream) {
+  // host checks first: a call the fixed area cannot serve enqueues nothing
+  int32_t st = check_tensors(q_win, k, v, out_k, out_v, out_idx);
+  if (st != SNAPKV_OK) return st;
+  Plan pl;
+  st = make_plan(batch, num_q_heads, num_kv_heads, head_dim, seq_lens, window, &pl);
+  if (st != SNAPKV_OK) return st;
+  if (budget <= window)
+    return fail(SNAPKV_ERR_INVALID_ARGUMENT, "budget must exceed window (it includes the window)");
+  st = check_pool(kernel_size, pool_mode);
+  if (st != SNAPKV_OK) return st;
+  if (pl.bytes > snapkv::kStaticScratchBytes)
+    return fail(SNAPKV_ERR_WORKSPACE, "this shape needs " + std::to_string(pl.bytes) +
+                                          " bytes of scratch; the static area holds " +
+                                          std::to_string(snapkv::kStaticScratchBytes));
+  void* ws = nullptr;
+  const hipError_t e = snapkv::static_scratch(&ws);
+  if (e != hipSuccess) return hip_fail(e, "static scratch lookup");
+  return compress_impl(batch, num_q_heads, num_kv_heads, head_dim, q_win, k, v, seq_lens, window,
+                       kernel_size, pool_mode, budget, out_k, out_v, out_idx, ws,
+                       snapkv::kStaticScratchBytes, stream, nullptr, nullptr);
 }
 
 int32_t snapkv_compress_with_scores(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

@@ -34,6 +34,12 @@ constexpr int kFusedMaxHalo = 16;               // kernel / 2 (at most)
 constexpr int kFusedMaxRows = 256;              // G * W rounded up to 32 (one row tile per wave)
 constexpr int kSpinLimit = 1 << 20;             // polls of a fused item's bounded wait (~1 s)
 
+// Size of the library's fixed scratch area (snapkv_compress_static).
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+// Device address of that area on the current device (looked up on the first
+// call for each device, then kept).
+hipError_t static_scratch(void** ptr);
+
 // Per-prompt table passed by value in the kernel arguments.
 struct PromptTable {
   int32_t off[kMaxBatch];  // first packed token of prompt b

@@ -81,6 +81,9 @@ def load_library():
                                                 _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
                                                 _i32, _vp, _sz, _vp]
     lib.snapkv_compress_with_scores.restype = _i32
+    lib.snapkv_compress_static.argtypes = [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _pi32, _i32,
+                                           _i32, _i32, _i32, _vp, _vp, _vp, _vp]
+    lib.snapkv_compress_static.restype = _i32
     lib.snapkv_compress_int4.argtypes = [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _pi32, _i32, _vp,
                                          _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                          _vp]
@@ -274,6 +277,37 @@ def snapkv_compress_from_lse(q_win: torch.Tensor, k: torch.Tensor, v: torch.Tens
         batch, hq, hkv, d, _ptr(q_win), _ptr(k), _ptr(v), arr, window, _ptr(window_lse),
         kernel_size, pool_mode_code(pool_mode), budget, _ptr(out_k), _ptr(out_v), _ptr(out_idx),
         _ptr(workspace), workspace.numel(), _stream(stream, dev)))
+    return out_k, out_v, out_idx
+
+
+SNAPKV_STATIC_SCRATCH_BYTES = 32 << 20
+
+
+def snapkv_compress_static(q_win: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                           seq_lens: Sequence[int], window: int, kernel_size: int, pool_mode,
+                           budget: int, *, out_k: Optional[torch.Tensor] = None,
+                           out_v: Optional[torch.Tensor] = None,
+                           out_idx: Optional[torch.Tensor] = None, stream=None):
+    """snapkv_compress without a workspace: the library's fixed scratch area
+    serves as one (the C call allocates nothing; outputs not passed in are
+    allocated here by torch). Calls that overlap on one device race; see
+    include/snapkv.h."""
+    lib = load_library()
+    _check_tensor("q_win", q_win, 4)
+    _check_tensor("k", k, 3)
+    _check_tensor("v", v, 3)
+    arr, vals = _lens(seq_lens)
+    batch, hq, hkv, d, w = _shapes(q_win, k, vals)
+    if v.shape != k.shape:
+        raise ValueError("k and v shapes differ")
+    if w != window:
+        raise ValueError(f"q_win holds {w} window rows but window={window}")
+    dev = q_win.device
+    out_k, out_v, out_idx = _outputs(batch, hkv, budget, d, dev, out_k, out_v, out_idx)
+    _check(lib.snapkv_compress_static(batch, hq, hkv, d, _ptr(q_win), _ptr(k), _ptr(v), arr,
+                                      window, kernel_size, pool_mode_code(pool_mode), budget,
+                                      _ptr(out_k), _ptr(out_v), _ptr(out_idx),
+                                      _stream(stream, dev)))
     return out_k, out_v, out_idx
 
 

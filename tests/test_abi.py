@@ -22,9 +22,10 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = skv.header_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     assert "snapkv_compress_staged" in names
     assert "snapkv_compress_with_scores" in names
+    assert "snapkv_compress_static" in names
     assert "snapkv_compress_from_lse" in names
     for name in names:
         assert hasattr(lib, name), name
@@ -143,6 +144,26 @@ def test_compress_with_scores_validation(lib):
     # valid arguments: the undersized workspace stops the call
     assert call() == 3
     assert call(lse=FAKE + 4) == 3
+
+
+def test_compress_static_rejects_before_any_device_call(lib):
+    # no workspace argument: shapes whose scratch exceeds the fixed area are
+    # refused on the host, like every other invalid argument
+    def call(lens, hq=64, hkv=8, budget=1024, kernel=7, ok=FAKE):
+        arr = (ctypes.c_int32 * len(lens))(*lens)
+        return lib.snapkv_compress_static(len(lens), hq, hkv, 128, FAKE, FAKE, FAKE, arr, 64,
+                                          kernel, 1, budget, ok, FAKE, FAKE, None)
+
+    assert skv.SNAPKV_STATIC_SCRATCH_BYTES == 32 << 20
+    assert call([131072] * 8) == 3 and "static area" in skv.snapkv_last_error()
+    assert skv.snapkv_workspace_size(64, 8, 128, [131072] * 8, 64) > skv.SNAPKV_STATIC_SCRATCH_BYTES
+    assert call([131072], budget=64) == 1
+    assert call([131072], kernel=4) == 1
+    assert call([131072], ok=None) == 1
+    assert call([131072], hq=63) == 1
+    # every benchmark workload fits the area
+    for lens, hq, w in (([131072], 64, 64), ([32768] * 8, 32, 64), ([16384], 32, 32)):
+        assert skv.snapkv_workspace_size(hq, 8, 128, lens, w) <= skv.SNAPKV_STATIC_SCRATCH_BYTES
 
 
 def test_compress_int4_validation(lib):
