@@ -1,18 +1,26 @@
 """Throughput of SnapKV prefill-time KV-cache compression on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--subs NAME,NAME|none] [--no-cpu-baseline]
 
 A step is one snapkv_compress call (vote statistics, vote with pooling,
 selection, gather: four kernels, or fewer when statistics and vote run as
-the fused score kernel and the selection runs inside the gather) on one
-layer of synthetic, seeded input
-already resident in HBM. Inputs and outputs rotate over enough buffer sets to
-exceed the 256 MB Infinity Cache, so every step streams its K from HBM.
-Prints one JSON line: value = prompt tokens compressed per second per layer;
-the roofline of the dominant kernel, timed per kernel with HIP events on the
-library's stream through snapkv_compress_staged (one kernel per stage) and
-priced with its algorithmic bytes per launch; and the fp64 CPU oracle timed
-on a bounded sample of the same workload on this host.
+one fused score kernel and the selection runs inside the gather) on one
+layer of synthetic, seeded input already resident in HBM. The headline
+workload is the largest single-GPU one, the 70B-shaped 80-layer stack at
+L = 131072 (64 query / 8 KV heads, W = 64, maxpool 7, B = 1024): each step
+compresses the next of its distinct-seed layers, so every step streams its
+K from HBM. The other workloads (8B-shaped 16K layer, 32K 32-layer stack,
+ragged batch of 8 prompts) are measured the same way as sub-records, each
+rotating over distinct-seed layers or input variants that together exceed
+the 256 MB Infinity Cache.
+
+Prints one JSON line: value = prompt tokens compressed per second per layer
+on the headline workload; `roofline` of its dominant kernel (per-kernel
+durations from HIP events that each dispatch records at its kernel's start
+and end, priced with the kernel's algorithmic work per launch); and
+`cpu_baseline`, the fp64 CPU oracle timed on this host over a bounded sample
+of the same workload, spread over worker processes one KV head per job.
 """
 
 from __future__ import annotations
@@ -31,8 +39,13 @@ HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 METRIC = "prompt tokens compressed/sec per layer; achieved HBM GB/s vs MI355X peak"
 CACHE_BYTES = 256 << 20       # Infinity Cache
+HEADLINE = "llama3_70b_128k_x80"
+SUBS = ("llama3_8b_16k", "llama3_8b_32k_x32", "llama3_8b_ragged8")
+# workloads whose score kernels sit above the HBM/MFMA balance point: their
+# roofline is the bf16 matrix cores (one pass of Q_win . K^T)
+MFMA_BOUND = ("llama3_70b_128k_x80",)
 KERNEL_SOURCES = ("snapkv_api.cpp", "snapkv_kernels.h", "snapkv_kernels.hip", "snapkv_score.h",
-                  "snapkv_select.h", "snapkv_gather.h", "snapkv_device.h")
+                  "snapkv_select.h", "snapkv_gather.h", "snapkv_device.h", "snapkv_static.hip")
 
 
 def algorithmic_bytes(w, seq_lens):
@@ -50,13 +63,14 @@ def algorithmic_bytes(w, seq_lens):
 def stage_bytes(w, seq_lens):
     """Algorithmic bytes of each stage kernel for one call (per launch):
     stats reads Q and all L keys; vote reads Q and the P prefix keys; the
-    fused score kernel (both in one launch) reads Q and all L keys once;
+    fused score kernels (both in one launch) read Q and all L keys once;
     select reads the P pooled scores and writes the index list; gather moves
     the kept rows (the gather term of algorithmic_bytes)."""
     d, q_bytes = w.head_dim, w.h_q * w.window * w.head_dim * 2
     gather = algorithmic_bytes(w, seq_lens)[1]
     out = {"snapkv_score_stats": 0, "snapkv_score_vote": 0, "snapkv_score_fused": 0,
-           "snapkv_score_fused_stream": 0, "snapkv_select": 0, "snapkv_gather": gather, "snapkv_gather_select": gather}
+           "snapkv_score_fused_stream": 0, "snapkv_select": 0, "snapkv_gather": gather,
+           "snapkv_gather_select": gather}
     for L in seq_lens:
         if L > w.budget:
             P = L - w.window
@@ -83,8 +97,9 @@ def _source_hash(names):
 
 
 def _traffic(kernel_key):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when the kernel source changed since the counters were taken."""
+    """HBM bytes per launch from the committed rocprofv3 counter summary (key
+    "<workload>:<kernel>"), or None when the kernel sources changed since the
+    counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -93,6 +108,228 @@ def _traffic(kernel_key):
     if not rec or rec.get("source_hash") != _source_hash(KERNEL_SOURCES):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------ CPU baseline --
+_JOBS = None  # per-worker copy of the sample's head slices (small layers)
+
+
+def _init_worker(jobs=None):
+    global _JOBS
+    _JOBS = jobs
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+    import oracle  # noqa: F401  (imported before any job is timed)
+
+
+def _oracle_head_job(job):
+    """One full oracle compression of one KV head (the oracle's per-head work
+    on a single-KV-head slice of the layer); returns its wall time. `job` is
+    the slice itself, or its index into the worker's copy."""
+    import oracle
+    args = _JOBS[job] if isinstance(job, int) else job
+    q, k, v, lens, window, kernel, pool, budget = args
+    t = time.perf_counter()
+    oracle.compress(q, k, v, lens, window, kernel, pool, budget, keep_scores=False)
+    return time.perf_counter() - t
+
+
+def _head_slices(w, x):
+    import numpy as np
+    g = w.h_q // w.h_kv
+    lens = x.seq_lens.tolist()
+    return [(np.ascontiguousarray(x.q_win[:, h * g:(h + 1) * g]),
+             np.ascontiguousarray(x.k[:, h:h + 1]), np.ascontiguousarray(x.v[:, h:h + 1]),
+             lens, w.window, w.kernel, w.pool, w.budget) for h in range(w.h_kv)]
+
+
+def cpu_baseline(w, cpu_seconds=12.0):
+    """The oracle as it stands, timed on this host: layer 0 of the workload
+    (the parity tests' input bits) split into one job per KV head, repeated
+    until the sample holds about `cpu_seconds` of single-threaded work, run
+    on a pool of worker processes (one BLAS thread each, up to 16, the host's
+    core count permitting). Input generation, pool start-up and handing the
+    inputs to the workers are outside the timed region (small layers are
+    copied to every worker once; a large layer's head slices travel with
+    their jobs)."""
+    import multiprocessing
+    from concurrent.futures import ProcessPoolExecutor
+
+    from synth import make_layer
+
+    x = make_layer(w, 0)
+    jobs = _head_slices(w, x)
+    host_cores = len(os.sched_getaffinity(0))
+    workers = max(1, min(16, host_cores))
+    tokens = int(x.seq_lens.sum())
+    layer_bytes = x.q_win.nbytes + x.k.nbytes + x.v.nbytes
+    resident = layer_bytes <= (64 << 20)
+    with ProcessPoolExecutor(max_workers=workers, mp_context=multiprocessing.get_context("spawn"),
+                             initializer=_init_worker,
+                             initargs=(jobs if resident else None,)) as ex:
+        ids = list(range(len(jobs))) if resident else jobs
+        # warm-up: every worker started and through one job; a second round
+        # sizes the sample
+        list(ex.map(_oracle_head_job, [ids[0]] * workers))
+        t_head = min(ex.map(_oracle_head_job, [ids[0]] * workers))
+        reps = max(1, int(round(cpu_seconds / (t_head * len(jobs)))))
+        sample = ids * reps
+        t0 = time.perf_counter()
+        busy = sum(ex.map(_oracle_head_job, sample))
+        wall = time.perf_counter() - t0
+    used = min(workers, len(sample))
+    return {"value": round(reps * tokens / wall, 1), "unit": "tokens/s/layer", "cores": used,
+            "kind": "oracle",
+            "sample": f"{w.name} layer 0 ({tokens} tokens): {reps} x {len(jobs)} one-KV-head "
+                      f"full oracle calls ({reps} layer(s) of work, {busy:.1f} s of CPU) in "
+                      f"{wall:.2f} s on {used} worker processes",
+            "host_cores": host_cores, "blas_threads_per_worker": 1}
+
+
+# ----------------------------------------------------------------- GPU ------
+def _input_sets(w, steps, warmup, dev):
+    """Distinct-seed inputs for the rotation: the stack's own layers when it
+    has several, else variants of its one layer; at least enough to exceed
+    four times the Infinity Cache, and for the stacks one layer per step up to
+    all of them."""
+    import torch  # noqa: F401
+
+    from synth.device import layer_lengths, make_layer_device
+
+    lens = layer_lengths(w, 0)
+    kv_bytes = 2 * sum(lens) * w.h_kv * w.head_dim * 2
+    need = max(2, -(-4 * CACHE_BYTES // kv_bytes))
+    if w.layers > 1:
+        n = min(w.layers, max(need, steps + warmup))
+        return [make_layer_device(w, layer, dev) for layer in range(n)], "layers"
+    n = min(64, need)
+    return [make_layer_device(w, 0, dev, variant=i) for i in range(n)], "variants"
+
+
+def measure(w, args, dev, stream, extras=False):
+    import numpy as np
+    import torch
+
+    import long_context_kv_snapkv_amd as skv
+
+    sets, kind = _input_sets(w, args.steps, args.warmup, dev)
+    batch, hkv, d, B = len(sets[0][3]), w.h_kv, w.head_dim, w.budget
+    outs = [(torch.empty((batch, hkv, B, d), dtype=torch.bfloat16, device=dev),
+             torch.empty((batch, hkv, B, d), dtype=torch.bfloat16, device=dev),
+             torch.empty((batch, hkv, B), dtype=torch.int32, device=dev)) for _ in range(2)]
+    ws = skv.new_workspace(w.h_q, hkv, d, sets[0][3], w.window, dev)
+    nsets = len(sets)
+
+    def step(i, staged=False, events=None):
+        q, k, v, lens = sets[i % nsets]
+        ok, ov, oi = outs[i % 2]
+        skv.snapkv_compress(q, k, v, lens, w.window, w.kernel, w.pool, B, out_k=ok, out_v=ov,
+                            out_idx=oi, workspace=ws, stream=stream, staged=staged,
+                            stage_events=events)
+
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        return t_start.elapsed_time(t_end) / args.steps
+
+    ms_step = timed(step)
+
+    # per-kernel durations: snapkv_compress_staged has each stage's dispatch
+    # record the caller's events at its kernel's start and end
+    nprof = min(args.steps, 200)
+    nst = skv.SNAPKV_NUM_STAGES
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nst)] for _ in range(nprof)]
+    for row in evs:  # materialise the HIP events before handing them over
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for i in range(nprof):
+        step(i, staged=True, events=evs[i])
+    torch.cuda.synchronize()
+    lens0 = sets[0][3]
+    score_kernels = skv.snapkv_score_kernels(w.h_q, hkv, d, lens0, w.window, w.kernel)
+    fused = score_kernels != 2
+    fused_name = "snapkv_score_fused" if score_kernels == 1 else "snapkv_score_fused_stream"
+    sel_in_gather = skv.snapkv_gather_selects(w.h_q, hkv, d, lens0, w.window, B) == 1
+    stage_ms = {}
+    for s_ in range(nst):
+        if (fused and s_ == 1) or (sel_in_gather and s_ == 2):
+            continue
+        vals = [row[2 * s_].elapsed_time(row[2 * s_ + 1]) for row in evs]
+        name = skv.snapkv_stage_name(s_)
+        if fused and s_ == 0:
+            name = fused_name
+        if sel_in_gather and s_ == 3:
+            name = "snapkv_gather_select"
+        stage_ms[name] = float(np.mean(vals))
+
+    sbytes = stage_bytes(w, lens0)
+    dominant = max(stage_ms, key=stage_ms.get)
+    kernel_ms = stage_ms[dominant]
+    score_b, gather_b = algorithmic_bytes(w, lens0)
+    total_b = score_b + gather_b
+    flops = score_flops(w, lens0)
+    score_ms = (stage_ms[fused_name] if fused else
+                stage_ms["snapkv_score_stats"] + stage_ms["snapkv_score_vote"])
+    hbm_gbps = sbytes[dominant] / (kernel_ms * 1e-3) / 1e9
+    traffic = _traffic(f"{w.name}:{dominant}")
+    if w.name in MFMA_BOUND and dominant in (fused_name, "snapkv_score_stats",
+                                             "snapkv_score_vote"):
+        tflops = flops / (kernel_ms * 1e-3) / 1e12
+        roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(tflops, 1),
+                    "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                    "flops_per_launch": flops, "bytes_per_launch": sbytes[dominant],
+                    "launch_ms": round(kernel_ms, 5), "hbm_gbps": round(hbm_gbps, 1),
+                    "hbm_frac": round(hbm_gbps / HBM_PEAK_GBPS, 4)}
+    else:
+        roofline = {"kernel": dominant, "bound": "hbm", "achieved": round(hbm_gbps, 1),
+                    "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(hbm_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                    "bytes_per_launch": sbytes[dominant], "launch_ms": round(kernel_ms, 5)}
+    tokens = sum(lens0)
+    rec = {
+        "value": round(tokens / (ms_step * 1e-3), 1), "unit": "tokens/s/layer",
+        "ms_per_step": round(ms_step, 5),
+        "config": {"workload": w.name, "batch": batch,
+                   "seq_len": lens0 if batch > 1 else lens0[0],
+                   "num_q_heads": w.h_q, "num_kv_heads": hkv, "head_dim": d,
+                   "window": w.window, "kernel_size": w.kernel, "pooling": w.pool + "pool",
+                   "budget": B, "layers": w.layers,
+                   "rotating_inputs": f"{nsets} distinct-seed {kind}"},
+        "hbm_gbps_whole_call": round(total_b / (ms_step * 1e-3) / 1e9, 1),
+        "hbm_frac_whole_call": round(total_b / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_call": total_b,
+        "mfma_util_score": {"algorithmic_1pass": round(flops / (score_ms * 1e-3) / 1e12 /
+                                                       BF16_PEAK_TFLOPS, 4),
+                            "issued_2pass": round(2 * flops / (score_ms * 1e-3) / 1e12 /
+                                                  BF16_PEAK_TFLOPS, 4)},
+        "score_kernels": score_kernels,
+        "score_kernel": fused_name if fused else "snapkv_score_stats + snapkv_score_vote",
+        "selection_in_gather": sel_in_gather,
+        "stage_kernels": {k: {"ms": round(v, 5), "alg_bytes": sbytes[k],
+                              "gbps": round(sbytes[k] / (v * 1e-3) / 1e9, 1)}
+                          for k, v in stage_ms.items()},
+        "roofline": roofline,
+    }
+    if extras:
+        rec.update(measure_extras(w, args, dev, stream, sets, outs, ws, timed))
+    del sets, outs, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
 
 
 def _window_lse(q, k, lens, window):
@@ -117,204 +354,68 @@ def _window_lse(q, k, lens, window):
     return out
 
 
-def cpu_baseline(w, x, budget_s=10.0):
-    import numpy as np  # noqa: F401
-
-    import oracle
-    threads = os.cpu_count()
-    try:
-        from threadpoolctl import threadpool_info
-        blas = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
-        threads = max(blas) if blas else 1
-    except Exception:
-        pass
-    lens = x.seq_lens.tolist()
-    t0 = time.perf_counter()
-    calls = 0
-    while True:
-        oracle.compress(x.q_win, x.k, x.v, lens, w.window, w.kernel, w.pool, w.budget,
-                        keep_scores=False)
-        calls += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = (time.perf_counter() - t0) / calls
-    return {"value": sum(lens) / dt, "unit": "tokens/s/layer", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{w.name} layer 0, all {w.h_kv} KV heads, {calls} full oracle "
-                      f"call(s) in {dt * calls:.1f} s ({dt:.2f} s per layer)"}
-
-
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="llama3_8b_16k")
-    ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0: auto)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain device copy of known size (counter scaling)")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the compression path runs on a single "
-              "MI355X and launches no multi-GPU work (--gpus must be 1).",
-              file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
+def measure_extras(w, args, dev, stream, sets, outs, ws, timed):
+    """The same workload through snapkv_compress_from_lse, _int4 and _fp8,
+    and one decode step's attention over the compressed and the full cache."""
     import torch
 
     import long_context_kv_snapkv_amd as skv
-    from synth import WORKLOADS, make_layer
 
-    w = WORKLOADS[args.workload]
-    x = make_layer(w, 0)
-    lens = x.seq_lens.tolist()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    skv.load_library()
-
-    def up(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
-            torch.bfloat16).to(dev)
-
-    q0, k0, v0 = up(x.q_win), up(x.k), up(x.v)
-    kv_bytes = 2 * k0.numel() * 2
-    nsets = args.sets or max(2, min(64, -(-4 * CACHE_BYTES // kv_bytes)))
-    batch, hkv, d, B = len(lens), w.h_kv, w.head_dim, w.budget
-    sets = []
-    for i in range(nsets):
-        sets.append(dict(q=q0.clone(), k=k0.clone(), v=v0.clone(),
-                         ok=torch.empty((batch, hkv, B, d), dtype=torch.bfloat16, device=dev),
-                         ov=torch.empty((batch, hkv, B, d), dtype=torch.bfloat16, device=dev),
-                         oi=torch.empty((batch, hkv, B), dtype=torch.int32, device=dev)))
-    del q0, k0, v0
-    ws = skv.new_workspace(w.h_q, hkv, d, lens, w.window, dev)
-    stream = torch.cuda.current_stream(dev)
-
-    def step(i, staged=False, events=None):
-        s = sets[i % nsets]
-        skv.snapkv_compress(s["q"], s["k"], s["v"], lens, w.window, w.kernel, w.pool, B,
-                            out_k=s["ok"], out_v=s["ov"], out_idx=s["oi"], workspace=ws,
-                            stream=stream, staged=staged, stage_events=events)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_total = t_start.elapsed_time(t_end)
-    ms_step = ms_total / args.steps
-
-    # per-kernel durations: snapkv_compress_staged has each stage's dispatch
-    # record the caller's events at its kernel's start and end
-    nprof = min(args.steps, 200)
-    nst = skv.SNAPKV_NUM_STAGES
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nst)]
-           for _ in range(nprof)]
-    for row in evs:  # materialise the HIP events before handing them over
-        for e in row:
-            e.record(stream)
-    torch.cuda.synchronize()
-    for i in range(nprof):
-        step(i, staged=True, events=evs[i])
-    torch.cuda.synchronize()
-    # with a fused score kernel, stage 0 is that kernel and stage 1 is empty
-    # and with the selection inside the gather, stage 3 is that kernel and
-    # stage 2 is empty
-    score_kernels = skv.snapkv_score_kernels(w.h_q, hkv, d, lens, w.window, w.kernel)
-    fused = score_kernels != 2
-    fused_name = "snapkv_score_fused" if score_kernels == 1 else "snapkv_score_fused_stream"
-    sel_in_gather = skv.snapkv_gather_selects(w.h_q, hkv, d, lens, w.window, B) == 1
-    stage_ms = {}
-    for s_ in range(nst):
-        if (fused and s_ == 1) or (sel_in_gather and s_ == 2):
-            continue
-        vals = [row[2 * s_].elapsed_time(row[2 * s_ + 1]) for row in evs]
-        name = skv.snapkv_stage_name(s_)
-        if fused and s_ == 0:
-            name = fused_name
-        if sel_in_gather and s_ == 3:
-            name = "snapkv_gather_select"
-        stage_ms[name] = float(np.mean(vals))
-
-    # the same compression when the caller's prefill attention hands over
-    # each window row's log-sum-exp (snapkv_compress_from_lse): the
-    # normalisers are computed here beforehand, outside the timed region, as
-    # a prefill kernel would have produced them
-    lse = _window_lse(sets[0]["q"], sets[0]["k"], lens, w.window)
+    nsets = len(sets)
+    batch, hkv, d, B = len(sets[0][3]), w.h_kv, w.head_dim, w.budget
+    lens = sets[0][3]
+    # the caller's prefill would hand over the normalisers: computed here
+    # beforehand, outside the timed region, for every input set
+    lses = [_window_lse(q, k, ls, w.window) for q, k, _, ls in sets]
 
     def step_lse(i):
-        s = sets[i % nsets]
-        skv.snapkv_compress_from_lse(s["q"], s["k"], s["v"], lens, w.window, lse, w.kernel,
-                                     w.pool, B, out_k=s["ok"], out_v=s["ov"], out_idx=s["oi"],
-                                     workspace=ws, stream=stream)
+        q, k, v, ls = sets[i % nsets]
+        ok, ov, oi = outs[i % 2]
+        skv.snapkv_compress_from_lse(q, k, v, ls, w.window, lses[i % nsets], w.kernel, w.pool, B,
+                                     out_k=ok, out_v=ov, out_idx=oi, workspace=ws, stream=stream)
 
-    for i in range(args.warmup):
-        step_lse(i)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step_lse(i)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_step_lse = t_start.elapsed_time(t_end) / args.steps
+    ms_lse = timed(step_lse)
+    quant = {}
+    for form, per_byte in (("int4", 2), ("fp8", 1)):
+        kq = [torch.empty((batch, hkv, B, d // per_byte), dtype=torch.uint8, device=dev)
+              for _ in range(2)]
+        vq = [torch.empty_like(t) for t in kq]
+        ks = [torch.empty((batch, hkv, B), dtype=torch.float32, device=dev) for _ in range(2)]
+        vs = [torch.empty_like(t) for t in ks]
+        fn = skv.snapkv_compress_int4 if form == "int4" else skv.snapkv_compress_fp8
 
-    # the same compression storing the kept rows at 4 bits per value
-    # (snapkv_compress_int4)
-    for s_ in sets:
-        s_["kq"] = torch.empty((batch, hkv, B, d // 2), dtype=torch.uint8, device=dev)
-        s_["vq"] = torch.empty_like(s_["kq"])
-        s_["ks"] = torch.empty((batch, hkv, B), dtype=torch.float32, device=dev)
-        s_["vs"] = torch.empty_like(s_["ks"])
+        def step_q(i, fn=fn, kq=kq, vq=vq, ks=ks, vs=vs):
+            q, k, v, ls = sets[i % nsets]
+            j = i % 2
+            fn(q, k, v, ls, w.window, w.kernel, w.pool, B,
+               out=(kq[j], ks[j], vq[j], vs[j], outs[j][2]), workspace=ws, stream=stream)
 
-    def step_int4(i):
-        s = sets[i % nsets]
-        skv.snapkv_compress_int4(s["q"], s["k"], s["v"], lens, w.window, w.kernel, w.pool, B,
-                                 out=(s["kq"], s["ks"], s["vq"], s["vs"], s["oi"]),
-                                 workspace=ws, stream=stream)
-
-    def timed(fn):
-        for i in range(args.warmup):
-            fn(i)
-        torch.cuda.synchronize()
-        t_start.record(stream)
-        for i in range(args.steps):
-            fn(i)
-        t_end.record(stream)
-        torch.cuda.synchronize()
-        return t_start.elapsed_time(t_end) / args.steps
-
-    ms_step_int4 = timed(step_int4)
-    # and as FP8 E4M3 bytes (snapkv_compress_fp8)
-    for s_ in sets:
-        s_["kq8"] = torch.empty((batch, hkv, B, d), dtype=torch.uint8, device=dev)
-        s_["vq8"] = torch.empty_like(s_["kq8"])
-
-    def step_fp8(i):
-        s = sets[i % nsets]
-        skv.snapkv_compress_fp8(s["q"], s["k"], s["v"], lens, w.window, w.kernel, w.pool, B,
-                                out=(s["kq8"], s["ks"], s["vq8"], s["vs"], s["oi"]),
-                                workspace=ws, stream=stream)
-
-    ms_step_fp8 = timed(step_fp8)
-    for s_ in sets:
-        del s_["kq8"], s_["vq8"]
+        ms = timed(step_q)
+        quant[form] = {"ms_per_step": round(ms, 5),
+                       "value": round(sum(lens) / (ms * 1e-3), 1), "unit": "tokens/s/layer",
+                       "cache_bytes": 2 * batch * hkv * B * (d // per_byte + 4)}
+    quant["int4"]["note"] = ("snapkv_compress_int4: kept rows stored as 4-bit codes with a "
+                             "float32 scale per row")
+    quant["fp8"]["note"] = ("snapkv_compress_fp8: kept rows stored as FP8 E4M3 bytes with a "
+                            "float32 scale per row")
 
     # one decode step's attention over the compressed cache against the full
-    # prefill cache (snapkv_decode_attention), each cache streamed from HBM:
-    # enough distinct compressed caches rotate to exceed the Infinity Cache
+    # prefill cache, each streamed from HBM: enough distinct compressed caches
+    # (the gathered rows of different input sets) to exceed the Infinity Cache
     n_kept = [min(L, B) for L in lens]
     qdec = torch.randn((batch, w.h_q, d), device=dev).to(torch.bfloat16)
     dout = torch.empty((batch, w.h_q, d), dtype=torch.float32, device=dev)
     comp_bytes = 2 * batch * hkv * B * d * 2
     ncomp = max(2, -(-4 * CACHE_BYTES // comp_bytes))
-    comp = [(sets[i % nsets]["ok"].clone(), sets[i % nsets]["ov"].clone()) for i in range(ncomp)]
+    comp = []
+    for i in range(ncomp):
+        q, k, v, ls = sets[i % nsets]
+        ok = torch.empty((batch, hkv, B, d), dtype=torch.bfloat16, device=dev)
+        ov = torch.empty_like(ok)
+        skv.snapkv_compress(q, k, v, ls, w.window, w.kernel, w.pool, B, out_k=ok, out_v=ov,
+                            workspace=ws, stream=stream)
+        comp.append((ok, ov))
+    torch.cuda.synchronize()
     ws_c = torch.empty(max(16, skv.snapkv_decode_workspace_size(
         w.h_q, hkv, d, n_kept, skv.SNAPKV_CACHE_COMPRESSED, B)), dtype=torch.uint8, device=dev)
     ws_f = torch.empty(max(16, skv.snapkv_decode_workspace_size(
@@ -325,69 +426,15 @@ def main():
         skv.snapkv_decode_attention(qdec, kc, vc, n_kept, out=dout, workspace=ws_c, stream=stream)
 
     def dec_full(i):
-        s = sets[i % nsets]
-        skv.snapkv_decode_attention(qdec, s["k"], s["v"], lens, out=dout, workspace=ws_f,
-                                    stream=stream)
+        _, k, v, ls = sets[i % nsets]
+        skv.snapkv_decode_attention(qdec, k, v, ls, out=dout, workspace=ws_f, stream=stream)
 
-    dec_ms = {}
-    for name, fn in (("compressed", dec_comp), ("full", dec_full)):
-        for i in range(args.warmup):
-            fn(i)
-        torch.cuda.synchronize()
-        t_start.record(stream)
-        for i in range(args.steps):
-            fn(i)
-        t_end.record(stream)
-        torch.cuda.synchronize()
-        dec_ms[name] = t_start.elapsed_time(t_end) / args.steps
-    dec_bytes = {"compressed": 2 * hkv * sum(n_kept) * d * 2,
-                 "full": 2 * hkv * sum(lens) * d * 2}
+    dec_ms = {"compressed": timed(dec_comp), "full": timed(dec_full)}
+    dec_bytes = {"compressed": 2 * hkv * sum(n_kept) * d * 2, "full": 2 * hkv * sum(lens) * d * 2}
     del comp
-
-    sbytes = stage_bytes(w, lens)
-    dominant = max(stage_ms, key=stage_ms.get)
-    kernel_ms = stage_ms[dominant]
-    achieved = sbytes[dominant] / (kernel_ms * 1e-3) / 1e9
-    score_b, gather_b = algorithmic_bytes(w, lens)
-    total_b = score_b + gather_b
-    flops = score_flops(w, lens)
-    score_ms = (stage_ms[fused_name] if fused else
-                stage_ms["snapkv_score_stats"] + stage_ms["snapkv_score_vote"])
-    tokens = sum(lens)
-    value = tokens / (ms_step * 1e-3)
-    roofline = {
-        "kernel": dominant, "bound": "hbm",
-        "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBPS, 4),
-        "traffic": _traffic(dominant),
-        "bytes_per_launch": sbytes[dominant], "launch_ms": round(kernel_ms, 5),
-    }
-    out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s/layer",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w.name, "batch": batch, "seq_len": lens if batch > 1 else lens[0],
-                   "num_q_heads": w.h_q, "num_kv_heads": hkv, "head_dim": d,
-                   "window": w.window, "kernel_size": w.kernel, "pooling": w.pool + "pool",
-                   "budget": B, "rotating_sets": nsets},
-        "hbm_gbps_whole_call": round(total_b / (ms_step * 1e-3) / 1e9, 1),
-        "hbm_frac_whole_call": round(total_b / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-        "algorithmic_bytes_per_call": total_b,
-        "mfma_util_score": {"algorithmic_1pass": round(flops / (score_ms * 1e-3) / 1e12 /
-                                                       BF16_PEAK_TFLOPS, 4),
-                            "issued_2pass": round(2 * flops / (score_ms * 1e-3) / 1e12 /
-                                                  BF16_PEAK_TFLOPS, 4)},
-        "score_kernels": 1 if fused else 2,
-        "score_kernel": fused_name if fused else "snapkv_score_stats + snapkv_score_vote",
-        "selection_in_gather": sel_in_gather,
-        "stage_kernels": {k: {"ms": round(v, 5), "alg_bytes": sbytes[k],
-                              "gbps": round(sbytes[k] / (v * 1e-3) / 1e9, 1)}
-                          for k, v in stage_ms.items()},
-        "roofline": roofline,
-        "from_lse": {"ms_per_step": round(ms_step_lse, 5),
-                     "value": round(sum(lens) / (ms_step_lse * 1e-3), 1),
-                     "unit": "tokens/s/layer",
+    return {
+        "from_lse": {"ms_per_step": round(ms_lse, 5),
+                     "value": round(sum(lens) / (ms_lse * 1e-3), 1), "unit": "tokens/s/layer",
                      "note": "snapkv_compress_from_lse: window-row log-sum-exp supplied by "
                              "the caller's prefill, computed before the timed region"},
         "decode": {
@@ -396,25 +443,68 @@ def main():
             "compressed_us": round(dec_ms["compressed"] * 1e3, 3),
             "full_us": round(dec_ms["full"] * 1e3, 3),
             "speedup": round(dec_ms["full"] / dec_ms["compressed"], 2),
-            "compressed_gbps": round(dec_bytes["compressed"] / (dec_ms["compressed"] * 1e-3) / 1e9,
-                                     1),
+            "compressed_gbps": round(dec_bytes["compressed"] / (dec_ms["compressed"] * 1e-3) /
+                                     1e9, 1),
             "full_gbps": round(dec_bytes["full"] / (dec_ms["full"] * 1e-3) / 1e9, 1),
             "full_hbm_frac": round(dec_bytes["full"] / (dec_ms["full"] * 1e-3) / 1e9 /
                                    HBM_PEAK_GBPS, 4),
             "cache_bytes": dec_bytes},
-        "int4": {"ms_per_step": round(ms_step_int4, 5),
-                 "value": round(sum(lens) / (ms_step_int4 * 1e-3), 1),
-                 "unit": "tokens/s/layer",
-                 "cache_bytes": 2 * batch * hkv * B * (d // 2 + 4),
-                 "note": "snapkv_compress_int4: kept rows stored as 4-bit codes with a "
-                         "float32 scale per row"},
-        "fp8": {"ms_per_step": round(ms_step_fp8, 5),
-                "value": round(sum(lens) / (ms_step_fp8 * 1e-3), 1),
-                "unit": "tokens/s/layer",
-                "cache_bytes": 2 * batch * hkv * B * (d + 4),
-                "note": "snapkv_compress_fp8: kept rows stored as FP8 E4M3 bytes with a "
-                        "float32 scale per row"},
+        "int4": quant["int4"],
+        "fp8": quant["fp8"],
     }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--subs", default=",".join(SUBS),
+                    help="comma-separated workloads measured as sub-records, or 'none'")
+    ap.add_argument("--extras-on", default="llama3_8b_16k",
+                    help="workload that also times from_lse, int4, fp8 and decode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="single-threaded oracle work per CPU baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of known size (counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the compression path runs on a single "
+              "MI355X and launches no multi-GPU work (--gpus must be 1).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import long_context_kv_snapkv_amd as skv
+    from synth import WORKLOADS
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    skv.load_library()
+    stream = torch.cuda.current_stream(dev)
+    subs = [] if args.subs in ("", "none") else [s for s in args.subs.split(",") if s]
+
+    w = WORKLOADS[args.workload]
+    head = measure(w, args, dev, stream, extras=(w.name == args.extras_on))
+    records = {}
+    for name in subs:
+        if name == w.name:
+            continue
+        records[name] = measure(WORKLOADS[name], args, dev, stream,
+                                extras=(name == args.extras_on))
+        print(f"[bench] {name}: {records[name]['ms_per_step'] * 1e3:.1f} us per call",
+              file=sys.stderr, flush=True)
+
+    out = {
+        "metric": METRIC, "value": head["value"], "unit": "tokens/s/layer",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+    }
+    out.update({k: v for k, v in head.items() if k not in ("value", "unit", "ms_per_step")})
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -423,9 +513,12 @@ def main():
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = src.numel()
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, x)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        for name, rec in records.items():
+            rec["cpu_baseline"] = cpu_baseline(WORKLOADS[name], args.cpu_seconds)
     else:
         out["cpu_baseline"] = None
+    out["workloads"] = records
     print(json.dumps(out), flush=True)
 
 

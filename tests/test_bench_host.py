@@ -55,16 +55,47 @@ def test_prompts_within_the_budget_move_only_their_rows():
 def test_traffic_is_reported_only_for_the_measured_sources(monkeypatch, tmp_path):
     prof = tmp_path / "profiles"
     prof.mkdir()
-    rec = {"snapkv_score_fused": {"source_hash": "abc", "hbm_bytes_per_launch": 123}}
+    key = "llama3_8b_16k:snapkv_score_fused"
+    rec = {key: {"source_hash": "abc", "hbm_bytes_per_launch": 123}}
     (prof / "traffic.json").write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     monkeypatch.setattr(bench, "_source_hash", lambda names: "abc")
-    assert bench._traffic("snapkv_score_fused") == 123
-    assert bench._traffic("snapkv_gather") is None
+    assert bench._traffic(key) == 123
+    assert bench._traffic("llama3_8b_16k:snapkv_gather") is None
+    assert bench._traffic("llama3_70b_128k_x80:snapkv_score_fused") is None
     monkeypatch.setattr(bench, "_source_hash", lambda names: "changed")
-    assert bench._traffic("snapkv_score_fused") is None
+    assert bench._traffic(key) is None
     (prof / "traffic.json").unlink()
-    assert bench._traffic("snapkv_score_fused") is None
+    assert bench._traffic(key) is None
+
+
+def test_headline_is_the_largest_single_gpu_workload():
+    # the 70B-shaped 128K stack has the most prompt tokens per layer and is
+    # priced against the matrix cores (one pass of Q_win . K^T)
+    w = WORKLOADS[bench.HEADLINE]
+    assert bench.HEADLINE == "llama3_70b_128k_x80" and w.layers == 80
+    assert all(WORKLOADS[s].name != bench.HEADLINE for s in bench.SUBS)
+    assert bench.score_flops(w, [131072]) == 2 * 64 * 64 * 128 * 131072
+    assert bench.HEADLINE in bench.MFMA_BOUND
+
+
+def test_cpu_baseline_splits_a_layer_into_one_job_per_kv_head():
+    # the oracle's per-head work on single-head slices: together they are the
+    # layer's oracle call (heads are independent)
+    import numpy as np
+    import oracle
+    from synth import make_custom
+    from synth.workloads import Workload
+    w = Workload(name="t", ident=99, h_q=8, h_kv=2, head_dim=64, window=16, kernel=5,
+                 pool="avg", budget=64, layers=1, batch=1, planting="points16", length=300)
+    x = make_custom([300], 8, 2, 64, 16, seed=4)
+    jobs = bench._head_slices(w, x)
+    assert len(jobs) == 2
+    full = oracle.compress(x.q_win, x.k, x.v, [300], 16, 5, "avg", 64)
+    for h, (q, k, v, lens, *rest) in enumerate(jobs):
+        part = oracle.compress(q, k, v, lens, *rest)
+        np.testing.assert_array_equal(part.out_idx[:, 0], full.out_idx[:, h])
+        np.testing.assert_array_equal(part.out_k[:, 0], full.out_k[:, h])
 
 
 def test_source_hash_covers_every_kernel_source():
