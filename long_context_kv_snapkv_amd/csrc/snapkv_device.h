@@ -120,6 +120,52 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Issue priority of this wave around its MFMA chains. Of the waves sharing a
+// SIMD, one that is about to issue matrix work goes ahead of one doing its
+// exp work, so the waves settle into alternating phases (one on the matrix
+// core while the other uses the VALU) instead of meeting at the matrix core
+// together after each barrier.
+__device__ __forceinline__ void mfma_phase_begin() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(2);
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void mfma_phase_end() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Scheduling hint for a region holding the MFMA chains of one key block (KS
+// k-steps, each a fragment read followed by RTW MFMAs, one per row tile) and
+// independent VALU work (the exp2 sums of another key block): the fragment
+// reads run two k-steps ahead of the MFMAs that use them, and every MFMA is
+// followed by a share of the VALU work, so the wave keeps the matrix core
+// fed while its VALU works and holds only a few fragments at a time.
+template <int KS, int RTW>
+__device__ __forceinline__ void interleave_mfma_valu() {
+  constexpr int kAhead = 2;
+  __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);  // fragment reads
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+#pragma unroll
+    for (int t = 0; t < RTW; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
+    }
+    if (s + kAhead < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // next read
+  }
+}
+
+// Marks the accumulators as rewritten here (an empty asm that takes and
+// returns their registers): work on them stays below this point, so it is
+// not hoisted out of the region that interleaves it with MFMAs.
+template <int N>
+__device__ __forceinline__ void pin_here(f32x16 (&a)[N]) {
+#pragma unroll
+  for (int t = 0; t < N; ++t) asm volatile("" : "+v"(a[t]));
+}
+
 // ------------------------------------------------------------ key tiles ---
 // A tile is 128 keys x D bf16 of one KV head. Threads load it from global
 // memory into registers (16-byte pieces, consecutive threads on consecutive

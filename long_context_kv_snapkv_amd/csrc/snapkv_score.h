@@ -47,7 +47,10 @@ template <int D>
 struct alignas(16) VoteSmem {
   unsigned char ring[2][KTile<D>::BYTES];
   float lse[kMaxRows];
-  float vred[2][2 * kWaves][KTile<D>::KEYS];  // per (row-tile wave, lane half)
+  // column partials per (row-tile wave, lane half), three tiles deep: a
+  // tile's last block may be summed while the next tile is processed
+  float vred[3][2 * kWaves][KTile<D>::KEYS];
+  float vdummy[kThreads];  // destination of the pipeline's empty first slot
   float s_chunk[kMaxChunk + kMaxKernel];  // the chunk plus its pooling halo
   uint32_t top[kTopBins];                 // top-digit histogram of this chunk's pooled keys
 };
@@ -126,7 +129,8 @@ struct KeyGroup {
 // stores (another workgroup of the same kernel reads them). Item 0 of a head
 // clears the head's selection histograms unless CLEAR is false (an item
 // recomputing another item's statistics leaves that to the owner).
-template <int D, int RTW, bool COHERENT, bool DEEP = false, bool CLEAR = true, typename Run>
+template <int D, int RTW, bool COHERENT, bool DEEP = false, bool CLEAR = true, bool PIPE = true,
+          typename Run>
 __device__ __forceinline__ void score_stats_body(const PathParams& p, unsigned char* qbuf,
                                                  float2 (*wstats)[kMaxRowTilesPerWave * 32],
                                                  bf16x8 (&qf)[RTW][D / 16], Run&& run, int b,
@@ -213,27 +217,32 @@ __device__ __forceinline__ void score_stats_body(const PathParams& p, unsigned c
   // The direct sum is computed unconditionally, so it can interleave with
   // the MFMA chain of the next block; with no reference yet (m = -inf) it is
   // +inf or NaN and the block falls to the maximum path.
-  auto update_full = [&](const f32x16& acc, int t) {
+  auto direct_sum = [&](const f32x16& acc, int t) {
     const float m = mrun[t];
     float s4[4];  // short dependent add chains, started by their first terms
 #pragma unroll
     for (int v = 0; v < 4; ++v) s4[v] = exp2_fast(fmaf(acc[v], scale, -m));
 #pragma unroll
     for (int v = 4; v < 16; ++v) s4[v & 3] += exp2_fast(fmaf(acc[v], scale, -m));
-    const float sb = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    return (s4[0] + s4[1]) + (s4[2] + s4[3]);
+  };
+  auto retire = [&](const f32x16& acc, int t, float sb) {
     const bool ok = sb <= kBlockSumCap;  // false for +inf and NaN too
     srun[t] = ok ? srun[t] + sb : srun[t];
     if (!ok) update_max(acc, t);
   };
-  // the MFMA chains of one key block for every row tile of this wave
+  auto update_full = [&](const f32x16& acc, int t) { retire(acc, t, direct_sum(acc, t)); };
+  // the MFMA chains of one key block for every row tile of this wave; the
+  // row tiles' chains alternate, k-step by k-step, so each key fragment is
+  // dead after its RTW uses (each chain sums its k-steps in the same order)
   auto chain_block = [&](f32x16 (&acc)[RTW], const bf16x8 (&kf)[D / 16]) {
 #pragma unroll
-    for (int t = 0; t < RTW; ++t) {
-      acc[t] = f32x16{};
+    for (int t = 0; t < RTW; ++t) acc[t] = f32x16{};
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s)
+    for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+      for (int t = 0; t < RTW; ++t)
         acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[t][s], acc[t], 0, 0, 0);
-    }
   };
   // Software pipeline over this wave's key blocks: the MFMA chains of block
   // n are issued, then the update of block n - 1 runs while they execute.
@@ -248,10 +257,11 @@ __device__ __forceinline__ void score_stats_body(const PathParams& p, unsigned c
     for (int v = 0; v < 16; ++v) pacc[t][v] = -kInf;
   auto compute = [&](const unsigned char* tile, int i) {
     const int tk0 = ks.tile_key(i);
-    if (RTW > 1 && tk0 + KTile<D>::KEYS <= full_end) {
-      // two row tiles: the block's second chain runs under the first
-      // update, and the block is retired within the iteration (a pending
-      // block would not fit the register budget)
+    if (RTW > 1 && !PIPE && tk0 + KTile<D>::KEYS <= full_end) {
+      // the same blocks in the same order, each retired right after its
+      // chains (fewer registers: for the rarely taken recomputation)
+#pragma unroll
+      for (int t = 0; t < RTW; ++t) update_full(pacc[t], t);
       for (int kb = role.wk; kb < KTile<D>::KEYS / 32; kb += role.nwk) {
         f32x16 acc[RTW];
         bf16x8 kf[D / 16];
@@ -259,6 +269,44 @@ __device__ __forceinline__ void score_stats_body(const PathParams& p, unsigned c
         chain_block(acc, kf);
 #pragma unroll
         for (int t = 0; t < RTW; ++t) update_full(acc[t], t);
+      }
+#pragma unroll
+      for (int t = 0; t < RTW; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) pacc[t][v] = -kInf;
+    } else if (RTW > 1 && role.nwk == 1 && tk0 + KTile<D>::KEYS <= full_end) {
+      // Two row tiles, and every wave visits every key block (nwk == 1).
+      // The chains of block kb are issued interleaved with the direct sums
+      // of the pending block (kb - 1, across tiles too), so one wave keeps
+      // both the matrix core and the VALU busy; the pending block is retired
+      // (its rare maximum path included) once the chains are issued. The
+      // pairs' accumulators take turns as the pending one.
+#pragma unroll
+      for (int kb = 0; kb < KTile<D>::KEYS / 32; kb += 2) {
+        f32x16 acc[RTW];
+        float sb[RTW];
+        {
+          pin_here(pacc);
+          bf16x8 kf[D / 16];
+          read_key_frags<D, false>(kf, tile, kb, lane);
+          chain_block(acc, kf);
+#pragma unroll
+          for (int t = 0; t < RTW; ++t) sb[t] = direct_sum(pacc[t], t);
+          interleave_mfma_valu<D / 16, RTW>();
+        }
+#pragma unroll
+        for (int t = 0; t < RTW; ++t) retire(pacc[t], t, sb[t]);
+        {
+          pin_here(acc);
+          bf16x8 kf[D / 16];
+          read_key_frags<D, false>(kf, tile, kb + 1, lane);
+          chain_block(pacc, kf);
+#pragma unroll
+          for (int t = 0; t < RTW; ++t) sb[t] = direct_sum(acc[t], t);
+          interleave_mfma_valu<D / 16, RTW>();
+        }
+#pragma unroll
+        for (int t = 0; t < RTW; ++t) retire(acc[t], t, sb[t]);
       }
     } else if (tk0 + KTile<D>::KEYS <= full_end) {
       for (int kb = role.wk; kb < KTile<D>::KEYS / 32; kb += 2 * role.nwk) {
@@ -526,12 +574,13 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
   constexpr int KEYS = KTile<D>::KEYS;
   const int ntiles = (kv1 - kv0 + KEYS - 1) / KEYS;
   const int nparts = 2 * role.nwr;  // (row-tile wave, lane half) partial sums per key
-  // fold tile i's partials (written before the barrier that precedes tile
-  // i + 1) in a fixed order
+  // fold tile i's partials in a fixed order; they are complete once the
+  // barrier that precedes tile i + 2 has passed (a tile's last block may be
+  // summed during the next tile)
   auto fold = [&](int i) {
     for (int kk = tid; kk < KEYS; kk += kThreads) {
       float s = 0.f;
-      for (int q = 0; q < nparts; ++q) s += sm.vred[i & 1][q][kk];
+      for (int q = 0; q < nparts; ++q) s += sm.vred[i % 3][q][kk];
       sm.s_chunk[i * KEYS + kk] = s;
     }
   };
@@ -557,10 +606,69 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
     }
     return (c4[0] + c4[1]) + (c4[2] + c4[3]);
   };
+  // Two row tiles per wave, every wave visiting every key block: the
+  // chains of block kb are issued interleaved with the column sums of the
+  // pending block (kb - 1, across tiles too), whose partial is stored once
+  // they are done. vacc holds the pending block's logits, vdst where its
+  // partial goes (at first a dummy slot, with -inf logits that sum to 0).
+  f32x16 vacc[RTW];
+#pragma unroll
+  for (int t = 0; t < RTW; ++t)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) vacc[t][v] = -kInf;
+  float* vdst = &sm.vdummy[tid];
+  auto flush_pending = [&] {
+    if constexpr (RTW > 1) {
+      *vdst = colsum(vacc);
+#pragma unroll
+      for (int t = 0; t < RTW; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) vacc[t][v] = -kInf;
+      vdst = &sm.vdummy[tid];
+    }
+  };
   auto compute = [&](const unsigned char* tile, int i) {
     const int tk0 = kv0 + i * KEYS;
-    float* vr = &sm.vred[i & 1][2 * role.wr + (lane >> 5)][lane & 31];
+    float* vr = &sm.vred[i % 3][2 * role.wr + (lane >> 5)][lane & 31];
     constexpr int GB = KeyGroup<RTW>::G;
+    if (RTW > 1 && role.nwk == 1 && tk0 + KEYS <= kv1 && role.my_nrt == RTW) {
+      auto chain = [&](f32x16 (&acc)[RTW], const bf16x8 (&kf)[D / 16]) {
+#pragma unroll
+        for (int t = 0; t < RTW; ++t) acc[t] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+          for (int t = 0; t < RTW; ++t)
+            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[t][s], kf[s], acc[t], 0, 0, 0);
+      };
+#pragma unroll
+      for (int kb = 0; kb < KEYS / 32; kb += 2) {
+        f32x16 acc[RTW];
+        float c;
+        {
+          pin_here(vacc);
+          bf16x8 kf[D / 16];
+          read_key_frags<D, false>(kf, tile, kb, lane);
+          chain(acc, kf);
+          c = colsum(vacc);
+          interleave_mfma_valu<D / 16, RTW>();
+        }
+        *vdst = c;
+        vdst = vr + kb * 32;
+        {
+          pin_here(acc);
+          bf16x8 kf[D / 16];
+          read_key_frags<D, false>(kf, tile, kb + 1, lane);
+          chain(vacc, kf);
+          c = colsum(acc);
+          interleave_mfma_valu<D / 16, RTW>();
+        }
+        *vdst = c;
+        vdst = vr + (kb + 1) * 32;
+      }
+      return;
+    }
+    flush_pending();
     // A tile inside the voted range, with every row tile of this wave present
     // and every group whole, takes a path without per-chain conditions (no
     // accumulators to define for chains that are not run).
@@ -570,6 +678,7 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
         f32x16 acc[GB][RTW];
 #pragma unroll
         for (int g = 0; g < GB; ++g) read_key_frags<D>(kf[g], tile, kb + g * role.nwk, lane);
+        mfma_phase_begin();
 #pragma unroll
         for (int g = 0; g < GB; ++g) {
 #pragma unroll
@@ -580,6 +689,7 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
               acc[g][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[t][s], kf[g][s], acc[g][t], 0, 0, 0);
           }
         }
+        mfma_phase_end();
 #pragma unroll
         for (int g = 0; g < GB; ++g) {
           // the order of colsum below
@@ -624,9 +734,11 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
     }
   };
   ks.run(sm.ring, compute, [&](int i) {
-    if (i > 0) fold(i - 1);
+    if (i > 1) fold(i - 2);
   });
+  flush_pending();
   __syncthreads();
+  if (ntiles > 1) fold(ntiles - 2);
   fold(ntiles - 1);
   __syncthreads();
   // snapkv_pool, staged in LDS: pooled scores of this item's positions
@@ -716,7 +828,7 @@ __device__ __forceinline__ void recompute_missing_stats(const PathParams& p, con
     int bb = b, hh = h;
     asm volatile("" : "+s"(bb), "+s"(hh));
     bf16x8 qf[RTW][D / 16];
-    score_stats_body<D, RTW, true, true, false>(p, qbuf, wstats, qf, run, bb, hh, cc);
+    score_stats_body<D, RTW, true, true, false, false>(p, qbuf, wstats, qf, run, bb, hh, cc);
     __syncthreads();  // the tiles and wstats are reused by the next chunk
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -971,6 +1083,9 @@ __device__ __forceinline__ void snapkv_score_fused_stream_item(const PathParams&
         [&](KeyStream<D>& ks, auto&& compute) { ks.run(sm.st.ring, compute, [](int) {}); }, b,
         h);
   }
+  // opaque copies of the indices: the vote recomputes what it derives from
+  // them instead of holding the statistics pass's values through it
+  asm volatile("" : "+s"(b), "+s"(h), "+s"(c));
   snapkv_score_vote_item<D, RTW, false, true>(p, sm.vt, b, h, c);
 }
 
