@@ -60,6 +60,58 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+SAN_DIR = os.path.join(ROOT, "_build", "sanitize")
+SAN_LIB = os.path.join(SAN_DIR, "libsnapkv_san.so")
+# AddressSanitizer and UndefinedBehaviorSanitizer on the host code only (each
+# -fsanitize= right after -Xarch_host; the device code is built as usual)
+SAN_HOST_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host",
+                  "-fno-sanitize-recover=undefined"]
+
+
+def asan_runtime() -> str:
+    """The AddressSanitizer runtime of ROCm's clang (to preload into a
+    process that loads the sanitized library)."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("clang's AddressSanitizer runtime was not found under /opt/rocm/llvm")
+    return hits[-1]
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """libsnapkv_san.so under _build/sanitize: the host source (argument
+    validation, planning, launches) compiled with ASan and UBSan, linked with
+    the kernels' objects. Returns its path. For host-side tests only: the
+    process must preload asan_runtime()."""
+    os.makedirs(SAN_DIR, exist_ok=True)
+    objs = []
+    for src in sources():
+        if src.endswith(".cpp"):
+            obj = os.path.join(SAN_DIR, os.path.basename(src) + ".o")
+            cmd = [hipcc(), *HIPCC_FLAGS, *SAN_HOST_FLAGS, "-c", src, "-o", obj]
+        else:
+            obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
+            if os.path.exists(obj):
+                objs.append(obj)
+                continue
+            os.makedirs(OBJ_DIR, exist_ok=True)
+            cmd = [hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n" + res.stdout + res.stderr)
+        objs.append(obj)
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host",
+           "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", *objs,
+           "-o", SAN_LIB]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("sanitized link failed:\n" + res.stdout + res.stderr)
+    return SAN_LIB
+
+
 def build(verbose: bool = False) -> str:
     """Compile and link; returns the library path. Always recompiles."""
     os.makedirs(OBJ_DIR, exist_ok=True)
