@@ -27,6 +27,7 @@ from .snapkv_oracle import (  # noqa: F401
     window_vote_from_lse,
 )
 from .decode import attend, decode_compressed, decode_packed  # noqa: F401
+from .prefill import causal_attention, prefill_attention, window_rows  # noqa: F401
 from .kv_quant import (  # noqa: F401
     Fp8Result,
     Int4Result,

@@ -2,7 +2,9 @@
 oracle function (a wrong scale, an off-by-one causal bound, a softmax over
 the prefix only, a wrong GQA mapping, pooling that divides by the in-range
 count, ties to the higher position, truncating quantisation, an unscaled
-decode logit, an exclusive normaliser bound, a flipped normaliser sign) and
+decode logit, an exclusive normaliser bound, a flipped normaliser sign, a
+prefill row that sees the next key, a base-2 normaliser, a strided head
+mapping) and
 checks that at least one of the pins fails on it. Mistakes are planted in
 the oracle, on the CPU, only for the duration of one test.
 """
@@ -189,3 +191,66 @@ def test_truncating_fp8_mutant_is_caught(monkeypatch):
     _patch(monkeypatch, "e4m3_encode", truncating, [oquant, oracle, t_fp8])
     assert _caught(lambda: t_fp8.test_encoding_matches_torch_float8_e4m3fn(),
                    lambda: t_fp8.test_hand_written_encodings())
+
+
+# ------------------------------------------------------------ prefill ------
+import oracle.prefill as oprefill  # noqa: E402
+import test_oracle_prefill as t_prefill  # noqa: E402
+
+
+def _attention_mutant(kind):
+    def mutant(q_rows, k_rows, v_rows):
+        length, d = q_rows.shape
+        scale = 1 / d if kind == "scale_1_over_d" else 1 / np.sqrt(d)
+        logits = (q_rows @ k_rows.T) * scale
+        bound = 1 if kind == "sees_next_key" else 0
+        visible = np.arange(length)[None, :] <= np.arange(length)[:, None] + bound
+        logits = np.where(visible, logits, -np.inf)
+        top = logits.max(axis=1, keepdims=True)
+        e = np.exp(logits - top)
+        s = e.sum(axis=1, keepdims=True)
+        lse = (top + np.log(s))[:, 0]
+        if kind == "log2_normaliser":
+            lse = lse / np.log(2.0)
+        return (e / s) @ v_rows, lse
+    return mutant
+
+
+PREFILL_PINS = [
+    lambda: t_prefill.test_matches_torch_causal_attention(40, 64),
+    lambda: t_prefill.test_zero_queries_give_running_means(),
+    lambda: t_prefill.test_equal_keys_give_running_means_and_shifted_normalisers(),
+    lambda: t_prefill.test_brute_force_tiny(),
+]
+
+
+@pytest.mark.parametrize("mutant", ["scale_1_over_d", "sees_next_key", "log2_normaliser"])
+def test_prefill_pins_catch(monkeypatch, mutant):
+    fn = _attention_mutant(mutant)
+    monkeypatch.setattr(oprefill, "causal_attention", fn)
+    monkeypatch.setattr(oracle, "causal_attention", fn)
+    assert _caught(*PREFILL_PINS)
+
+
+def test_prefill_gqa_pin_catches_a_strided_mapping(monkeypatch):
+    # head q reads KV head q % H_kv instead of q // G
+    def _strided(q_bits, k_bits, v_bits, seq_lens):
+        total, h_q, d = q_bits.shape
+        h_kv = k_bits.shape[1]
+        out = np.zeros((total, h_q, d))
+        lse = np.zeros((total, h_q))
+        off = 0
+        for length in np.asarray(seq_lens).tolist():
+            for q in range(h_q):
+                o, l_ = oprefill.causal_attention(
+                    oracle.bf16_bits_to_f64(q_bits[off:off + length, q]),
+                    oracle.bf16_bits_to_f64(k_bits[off:off + length, q % h_kv]),
+                    oracle.bf16_bits_to_f64(v_bits[off:off + length, q % h_kv]))
+                out[off:off + length, q] = o
+                lse[off:off + length, q] = l_
+            off += length
+        return out, lse
+
+    monkeypatch.setattr(oprefill, "prefill_attention", _strided)
+    monkeypatch.setattr(oracle, "prefill_attention", _strided)
+    assert _caught(t_prefill.test_packed_prompts_and_gqa_mapping)
