@@ -430,9 +430,48 @@ def measure_extras(w, args, dev, stream, sets, outs, ws, timed):
         skv.snapkv_decode_attention(qdec, k, v, ls, out=dout, workspace=ws_f, stream=stream)
 
     dec_ms = {"compressed": timed(dec_comp), "full": timed(dec_full)}
+
+    # the prefill attention whose by-product the compression reads: causal
+    # attention of every prompt row (queries drawn here, N(0, 1/D)), with the
+    # window normalisers and window queries it hands to
+    # snapkv_compress_from_lse; alone, and followed by that compression
+    npre = 2
+    total = sum(lens)
+    qfull = [(torch.randn((total, w.h_q, d), device=dev) / d ** 0.5).to(torch.bfloat16)
+             for _ in range(npre)]
+    pre_out = torch.empty((total, w.h_q, d), dtype=torch.bfloat16, device=dev)
+    pre_lse = torch.empty((batch, w.h_q, w.window), dtype=torch.float32, device=dev)
+    pre_qw = torch.empty((batch, w.h_q, w.window, d), dtype=torch.bfloat16, device=dev)
+
+    def step_pre(i):
+        _, k, v, ls = sets[i % nsets]
+        skv.snapkv_prefill_attention(qfull[i % npre], k, v, ls, w.window, out=pre_out,
+                                     window_lse=pre_lse, q_win=pre_qw, stream=stream)
+
+    def step_pipe(i):
+        step_pre(i)
+        _, k, v, ls = sets[i % nsets]
+        ok, ov, oi = outs[i % 2]
+        skv.snapkv_compress_from_lse(pre_qw, k, v, ls, w.window, pre_lse, w.kernel, w.pool, B,
+                                     out_k=ok, out_v=ov, out_idx=oi, workspace=ws, stream=stream)
+
+    ms_pre = timed(step_pre)
+    ms_pipe = timed(step_pipe)
+    pre_flops = sum(4 * d * w.h_q * L * (L + 1) // 2 for L in lens)
+    del qfull
     dec_bytes = {"compressed": 2 * hkv * sum(n_kept) * d * 2, "full": 2 * hkv * sum(lens) * d * 2}
     del comp
+    pre_tflops = pre_flops / (ms_pre * 1e-3) / 1e12
     return {
+        "prefill": {
+            "note": "snapkv_prefill_attention: causal attention of every prompt row (bf16 MFMA), "
+                    "emitting the window normalisers and queries; then "
+                    "snapkv_compress_from_lse on them",
+            "prefill_ms": round(ms_pre, 4), "prefill_tflops": round(pre_tflops, 1),
+            "prefill_mfma_frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4),
+            "prefill_flops": pre_flops,
+            "prefill_then_compress_ms": round(ms_pipe, 4),
+            "compress_share_of_pipeline": round((ms_pipe - ms_pre) / ms_pipe, 4)},
         "from_lse": {"ms_per_step": round(ms_lse, 5),
                      "value": round(sum(lens) / (ms_lse * 1e-3), 1), "unit": "tokens/s/layer",
                      "note": "snapkv_compress_from_lse: window-row log-sum-exp supplied by "

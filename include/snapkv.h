@@ -437,6 +437,43 @@ int32_t snapkv_decode_attention(int32_t batch, int32_t num_q_heads,
                                 float* out, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/*
+ * Prefill attention with the window normalisers as a by-product, for a
+ * caller without a prefill kernel of its own (glossary page
+ * "SnapKV(スナップケーブイ)", FAQ Q3: the window scores can come out of the
+ * ordinary prefill attention at almost no extra cost). Causal attention of
+ * every prompt row at scale 1/sqrt(D), computed with bf16 MFMAs and float32
+ * softmax and accumulation: for prompt b, query head q of KV head h = q / G
+ * and row i,
+ *
+ *   out[i] = sum_{j <= i} softmax_j(q_i . k_j / sqrt(D)) v_j
+ *
+ *   q        device bf16 [T, H_q, D], the prompts' queries packed back to back
+ *   k, v     device bf16 [T, H_kv, D] (as for snapkv_compress)
+ *   out      device bf16 [T, H_q, D] (each row rounded once to bf16)
+ *   window_lse  device float32 [batch, H_q, W] or NULL: for the last W rows
+ *            of each prompt (row L - W + i), the natural log of
+ *            sum_{j <= row} exp(q . k_j / sqrt(D)), exactly the input of
+ *            snapkv_compress_from_lse; NaN for rows before a prompt's start
+ *            (L < W). 4-byte aligned.
+ *   q_win    device bf16 [batch, H_q, W, D] or NULL: copies of those rows'
+ *            queries, the q_win argument of the compression calls (zero
+ *            rows before a prompt's start).
+ *   window   W >= 1 when window_lse or q_win is given (ignored otherwise)
+ *
+ * One kernel on `stream`; repeated calls give identical bits. Conventions
+ * and errors as for snapkv_compress: SNAPKV_ERR_INVALID_ARGUMENT for null or
+ * misaligned pointers, a bad batch, head counts or seq_len, or window < 1
+ * with a window output; SNAPKV_ERR_UNSUPPORTED for head_dim not in {64, 128}
+ * or batch * num_q_heads > 65535; SNAPKV_ERR_HIP when the launch fails.
+ */
+int32_t snapkv_prefill_attention(int32_t batch, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim,
+                                 const void* q, const void* k, const void* v,
+                                 const int32_t* seq_lens, int32_t window,
+                                 void* out, float* window_lse, void* q_win,
+                                 void* stream);
+
 /* Static text of a status code ("ok", "invalid argument", ...). */
 const char* snapkv_status_string(int32_t status);
 

@@ -34,6 +34,7 @@ from .snapkv import (  # noqa: F401
     snapkv_decode_attention,
     snapkv_decode_workspace_size,
     snapkv_last_error,
+    snapkv_prefill_attention,
     snapkv_gather_selects,
     snapkv_score_kernels,
     snapkv_stage_name,

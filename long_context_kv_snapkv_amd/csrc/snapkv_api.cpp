@@ -15,6 +15,7 @@
 #include "snapkv.h"
 #include "snapkv_decode.h"
 #include "snapkv_kernels.h"
+#include "snapkv_prefill.h"
 
 static_assert(SNAPKV_STATIC_SCRATCH_BYTES == snapkv::kStaticScratchBytes,
               "static scratch size in the header and the library");
@@ -767,6 +768,62 @@ int32_t snapkv_decode_attention(int32_t batch, int32_t num_q_heads, int32_t num_
   std::memcpy(p.len, pl.len, sizeof(p.len));
   const hipError_t e = snapkv::launch_decode(p, head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "snapkv_decode launch");
+  return SNAPKV_OK;
+}
+
+int32_t snapkv_prefill_attention(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, const void* q, const void* k, const void* v,
+                                 const int32_t* seq_lens, int32_t window, void* out,
+                                 float* window_lse, void* q_win, void* stream) {
+  if (!q || !k || !v || !out) return fail(SNAPKV_ERR_INVALID_ARGUMENT, "a tensor pointer is NULL");
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) ||
+      (q_win != nullptr && misaligned(q_win)))
+    return fail(SNAPKV_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+  if (window_lse != nullptr && (reinterpret_cast<uintptr_t>(window_lse) & 3u) != 0)
+    return fail(SNAPKV_ERR_INVALID_ARGUMENT, "window_lse must be 4-byte aligned");
+  if (seq_lens == nullptr) return fail(SNAPKV_ERR_INVALID_ARGUMENT, "seq_lens is NULL");
+  if (batch < 1 || batch > SNAPKV_MAX_BATCH)
+    return fail(SNAPKV_ERR_INVALID_ARGUMENT,
+                "batch must be in [1, " + std::to_string(SNAPKV_MAX_BATCH) + "]");
+  if (num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0)
+    return fail(SNAPKV_ERR_INVALID_ARGUMENT,
+                "num_q_heads must be a positive multiple of num_kv_heads");
+  if ((window_lse != nullptr || q_win != nullptr) && window < 1)
+    return fail(SNAPKV_ERR_INVALID_ARGUMENT, "window must be >= 1 when its outputs are asked for");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(SNAPKV_ERR_UNSUPPORTED, "head_dim must be 64 or 128, got " +
+                                            std::to_string(head_dim));
+  if ((int64_t)batch * num_q_heads > 65535)
+    return fail(SNAPKV_ERR_UNSUPPORTED, "batch * num_q_heads must be <= 65535");
+  snapkv::PrefillParams p{};
+  int64_t total = 0;
+  int l_max = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int32_t L = seq_lens[b];
+    if (L < 1)
+      return fail(SNAPKV_ERR_INVALID_ARGUMENT,
+                  "seq_lens[" + std::to_string(b) + "] must be >= 1, got " + std::to_string(L));
+    p.tab.off[b] = (int32_t)total;
+    p.tab.len[b] = L;
+    total += L;
+    if (total > INT32_MAX) return fail(SNAPKV_ERR_INVALID_ARGUMENT, "more than 2^31-1 tokens");
+    l_max = L > l_max ? L : l_max;
+  }
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.out = static_cast<uint16_t*>(out);
+  p.window_lse = window_lse;
+  p.q_win = static_cast<uint16_t*>(q_win);
+  p.batch = batch;
+  p.hq = num_q_heads;
+  p.hkv = num_kv_heads;
+  p.group = num_q_heads / num_kv_heads;
+  p.window = window_lse != nullptr || q_win != nullptr ? window : 0;
+  p.nqb = (l_max + snapkv::kPrefillRows - 1) / snapkv::kPrefillRows;
+  p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+  const hipError_t e = snapkv::launch_prefill(p, head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "snapkv_prefill launch");
   return SNAPKV_OK;
 }
 

@@ -139,12 +139,12 @@ __device__ __forceinline__ void mfma_phase_end() {
 // Scheduling hint for a region holding the MFMA chains of one key block (KS
 // k-steps, each a fragment read followed by RTW MFMAs, one per row tile) and
 // independent VALU work (the exp2 sums of another key block): the fragment
-// reads run two k-steps ahead of the MFMAs that use them, and every MFMA is
+// reads run four k-steps ahead of the MFMAs that use them, and every MFMA is
 // followed by a share of the VALU work, so the wave keeps the matrix core
 // fed while its VALU works and holds only a few fragments at a time.
 template <int KS, int RTW>
 __device__ __forceinline__ void interleave_mfma_valu() {
-  constexpr int kAhead = 2;
+  constexpr int kAhead = 4;
   __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);  // fragment reads
 #pragma unroll
   for (int s = 0; s < KS; ++s) {

@@ -84,6 +84,9 @@ def load_library():
     lib.snapkv_compress_static.argtypes = [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _pi32, _i32,
                                            _i32, _i32, _i32, _vp, _vp, _vp, _vp]
     lib.snapkv_compress_static.restype = _i32
+    lib.snapkv_prefill_attention.argtypes = [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _pi32, _i32,
+                                             _vp, _vp, _vp, _vp]
+    lib.snapkv_prefill_attention.restype = _i32
     lib.snapkv_compress_int4.argtypes = [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _pi32, _i32, _vp,
                                          _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                          _vp]
@@ -309,6 +312,53 @@ def snapkv_compress_static(q_win: torch.Tensor, k: torch.Tensor, v: torch.Tensor
                                       _ptr(out_k), _ptr(out_v), _ptr(out_idx),
                                       _stream(stream, dev)))
     return out_k, out_v, out_idx
+
+
+def snapkv_prefill_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                             seq_lens: Sequence[int], window: int = 0, *,
+                             out: Optional[torch.Tensor] = None,
+                             window_lse: Optional[torch.Tensor] = None,
+                             q_win: Optional[torch.Tensor] = None, stream=None):
+    """Causal prefill attention of packed prompts q [T, H_q, D] over k, v
+    [T, H_kv, D]. Returns (out, window_lse, q_win): out bf16 [T, H_q, D];
+    with window > 0 also the last `window` rows' natural-log normalisers
+    float32 [batch, H_q, W] and their queries bf16 [batch, H_q, W, D] (the
+    inputs of snapkv_compress_from_lse), else None for both; see
+    include/snapkv.h."""
+    lib = load_library()
+    _check_tensor("q", q, 3)
+    _check_tensor("k", k, 3)
+    _check_tensor("v", v, 3)
+    arr, vals = _lens(seq_lens)
+    total, hq, d = q.shape
+    if k.shape != v.shape or k.shape[0] != total or k.shape[2] != d:
+        raise ValueError("q, k and v must be [T, H_q, D] and [T, H_kv, D]")
+    if total != sum(vals):
+        raise ValueError("q rows must equal sum(seq_lens)")
+    hkv = k.shape[1]
+    batch = len(vals)
+    dev = q.device
+    if out is None:
+        out = torch.empty((total, hq, d), dtype=torch.bfloat16, device=dev)
+    _check_tensor("out", out, 3)
+    if tuple(out.shape) != (total, hq, d):
+        raise ValueError("out must be [T, H_q, D]")
+    if window > 0:
+        if window_lse is None:
+            window_lse = torch.empty((batch, hq, window), dtype=torch.float32, device=dev)
+        if q_win is None:
+            q_win = torch.empty((batch, hq, window, d), dtype=torch.bfloat16, device=dev)
+        _check_tensor("window_lse", window_lse, 3, torch.float32)
+        _check_tensor("q_win", q_win, 4)
+        if tuple(window_lse.shape) != (batch, hq, window) or \
+                tuple(q_win.shape) != (batch, hq, window, d):
+            raise ValueError("window_lse / q_win must be [batch, H_q, W] / [batch, H_q, W, D]")
+    else:
+        window_lse = q_win = None
+    _check(lib.snapkv_prefill_attention(batch, hq, hkv, d, _ptr(q), _ptr(k), _ptr(v), arr,
+                                        window, _ptr(out), _ptr(window_lse), _ptr(q_win),
+                                        _stream(stream, dev)))
+    return out, window_lse, q_win
 
 
 def snapkv_compress_with_scores(q_win: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

@@ -22,7 +22,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = skv.header_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     assert "snapkv_compress_staged" in names
     assert "snapkv_compress_with_scores" in names
     assert "snapkv_compress_static" in names
@@ -164,6 +164,24 @@ def test_compress_static_rejects_before_any_device_call(lib):
     # every benchmark workload fits the area
     for lens, hq, w in (([131072], 64, 64), ([32768] * 8, 32, 64), ([16384], 32, 32)):
         assert skv.snapkv_workspace_size(hq, 8, 128, lens, w) <= skv.SNAPKV_STATIC_SCRATCH_BYTES
+
+
+def test_prefill_attention_validation(lib):
+    def call(lens=(100,), hq=4, hkv=2, d=128, q=FAKE, out=FAKE, window=8, lse=FAKE, qw=FAKE):
+        arr = (ctypes.c_int32 * max(1, len(lens)))(*lens)
+        return lib.snapkv_prefill_attention(len(lens), hq, hkv, d, q, FAKE, FAKE, arr, window,
+                                            out, lse, qw, None)
+
+    assert call(q=None) == 1 and "NULL" in skv.snapkv_last_error()
+    assert call(out=FAKE + 8) == 1
+    assert call(qw=FAKE + 8) == 1
+    assert call(lse=FAKE + 2) == 1 and "window_lse" in skv.snapkv_last_error()
+    assert call(lens=()) == 1
+    assert call(lens=(5, 0)) == 1
+    assert call(hq=6, hkv=4) == 1
+    assert call(window=0) == 1 and "window" in skv.snapkv_last_error()
+    assert call(d=96) == 2
+    assert call(lens=(10,) * 256, hq=512, hkv=8) == 2
 
 
 def test_compress_int4_validation(lib):

@@ -99,8 +99,11 @@ def test_cpu_baseline_splits_a_layer_into_one_job_per_kv_head():
 
 
 def test_source_hash_covers_every_kernel_source():
+    # every source of the compression kernels (the decode and prefill
+    # attention kernels are separate launches with no counters recorded)
     csrc = os.path.join(ROOT, "long_context_kv_snapkv_amd", "csrc")
     device_sources = {f for f in os.listdir(csrc) if f.startswith("snapkv_")
-                      and f.endswith((".h", ".hip", ".cpp")) and "decode" not in f}
+                      and f.endswith((".h", ".hip", ".cpp")) and "decode" not in f
+                      and "prefill" not in f}
     missing = device_sources - set(bench.KERNEL_SOURCES)
     assert not missing, missing
