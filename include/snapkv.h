@@ -411,10 +411,17 @@ int32_t snapkv_window_scores(int32_t batch, int32_t num_q_heads,
  *   cache_lens  HOST int32[batch], each >= 1 (and <= capacity when compressed)
  *   out      device float32 [batch, H_q, D]
  *   workspace   at least snapkv_decode_workspace_size bytes (per-chunk
- *            partial softmax; no initialisation, not shared by calls in flight)
+ *            partial softmax and done marks; no initialisation, not shared
+ *            by calls in flight)
  *
- * Two kernels on `stream`; computed in float32 from the bf16 inputs with
- * fixed summation orders (repeated calls give identical bits). Conventions
+ * Rows are split into chunks (a multiple of 128 rows, about 1024 chunk items
+ * per call). When no prompt has more than 16 chunks (a compressed cache) the
+ * step is one kernel: each chunk item publishes its partial and a done mark
+ * tagged with the call, and an item that finds all marks of its head merges
+ * the head's chunks (no item waits for another); otherwise two kernels,
+ * chunk partials then a merge (snapkv_decode_kernels reports which). Both forms
+ * compute in float32 from the bf16 inputs with the same fixed summation
+ * orders, so they give identical bits, and so do repeated calls. Conventions
  * and error behaviour as for snapkv_compress: SNAPKV_ERR_INVALID_ARGUMENT
  * for null or misaligned pointers, batch outside [1, SNAPKV_MAX_BATCH], bad
  * head counts, an unknown layout, a cache length < 1 or above capacity;
@@ -436,6 +443,32 @@ int32_t snapkv_decode_attention(int32_t batch, int32_t num_q_heads,
                                 int32_t capacity, const int32_t* cache_lens,
                                 float* out, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/*
+ * snapkv_decode_attention with the step's device time: start_event and
+ * stop_event (hipEvent_t created by the caller, or NULL) are recorded by the
+ * dispatches themselves at the first kernel's start and the last kernel's
+ * end, so hipEventElapsedTime between them is the step's GPU time, free of
+ * host launch cost. Same arguments, results and errors otherwise.
+ */
+int32_t snapkv_decode_attention_timed(int32_t batch, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim,
+                                      const void* q, const void* k_cache,
+                                      const void* v_cache, int32_t layout,
+                                      int32_t capacity, const int32_t* cache_lens,
+                                      float* out, void* workspace,
+                                      size_t workspace_bytes, void* stream,
+                                      void* start_event, void* stop_event);
+
+/*
+ * How many kernels snapkv_decode_attention launches for this shape (1 or 2,
+ * into *kernels), without launching anything. Errors as for
+ * snapkv_decode_workspace_size.
+ */
+int32_t snapkv_decode_kernels(int32_t batch, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim,
+                              int32_t layout, int32_t capacity,
+                              const int32_t* cache_lens, int32_t* kernels);
 
 /*
  * Prefill attention with the window normalisers as a by-product, for a

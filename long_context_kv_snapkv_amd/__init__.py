@@ -32,6 +32,9 @@ from .snapkv import (  # noqa: F401
     snapkv_compress_static,
     snapkv_compress_with_scores,
     snapkv_decode_attention,
+    snapkv_decode_kernels,
+    prepare_decode,
+    DecodeStep,
     snapkv_decode_workspace_size,
     snapkv_last_error,
     snapkv_prefill_attention,

@@ -465,10 +465,13 @@ int32_t compress_impl(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const v
 }
 
 // Decode step: rows per prompt, chunking and workspace, from shapes alone.
-//   part  float[batch * H_kv, nchunk, G, D + 2]  per-chunk partial softmax
+//   part     float[batch * H_kv, nchunk, G, D + 2]  per-chunk partial softmax
+//   flags    uint64[batch * H_kv, 16]              one-launch form's chunk marks
+// The one-launch form is taken when no prompt has more than
+// kDecodeFusedMaxChunks chunks (SNAPKV_NO_FUSED_DECODE turns it off).
 struct DecodePlan {
-  int batch, hq, hkv, d, group, layout, capacity, chunk, nchunk;
-  size_t bytes;
+  int batch, hq, hkv, d, group, layout, capacity, chunk, nchunk, fused;
+  size_t off_flags, bytes;
   int32_t off[snapkv::kMaxBatch], len[snapkv::kMaxBatch];
 };
 
@@ -526,7 +529,11 @@ int32_t make_decode_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t d, int3
   if (chunk > 8192) chunk = 8192;
   pl->chunk = (int)chunk;
   pl->nchunk = (int)((n_max + chunk - 1) / chunk);
-  pl->bytes = align_up((size_t)batch * hkv * pl->nchunk * pl->group * (d + 2) * sizeof(float),
+  pl->fused = pl->nchunk <= snapkv::kDecodeFusedMaxChunks && !env_flag("SNAPKV_NO_FUSED_DECODE");
+  pl->off_flags = align_up(
+      (size_t)batch * hkv * pl->nchunk * pl->group * (d + 2) * sizeof(float), 256);
+  pl->bytes = align_up(pl->off_flags + (size_t)batch * hkv * snapkv::kDecodeFusedMaxChunks *
+                                           sizeof(uint64_t),
                        256);
   return SNAPKV_OK;
 }
@@ -733,11 +740,24 @@ int32_t snapkv_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t
   return SNAPKV_OK;
 }
 
-int32_t snapkv_decode_attention(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                                int32_t head_dim, const void* q, const void* k_cache,
-                                const void* v_cache, int32_t layout, int32_t capacity,
-                                const int32_t* cache_lens, float* out, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+int32_t snapkv_decode_kernels(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t layout, int32_t capacity,
+                              const int32_t* cache_lens, int32_t* kernels) {
+  if (kernels == nullptr) return fail(SNAPKV_ERR_INVALID_ARGUMENT, "kernels is NULL");
+  DecodePlan pl;
+  const int32_t st = make_decode_plan(batch, num_q_heads, num_kv_heads, head_dim, layout,
+                                      capacity, cache_lens, &pl);
+  if (st != SNAPKV_OK) return st;
+  *kernels = pl.fused ? 1 : 2;
+  return SNAPKV_OK;
+}
+
+int32_t snapkv_decode_attention_timed(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, const void* q, const void* k_cache,
+                                      const void* v_cache, int32_t layout, int32_t capacity,
+                                      const int32_t* cache_lens, float* out, void* workspace,
+                                      size_t workspace_bytes, void* stream, void* start_event,
+                                      void* stop_event) {
   if (!q || !k_cache || !v_cache || !out)
     return fail(SNAPKV_ERR_INVALID_ARGUMENT, "a tensor pointer is NULL");
   if (misaligned(q) || misaligned(k_cache) || misaligned(v_cache) || misaligned(out))
@@ -763,12 +783,27 @@ int32_t snapkv_decode_attention(int32_t batch, int32_t num_q_heads, int32_t num_
   p.nchunk = pl.nchunk;
   p.layout = pl.layout;
   p.capacity = pl.capacity;
+  p.fused = pl.fused;
+  p.flags = reinterpret_cast<uint64_t*>(static_cast<unsigned char*>(workspace) + pl.off_flags);
+  p.epoch = next_epoch();
   p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
   std::memcpy(p.off, pl.off, sizeof(p.off));
   std::memcpy(p.len, pl.len, sizeof(p.len));
-  const hipError_t e = snapkv::launch_decode(p, head_dim, static_cast<hipStream_t>(stream));
+  const hipError_t e =
+      snapkv::launch_decode(p, head_dim, static_cast<hipStream_t>(stream),
+                            static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event));
   if (e != hipSuccess) return hip_fail(e, "snapkv_decode launch");
   return SNAPKV_OK;
+}
+
+int32_t snapkv_decode_attention(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, const void* q, const void* k_cache,
+                                const void* v_cache, int32_t layout, int32_t capacity,
+                                const int32_t* cache_lens, float* out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return snapkv_decode_attention_timed(batch, num_q_heads, num_kv_heads, head_dim, q, k_cache,
+                                       v_cache, layout, capacity, cache_lens, out, workspace,
+                                       workspace_bytes, stream, nullptr, nullptr);
 }
 
 int32_t snapkv_prefill_attention(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

@@ -13,6 +13,9 @@ constexpr int kDecodeThreads = 256;  // 4 wave64s per workgroup
 constexpr int kDecodeMaxGroup = 8;   // query heads per KV head
 constexpr int kDecodeRowQuantum = 128;  // chunk sizes are multiples of this
 constexpr int kDecodeMergeThreads = 1024;
+// at most this many chunks per (prompt, KV head): one launch, a chunk item
+// that finds every chunk of its head done merges them
+constexpr int kDecodeFusedMaxChunks = 16;
 
 // One decode step over a cache. Rows of (prompt b, KV head h) start at
 //   compressed: k + ((b * hkv + h) * capacity) * D, consecutive rows D apart;
@@ -24,6 +27,9 @@ struct DecodeParams {
   float* out;         // float32 [batch, hq, D]
   float* part;        // [batch * hkv, nchunk, group, D + 2]: per chunk and query
                       // head (max in log2 units, sum of weights, weighted V sum)
+  uint64_t* flags;    // [batch * hkv, kDecodeFusedMaxChunks] one-launch form: chunk done marks
+  uint64_t epoch;     // this call's mark (new per call)
+  int32_t fused;      // one launch (every prompt has at most kDecodeFusedMaxChunks chunks)
   int32_t batch, hq, hkv, group;
   int32_t chunk;      // cache rows per work item (a multiple of kDecodeRowQuantum)
   int32_t nchunk;     // chunk slots per (prompt, head) in part
@@ -35,7 +41,10 @@ struct DecodeParams {
 };
 
 // Partial attention per chunk of rows, then the per-(prompt, head) merge
-// that writes out.
-hipError_t launch_decode(const DecodeParams& p, int head_dim, hipStream_t stream);
+// that writes out: in one launch when p.fused, else two. The events, if not
+// null, are recorded by the dispatches at the first kernel's start and the
+// last kernel's end.
+hipError_t launch_decode(const DecodeParams& p, int head_dim, hipStream_t stream,
+                         hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
 }  // namespace snapkv

@@ -7,7 +7,8 @@
 //   out[b, q] = sum_t softmax_t(q_dec . k_t / sqrt(D)) v_t  over the cached rows
 //
 // The step streams each row of K and V once, so it is bound by HBM. Two
-// kernels:
+// kernels, or the first alone when every prompt's rows form few chunks (a
+// compressed cache):
 //
 //   snapkv_decode_partial  (chunk, KV head, prompt)  one chunk of rows for all
 //                          G query heads of the KV head, in tiles of 16 rows
@@ -23,6 +24,18 @@
 //                          partial goes to the workspace;
 //   snapkv_decode_merge    (query head of the group, KV head, prompt)
 //                          merges the chunks in a fixed order and writes out.
+//
+// In the one-launch form a prompt of one chunk writes out directly. For
+// more chunks each chunk item stores its partial with device-coherent
+// stores and waits until they are acknowledged, then stores its chunk's
+// done mark (this call's epoch) the same way, waits for that too, and reads
+// the marks of all chunks of its head. An item that finds every mark merges
+// the head's chunks (device-coherent loads) in the merge kernel's order, so
+// both forms give the same bits; the others end. Since every item's mark is
+// at the coherence point before it reads the others', the item whose reads
+// come last finds them all: at least one item merges (two that finish
+// together may both merge, writing the same bits). Nothing waits, and the
+// marks carry the call's epoch, so they need no clearing between calls.
 //
 // Logits are taken in log2 units (q pre-scaled by log2(e)/sqrt(D)); every
 // sum has a fixed order, so results are bit-reproducible.
@@ -71,7 +84,74 @@ __device__ __forceinline__ float group_max(float x) {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <int D, int GM>
+__device__ __forceinline__ void store_coherent(float* a, float x) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(a), __float_as_uint(x), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float load_coherent(const float* a) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<float*>(a)),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// One chunk's (max, sum of weights, weighted sum) folded into a running
+// triple: the merge's arithmetic, shared by both forms.
+__device__ __forceinline__ void fold_chunk(float& rm, float& rl, float& ra, float mc, float lc,
+                                           float ac) {
+  if (rm == -kInf) {  // the first chunk (finite max): what the general step gives, exactly
+    rm = mc;
+    rl = lc;
+    ra = ac;
+    return;
+  }
+  const float mx = fmaxf(rm, mc);
+  const float fr = exp2_fast(rm - mx), fc = exp2_fast(mc - mx);
+  rl = fmaf(rl, fr, lc * fc);
+  ra = fmaf(ra, fr, ac * fc);
+  rm = mx;
+}
+
+// The slices' running triples combined in order, and the output element.
+template <int S>
+__device__ __forceinline__ float combine_slices(const float (&sm)[S], const float (&sl)[S],
+                                                const float (&sa)[S]) {
+  float mx = -kInf;
+#pragma unroll
+  for (int s = 0; s < S; ++s) mx = fmaxf(mx, sm[s]);
+  float a = 0.f, l = 0.f;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    if (sm[s] == -kInf) continue;  // a slice without chunks
+    const float f = exp2_fast(sm[s] - mx);
+    a = fmaf(sa[s], f, a);
+    l = fmaf(sl[s], f, l);
+  }
+  return a / l;
+}
+
+// The merge of one output element of query head g over nch <= C chunk
+// partials, in the merge kernel's order: slice s folds chunks s, s + S, ...,
+// then the slices combine in order. (max, sum) pairs come from LDS, the
+// weighted sums from registers (all loaded before this runs).
+template <int D, int C, int GM>
+__device__ __forceinline__ float merge_loaded(const float2 (*mlc)[GM], int g, const float (&a)[C],
+                                              int nch) {
+  constexpr int S = kDecodeMergeThreads / D;
+  float sm[S], sl[S], sa[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    float rm = -kInf, rl = 0.f, ra = 0.f;
+#pragma unroll
+    for (int c = s; c < C; c += S)
+      if (c < nch) fold_chunk(rm, rl, ra, mlc[c][g].x, mlc[c][g].y, a[c]);
+    sm[s] = rm;
+    sl[s] = rl;
+    sa[s] = ra;
+  }
+  return combine_slices<S>(sm, sl, sa);
+}
+
+template <int D, int GM, bool FUSED>
 __global__ void __launch_bounds__(kDecodeThreads) snapkv_decode_partial(const DecodeParams p) {
   constexpr int PIECES = D / 8;         // lanes per row in the row layout
   constexpr int RPI = 64 / PIECES;      // rows per wave instruction in the row layout
@@ -87,31 +167,42 @@ __global__ void __launch_bounds__(kDecodeThreads) snapkv_decode_partial(const De
   __shared__ float sm_ml[NG][GM][2];
   __shared__ float sm_acc[NG][GM][D];
   __shared__ float sm_f[NG][GM];
+  __shared__ float sm_l[GM];  // one-chunk prompts of the one-launch form: sum of weights
+  __shared__ float2 sm_mlc[FUSED ? kDecodeFusedMaxChunks : 1][GM];  // the merging item's (max, sum)
   static_assert(NG == 16 || NG == 32, "lane groups per workgroup");
 
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int n = p.len[b];
-  const int r0 = c * p.chunk;
+  // the kernel arguments the item starts with, requested together: one
+  // scalar round trip instead of one per branch that depends on them
+  const int n = p.len[b], off_b = p.off[b], chunk = p.chunk, layout = p.layout;
+  const int capacity = p.capacity, hkv = p.hkv, hq = p.hq, group = p.group;
+  const uint16_t *pq = p.q, *pk = p.k, *pv = p.v;
+  asm volatile("" ::"s"(n), "s"(off_b), "s"(chunk), "s"(layout), "s"(capacity), "s"(hkv), "s"(hq),
+               "s"(group), "s"(pq), "s"(pk), "s"(pv));
+  const int r0 = c * chunk;
   if (r0 >= n) return;
-  const int r1 = min(r0 + p.chunk, n);
+  const int r1 = min(r0 + chunk, n);
+  const int nch = (n + chunk - 1) / chunk;
+  // the one-launch form writes out directly when the prompt has one chunk
+  const bool direct = FUSED && nch == 1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int piece = lane % PIECES, grp = lane / PIECES, gi = wave * RPI + grp;
   const int mrow = lane % 16, mk = lane / 16;  // MFMA operand layout
   size_t base, rs;
-  if (p.layout == 0) {
-    base = (size_t)(b * p.hkv + h) * p.capacity * D;
+  if (layout == 0) {
+    base = (size_t)(b * hkv + h) * capacity * D;
     rs = D;
   } else {
-    base = ((size_t)p.off[b] * p.hkv + h) * D;
-    rs = (size_t)p.hkv * D;
+    base = ((size_t)off_b * hkv + h) * D;
+    rs = (size_t)hkv * D;
   }
-  const uint16_t* kbase = p.k + base + mk * 8;
-  const uint16_t* vbase = p.v + base + piece * 8;
+  const uint16_t* kbase = pk + base + mk * 8;
+  const uint16_t* vbase = pv + base + piece * 8;
 
   // Q^T as the MFMA B operand: query mrow, elements kb * 32 + 8 * mk + e
   // (slots past the group repeat its last query; their results are unused)
   u32x4 qop[KB];
-  const uint16_t* qrow = p.q + (size_t)(b * p.hq + h * p.group + min(mrow, p.group - 1)) * D;
+  const uint16_t* qrow = pq + (size_t)(b * hq + h * group + min(mrow, group - 1)) * D;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) qop[kb] = *reinterpret_cast<const u32x4*>(qrow + kb * 32 + mk * 8);
 
@@ -250,17 +341,71 @@ __global__ void __launch_bounds__(kDecodeThreads) snapkv_decode_partial(const De
     sm_f[w][g] = f;
     const float lsum = group_sum<NG>(f * sm_ml[w][g][1]);
     if (w == 0 && g < p.group) {
-      dst[g * (D + 2)] = mx;
-      dst[g * (D + 2) + 1] = lsum;
+      if (direct) {
+        sm_l[g] = lsum;
+      } else if (FUSED) {
+        store_coherent(&dst[g * (D + 2)], mx);
+        store_coherent(&dst[g * (D + 2) + 1], lsum);
+      } else {
+        dst[g * (D + 2)] = mx;
+        dst[g * (D + 2) + 1] = lsum;
+      }
     }
   }
   __syncthreads();
+  float* out = p.out + (size_t)(b * p.hq + h * p.group) * D;
   for (int i = tid; i < p.group * D; i += kDecodeThreads) {
     const int g = i / D, d = i % D;
     float sa = 0.f;
 #pragma unroll
     for (int w = 0; w < NG; ++w) sa = fmaf(sm_f[w][g], sm_acc[w][g][d], sa);
-    dst[g * (D + 2) + 2 + d] = sa;
+    if (direct)
+      out[i] = sa / sm_l[g];  // the merge of a single chunk, exactly
+    else if (FUSED)
+      store_coherent(&dst[g * (D + 2) + 2 + d], sa);
+    else
+      dst[g * (D + 2) + 2 + d] = sa;
+  }
+  if constexpr (FUSED) {
+    if (direct) return;
+    // this item's partial is at the coherence point before its mark, and its
+    // mark before it reads the others' (wave 0 does both)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    uint64_t* marks = p.flags + (size_t)(b * p.hkv + h) * kDecodeFusedMaxChunks;
+    if (tid == 0) __hip_atomic_store(&marks[c], p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    int missing = 0;
+    if (tid < nch)
+      missing = __hip_atomic_load(&marks[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != p.epoch;
+    if (__syncthreads_or(missing)) return;
+    // every chunk's partial was acknowledged before its mark, and these
+    // loads are issued after the marks were read. All of them are in flight
+    // at once: each thread's weighted sums into registers, the (max, sum)
+    // pairs of every (chunk, query head) into LDS.
+    constexpr int C = kDecodeFusedMaxChunks;
+    constexpr int KO = (GM * D + kDecodeThreads - 1) / kDecodeThreads;
+    const size_t cstride = (size_t)p.group * (D + 2);
+    const float* col0 = p.part + (size_t)(b * p.hkv + h) * p.nchunk * cstride;
+    float av[KO][C];
+#pragma unroll
+    for (int o = 0; o < KO; ++o) {
+      const int i = tid + o * kDecodeThreads;
+      const int g = min(i / D, p.group - 1), d = i % D;  // past the group: an unused in-range load
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+        av[o][c] = c < nch ? load_coherent(col0 + c * cstride + g * (D + 2) + 2 + d) : 0.f;
+    }
+    for (int j = tid; j < nch * p.group; j += kDecodeThreads) {
+      const float* e = col0 + (j / p.group) * cstride + (j % p.group) * (D + 2);
+      sm_mlc[j / p.group][j % p.group] = make_float2(load_coherent(e), load_coherent(e + 1));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int o = 0; o < KO; ++o) {
+      const int i = tid + o * kDecodeThreads;
+      if (i < p.group * D) out[i] = merge_loaded<D, C, GM>(sm_mlc, i / D, av[o], nch);
+    }
   }
 }
 
@@ -280,13 +425,7 @@ __global__ void __launch_bounds__(kDecodeMergeThreads) snapkv_decode_merge(const
   const float* col = p.part + (size_t)(b * p.hkv + h) * p.nchunk * cstride + g * (D + 2);
   const int tid = threadIdx.x, d = tid % D, sl = tid / D;
   float rm = -kInf, rl = 0.f, ra = 0.f;
-  auto fold = [&](float mc, float lc, float ac) {
-    const float mx = fmaxf(rm, mc);
-    const float fr = exp2_fast(rm - mx), fc = exp2_fast(mc - mx);
-    rl = rl * fr + lc * fc;
-    ra = ra * fr + ac * fc;
-    rm = mx;
-  };
+  auto fold = [&](float mc, float lc, float ac) { fold_chunk(rm, rl, ra, mc, lc, ac); };
   int c = sl;
   for (; c + (U - 1) * S < nch; c += U * S) {
     float mc[U], lc[U], ac[U];
@@ -309,47 +448,60 @@ __global__ void __launch_bounds__(kDecodeMergeThreads) snapkv_decode_merge(const
   red_a[tid] = ra;
   __syncthreads();
   if (sl == 0) {
-    float mx = -kInf;
-#pragma unroll
-    for (int s2 = 0; s2 < S; ++s2) mx = fmaxf(mx, red_m[s2 * D + d]);
-    float a = 0.f, l = 0.f;
+    float ms[S], ls[S], as[S];
 #pragma unroll
     for (int s2 = 0; s2 < S; ++s2) {
-      const float ms = red_m[s2 * D + d];
-      if (ms == -kInf) continue;  // a slice without chunks
-      const float f = exp2_fast(ms - mx);
-      a = fmaf(red_a[s2 * D + d], f, a);
-      l = fmaf(red_l[s2 * D + d], f, l);
+      ms[s2] = red_m[s2 * D + d];
+      ls[s2] = red_l[s2 * D + d];
+      as[s2] = red_a[s2 * D + d];
     }
-    p.out[(size_t)(b * p.hq + h * p.group + g) * D + d] = a / l;
+    p.out[(size_t)(b * p.hq + h * p.group + g) * D + d] = combine_slices<S>(ms, ls, as);
   }
 }
 
-template <int D, int GM>
-hipError_t launch_decode_dg(const DecodeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((snapkv_decode_partial<D, GM>), dim3(p.nchunk, p.hkv, p.batch),
-                     dim3(kDecodeThreads), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((snapkv_decode_merge<D>), dim3(p.group, p.hkv, p.batch),
-                     dim3(kDecodeMergeThreads), 0, stream, p);
+// With events, through the extended launch that has the dispatch record
+// them at the kernel's own start and end.
+template <typename K>
+hipError_t launch_ev(K kernel, dim3 grid, int threads, hipStream_t stream, hipEvent_t start,
+                     hipEvent_t stop, const DecodeParams& p) {
+  if (start != nullptr || stop != nullptr) {
+    void* args[] = {const_cast<DecodeParams*>(&p)};
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, dim3(threads), args,
+                              0, stream, start, stop, 0);
+  }
+  hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, stream, p);
   return hipGetLastError();
 }
 
+template <int D, int GM>
+hipError_t launch_decode_dg(const DecodeParams& p, hipStream_t stream, hipEvent_t start,
+                            hipEvent_t stop) {
+  const dim3 grid(p.nchunk, p.hkv, p.batch);
+  if (p.fused) return launch_ev(snapkv_decode_partial<D, GM, true>, grid, kDecodeThreads, stream,
+                                start, stop, p);
+  hipError_t e = launch_ev(snapkv_decode_partial<D, GM, false>, grid, kDecodeThreads, stream,
+                           start, nullptr, p);
+  if (e != hipSuccess) return e;
+  return launch_ev(snapkv_decode_merge<D>, dim3(p.group, p.hkv, p.batch), kDecodeMergeThreads,
+                   stream, nullptr, stop, p);
+}
+
 template <int D>
-hipError_t launch_decode_d(const DecodeParams& p, hipStream_t stream) {
-  if (p.group <= 1) return launch_decode_dg<D, 1>(p, stream);
-  if (p.group <= 2) return launch_decode_dg<D, 2>(p, stream);
-  if (p.group <= 4) return launch_decode_dg<D, 4>(p, stream);
-  if (p.group <= kDecodeMaxGroup) return launch_decode_dg<D, 8>(p, stream);
+hipError_t launch_decode_d(const DecodeParams& p, hipStream_t stream, hipEvent_t start,
+                           hipEvent_t stop) {
+  if (p.group <= 1) return launch_decode_dg<D, 1>(p, stream, start, stop);
+  if (p.group <= 2) return launch_decode_dg<D, 2>(p, stream, start, stop);
+  if (p.group <= 4) return launch_decode_dg<D, 4>(p, stream, start, stop);
+  if (p.group <= kDecodeMaxGroup) return launch_decode_dg<D, 8>(p, stream, start, stop);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, int head_dim, hipStream_t stream) {
-  if (head_dim == 128) return launch_decode_d<128>(p, stream);
-  if (head_dim == 64) return launch_decode_d<64>(p, stream);
+hipError_t launch_decode(const DecodeParams& p, int head_dim, hipStream_t stream,
+                         hipEvent_t start, hipEvent_t stop) {
+  if (head_dim == 128) return launch_decode_d<128>(p, stream, start, stop);
+  if (head_dim == 64) return launch_decode_d<64>(p, stream, start, stop);
   return hipErrorInvalidValue;
 }
 

@@ -35,6 +35,25 @@
 namespace snapkv {
 namespace {
 
+// The kernel arguments an item's first decisions and address computations
+// read, requested at entry in one batch: each scalar load from the argument
+// block is a round trip of a few hundred nanoseconds, and without this the
+// compiler issues them one branch at a time.
+__device__ __forceinline__ void prefetch_score_args(const PathParams& p, int b) {
+  asm volatile("" ::"s"(p.tab.len[b]), "s"(p.tab.off[b]), "s"(p.window), "s"(p.budget),
+               "s"(p.score_all), "s"(p.chunk), "s"(p.nchunk), "s"(p.rows), "s"(p.rows_pad),
+               "s"(p.nwr), "s"(p.hkv), "s"(p.hq), "s"(p.group), "s"(p.q), "s"(p.k));
+  asm volatile("" ::"s"(p.export_scores), "s"(p.pooled_stride), "s"(p.kernel), "s"(p.pooled),
+               "s"(p.part));
+}
+
+__device__ __forceinline__ void prefetch_gather_args(const PathParams& p, int b) {
+  asm volatile("" ::"s"(p.tab.len[b]), "s"(p.tab.off[b]), "s"(p.window), "s"(p.budget),
+               "s"(p.hkv), "s"(p.pooled_stride), "s"(p.table_stride), "s"(p.pooled),
+               "s"(p.k), "s"(p.v), "s"(p.out_k), "s"(p.out_v), "s"(p.out_idx));
+  asm volatile("" ::"s"(p.hist_bad), "s"(p.epoch));
+}
+
 __device__ __forceinline__ bool is_scored(const PathParams& p, int b) {
   const int L = p.tab.len[b];
   return L - p.window >= 1 && (p.score_all || L > p.budget);
@@ -48,6 +67,7 @@ template <int D, int RTW>
 __global__ void __launch_bounds__(kThreads) snapkv_score_stats(const PathParams p) {
   __shared__ StatsSmem<D> sm;
   const int b = blockIdx.z, h = blockIdx.y, c = blockIdx.x;
+  prefetch_score_args(p, b);
   if (!is_scored(p, b) || c >= num_chunks(p, b)) return;
   snapkv_score_stats_item<D, RTW>(p, sm, b, h, c);
 }
@@ -56,6 +76,7 @@ template <int D, int RTW, bool EXT_LSE, bool ZERO_FIRST = false>
 __global__ void __launch_bounds__(kThreads) snapkv_score_vote(const PathParams p) {
   __shared__ VoteSmem<D> sm;
   const int b = blockIdx.z, h = blockIdx.y, c = blockIdx.x;
+  prefetch_score_args(p, b);
   const int P = p.tab.len[b] - p.window;
   const int nvote = P >= 1 ? (P + p.chunk - 1) / p.chunk : 0;
   if (p.export_scores && c == (nvote > 0 ? nvote - 1 : 0)) {
@@ -73,6 +94,7 @@ template <int D>
 __global__ void __launch_bounds__(kThreads) snapkv_score_fused(const PathParams p) {
   __shared__ FusedSmem<D> sm;
   const int b = blockIdx.z, h = blockIdx.y, c = blockIdx.x;
+  prefetch_score_args(p, b);
   if (!is_scored(p, b) || c >= num_chunks(p, b)) return;
   snapkv_score_fused_item<D>(p, sm, b, h, c);
 }
@@ -83,6 +105,7 @@ template <int D, int RTW>
 __global__ void __launch_bounds__(kThreads) snapkv_score_fused_stream(const PathParams p) {
   __shared__ FusedStreamSmem<D, RTW> sm;
   const int b = blockIdx.z, h = blockIdx.y, c = blockIdx.x;
+  prefetch_score_args(p, b);
   if (!is_scored(p, b) || c >= num_chunks(p, b)) return;
   snapkv_score_fused_stream_item<D, RTW>(p, sm, b, h, c);
 }
@@ -122,6 +145,7 @@ __global__ void __launch_bounds__(kThreads) snapkv_select_count(const PathParams
 template <int D, int FORM, int RW>
 __global__ void __launch_bounds__(kThreads) snapkv_gather(const PathParams p) {
   __shared__ GatherSmem sm;
+  prefetch_gather_args(p, blockIdx.z);
   snapkv_gather_item<D, FORM, RW>(p, sm, blockIdx.z, blockIdx.y, blockIdx.x);
 }
 
@@ -143,6 +167,7 @@ template <int D, int FORM, int RW>
 __global__ void __launch_bounds__(kThreads) snapkv_gather_select(const PathParams p) {
   __shared__ GatherSelectSmem sm;
   const int b = blockIdx.z, h = blockIdx.y, rb = blockIdx.x;
+  prefetch_gather_args(p, b);
   const int t0 = rb * RW;
   const int L = p.tab.len[b];
   const int m = p.budget - p.window;

@@ -99,6 +99,11 @@ def load_library():
     lib.snapkv_decode_attention.argtypes = [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _i32,
                                             _pi32, _vp, _vp, _sz, _vp]
     lib.snapkv_decode_attention.restype = _i32
+    lib.snapkv_decode_attention_timed.argtypes = lib.snapkv_decode_attention.argtypes + [_vp,
+                                                                                           _vp]
+    lib.snapkv_decode_attention_timed.restype = _i32
+    lib.snapkv_decode_kernels.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _pi32, _pi32]
+    lib.snapkv_decode_kernels.restype = _i32
     lib.snapkv_window_scores.argtypes = [_i32, _i32, _i32, _i32, _vp, _vp, _pi32, _i32,
                                          _i32, _i32, _vp, _i32, _vp, _sz, _vp]
     lib.snapkv_window_scores.restype = _i32
@@ -495,13 +500,51 @@ def snapkv_decode_workspace_size(num_q_heads: int, num_kv_heads: int, head_dim: 
     return out.value
 
 
+def snapkv_decode_kernels(num_q_heads: int, num_kv_heads: int, head_dim: int,
+                          cache_lens: Sequence[int], layout: int, capacity: int = 0) -> int:
+    """How many kernels snapkv_decode_attention launches for this shape (1 or 2)."""
+    lib = load_library()
+    arr, vals = _lens(cache_lens)
+    out = ctypes.c_int32(0)
+    _check(lib.snapkv_decode_kernels(len(vals), num_q_heads, num_kv_heads, head_dim, layout,
+                                     capacity, arr, ctypes.byref(out)))
+    return out.value
+
+
 def snapkv_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                             cache_lens: Sequence[int], *, out: Optional[torch.Tensor] = None,
-                            workspace: Optional[torch.Tensor] = None, stream=None):
+                            workspace: Optional[torch.Tensor] = None, stream=None,
+                            events=None):
     """One decode step's attention, float32 [batch, H_q, D]. The layout
     follows k_cache's rank: [batch, H_kv, capacity, D] is a compressed cache
     (snapkv_compress's out_k / out_v), [T, H_kv, D] the packed prefill cache;
-    see include/snapkv.h."""
+    see include/snapkv.h. With events = (start, stop) (torch.cuda.Event with
+    timing, already recorded once), the dispatches record them at the step's
+    first kernel start and last kernel end."""
+    return prepare_decode(q, k_cache, v_cache, cache_lens, out=out, workspace=workspace,
+                          stream=stream, events=events)()
+
+
+class DecodeStep:
+    """A decode step whose arguments were checked once: calling it launches
+    the step (one C call, nothing else), for loops that repeat a step on the
+    same buffers. It holds references to its tensors; their contents may
+    change between calls, their shapes and storage may not."""
+
+    def __init__(self, fn, args, out, tensors):
+        self._fn, self._args, self.out, self._tensors = fn, args, out, tensors
+
+    def __call__(self):
+        _check(self._fn(*self._args))
+        return self.out
+
+
+def prepare_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   cache_lens: Sequence[int], *, out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None,
+                   events=None) -> DecodeStep:
+    """Check the arguments of snapkv_decode_attention and return the step as
+    a DecodeStep (see snapkv_decode_attention for the arguments)."""
     lib = load_library()
     _check_tensor("q", q, 3)
     layout, hkv, capacity, d = _decode_layout(k_cache)
@@ -526,10 +569,15 @@ def snapkv_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
     if workspace is None:
         nbytes = snapkv_decode_workspace_size(hq, hkv, d, vals, layout, capacity)
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
-    _check(lib.snapkv_decode_attention(batch, hq, hkv, d, _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                                       layout, capacity, arr, _ptr(out), _ptr(workspace),
-                                       workspace.numel(), _stream(stream, dev)))
-    return out
+    args = (batch, hq, hkv, d, _ptr(q), _ptr(k_cache), _ptr(v_cache), layout, capacity, arr,
+            _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream, dev))
+    tensors = (q, k_cache, v_cache, out, workspace)
+    if events is None:
+        return DecodeStep(lib.snapkv_decode_attention, args, out, tensors)
+    start, stop = events
+    return DecodeStep(lib.snapkv_decode_attention_timed,
+                      args + (int(start.cuda_event), int(stop.cuda_event)), out,
+                      tensors + (start, stop))
 
 
 def snapkv_window_scores(q_win: torch.Tensor, k: torch.Tensor, seq_lens: Sequence[int],

@@ -22,7 +22,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = skv.header_functions()
-    assert len(names) == 17, names
+    assert len(names) == 19, names
     assert "snapkv_compress_staged" in names
     assert "snapkv_compress_with_scores" in names
     assert "snapkv_compress_static" in names
@@ -229,6 +229,27 @@ def test_decode_validation_and_workspace(lib):
     st = lib.snapkv_decode_attention(1, 32, 8, 128, FAKE, FAKE, FAKE, 0, 128, lens, FAKE,
                                      FAKE, 1, None)
     assert st == 3
+    # the timed form validates the same way before touching its events
+    st = lib.snapkv_decode_attention_timed(1, 32, 8, 128, FAKE, FAKE, FAKE + 8, 0, 128, lens,
+                                           FAKE, FAKE, 1 << 30, None, None, None)
+    assert st == 1 and "aligned" in skv.snapkv_last_error()
+    st = lib.snapkv_decode_attention_timed(1, 32, 8, 128, FAKE, FAKE, FAKE, 0, 128, lens, FAKE,
+                                           FAKE, 1, None, None, None)
+    assert st == 3
+
+
+def test_decode_kernel_count(lib):
+    # one launch while no prompt has more than 16 chunks of rows (chunks of
+    # at least 128 rows, about 1024 chunk items per call), else two
+    comp = skv.SNAPKV_CACHE_COMPRESSED
+    packed = skv.SNAPKV_CACHE_PACKED
+    assert skv.snapkv_decode_kernels(32, 8, 128, [1024], comp, 1024) == 1
+    assert skv.snapkv_decode_kernels(32, 8, 128, [4096] * 8, comp, 4096) == 1
+    assert skv.snapkv_decode_kernels(32, 8, 128, [16384], packed) == 2
+    assert skv.snapkv_decode_kernels(8, 8, 64, [2048], packed) == 1   # 16 chunks of 128
+    assert skv.snapkv_decode_kernels(8, 8, 64, [2049], packed) == 2   # 17
+    with pytest.raises(skv.SnapKVError):
+        skv.snapkv_decode_kernels(32, 8, 96, [10], comp, 16)
 
 
 def test_score_kernels_host_logic(lib):

@@ -174,3 +174,91 @@ def test_decode_70b_shape_128k_packed_and_compressed():
                                         [w.budget]).cpu().numpy()
     want_c = oracle.decode_compressed(qd, kc, vc, [w.budget])
     _check(got_c.astype(np.float64), want_c, vmax, w.h_kv)
+
+
+FORM_CASES = [
+    # (cache_lens, h_q, h_kv, d, capacity or None for the packed layout)
+    ([4096] * 8, 32, 8, 128, 4096),          # 16 chunks per head, one launch
+    ([1024, 1, 300, 1024], 32, 8, 128, 1024),  # one-chunk prompts written directly
+    ([2048], 8, 8, 64, None),                # packed, 16 chunks
+    ([1500, 100, 9], 24, 8, 128, None),      # packed, G = 3, ragged
+]
+
+
+def _random_cache(lens, hkv, d, capacity, seed):
+    rng = np.random.default_rng(seed)
+    if capacity is None:
+        shape = (sum(lens), hkv, d)
+    else:
+        shape = (len(lens), hkv, capacity, d)
+    k = bf16_round_bits(rng.standard_normal(shape).astype(np.float32) * 0.3)
+    v = bf16_round_bits(rng.standard_normal(shape).astype(np.float32))
+    return k, v
+
+
+@needs_gpu
+@pytest.mark.parametrize("case", FORM_CASES, ids=[f"form{i}" for i in range(len(FORM_CASES))])
+def test_one_launch_and_two_launch_forms_give_identical_bits(case, monkeypatch):
+    # the one-launch form (an item that finds every chunk done merges) folds
+    # the chunks in the merge kernel's order, so both forms agree bit for bit
+    lens, hq, hkv, d, cap = case
+    layout = skv.SNAPKV_CACHE_PACKED if cap is None else skv.SNAPKV_CACHE_COMPRESSED
+    print(f"[decode] forms {case}", flush=True)
+    k, v = _random_cache(lens, hkv, d, cap, seed=len(lens) + hq)
+    qd = _query(len(lens), hq, d, seed=5)
+    qg, kg, vg = bits_to_device(qd), bits_to_device(k), bits_to_device(v)
+    assert skv.snapkv_decode_kernels(hq, hkv, d, lens, layout, cap or 0) == 1
+    one = skv.snapkv_decode_attention(qg, kg, vg, lens)
+    monkeypatch.setenv("SNAPKV_NO_FUSED_DECODE", "1")
+    assert skv.snapkv_decode_kernels(hq, hkv, d, lens, layout, cap or 0) == 2
+    two = skv.snapkv_decode_attention(qg, kg, vg, lens)
+    torch.cuda.synchronize()
+    assert torch.equal(one, two)
+    if cap is None:
+        want = oracle.decode_packed(qd, k, v, lens)
+        vmax = [[np.abs(oracle.bf16_bits_to_f64(v[sum(lens[:b]):sum(lens[:b + 1]), h])).max()
+                 for h in range(hkv)] for b in range(len(lens))]
+    else:
+        want = oracle.decode_compressed(qd, k, v, lens)
+        vmax = [[np.abs(oracle.bf16_bits_to_f64(v[b, h, :n])).max() for h in range(hkv)]
+                for b, n in enumerate(lens)]
+    _check(one.cpu().numpy().astype(np.float64), want, vmax, hkv)
+
+
+@needs_gpu
+def test_one_launch_marks_need_no_clearing_across_calls_and_shapes():
+    # one workspace reused by calls of different chunk counts: each call's
+    # done marks carry its own epoch, so stale marks never start a merge
+    cases = [([2048] * 2, 2048), ([1024, 1024], 1024), ([1900, 200], 2048)]
+    ws = torch.empty(1 << 22, dtype=torch.uint8, device="cuda")
+    data = []
+    for i, (lens, cap) in enumerate(cases):
+        assert skv.snapkv_decode_kernels(32, 8, 128, lens, skv.SNAPKV_CACHE_COMPRESSED, cap) == 1
+        k, v = _random_cache(lens, 8, 128, cap, seed=40 + i)
+        q = bits_to_device(_query(len(lens), 32, 128, seed=50 + i))
+        data.append((q, bits_to_device(k), bits_to_device(v), lens))
+    fresh = [skv.snapkv_decode_attention(*x[:3], x[3]) for x in data]
+    for _ in range(3):
+        for x, want in zip(data, fresh):
+            got = skv.snapkv_decode_attention(*x[:3], x[3], workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(got, want)
+
+
+@needs_gpu
+def test_timed_step_records_the_dispatch_events_and_gives_the_same_bits():
+    lens = [1024]
+    k, v = _random_cache(lens, 8, 128, 1024, seed=61)
+    q = bits_to_device(_query(1, 32, 128, seed=62))
+    kg, vg = bits_to_device(k), bits_to_device(v)
+    plain = skv.snapkv_decode_attention(q, kg, vg, lens)
+    start, stop = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+    start.record()
+    stop.record()  # the events exist before the dispatches record them
+    torch.cuda.synchronize()
+    step = skv.prepare_decode(q, kg, vg, lens, events=(start, stop))
+    timed = step()
+    torch.cuda.synchronize()
+    assert torch.equal(plain, timed)
+    ms = start.elapsed_time(stop)
+    assert 0.0 < ms < 10.0
