@@ -95,20 +95,27 @@ __device__ __forceinline__ float load_coherent(const float* a) {
 }
 
 // One chunk's (max, sum of weights, weighted sum) folded into a running
-// triple: the merge's arithmetic, shared by both forms.
-__device__ __forceinline__ void fold_chunk(float& rm, float& rl, float& ra, float mc, float lc,
-                                           float ac) {
-  if (rm == -kInf) {  // the first chunk (finite max): what the general step gives, exactly
-    rm = mc;
-    rl = lc;
-    ra = ac;
-    return;
-  }
+// triple with a finite max: the merge's arithmetic, shared by both forms.
+__device__ __forceinline__ void fold_step(float& rm, float& rl, float& ra, float mc, float lc,
+                                          float ac) {
   const float mx = fmaxf(rm, mc);
   const float fr = exp2_fast(rm - mx), fc = exp2_fast(mc - mx);
   rl = fmaf(rl, fr, lc * fc);
   ra = fmaf(ra, fr, ac * fc);
   rm = mx;
+}
+
+// The same from any running triple: the first chunk (running max -inf) is
+// taken as it is, which is what the general step gives for it, exactly.
+__device__ __forceinline__ void fold_chunk(float& rm, float& rl, float& ra, float mc, float lc,
+                                           float ac) {
+  if (rm == -kInf) {
+    rm = mc;
+    rl = lc;
+    ra = ac;
+    return;
+  }
+  fold_step(rm, rl, ra, mc, lc, ac);
 }
 
 // The slices' running triples combined in order, and the output element.
@@ -137,13 +144,18 @@ template <int D, int C, int GM>
 __device__ __forceinline__ float merge_loaded(const float2 (*mlc)[GM], int g, const float (&a)[C],
                                               int nch) {
   constexpr int S = kDecodeMergeThreads / D;
+  static_assert(S <= C, "slices");
+  float2 e[C];  // every slot read at once (slots past nch are not used)
+#pragma unroll
+  for (int c = 0; c < C; ++c) e[c] = mlc[c][g];
   float sm[S], sl[S], sa[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    float rm = -kInf, rl = 0.f, ra = 0.f;
+    const bool live = s < nch;  // the slice's first chunk, taken as it is
+    float rm = live ? e[s].x : -kInf, rl = live ? e[s].y : 0.f, ra = live ? a[s] : 0.f;
 #pragma unroll
-    for (int c = s; c < C; c += S)
-      if (c < nch) fold_chunk(rm, rl, ra, mlc[c][g].x, mlc[c][g].y, a[c]);
+    for (int c = s + S; c < C; c += S)
+      if (c < nch) fold_step(rm, rl, ra, e[c].x, e[c].y, a[c]);
     sm[s] = rm;
     sl[s] = rl;
     sa[s] = ra;
