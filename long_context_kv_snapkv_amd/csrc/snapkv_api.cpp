@@ -57,6 +57,8 @@ int largest_pow2_at_most(int x) {
 struct Plan {
   int batch, hq, hkv, d, window, group, rows, rows_pad, nrt, nwr;
   int chunk, nchunk, l_max, p_max, p_stride;
+  int scored_pairs;  // (prompt, chunk) pairs of the prompts longer than the window
+  bool compact;      // the score kernels can run over a compact (pair, head) grid
   size_t off_top, off_table, off_meta, off_part, off_flags, off_bad, off_pooled, bytes;
   int t_stride;
   snapkv::PromptTable tab;
@@ -107,14 +109,29 @@ int32_t make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const int32
   pl->rows_pad = (pl->rows + 31) / 32 * 32;
   pl->nrt = pl->rows_pad / 32;
   pl->nwr = largest_pow2_at_most(pl->nrt < 8 ? pl->nrt : 8);
-  // keys per scoring item: about 256 items over the whole call (one per CU
-  // and phase), 64-key granularity, 256 .. 4096 keys
-  int64_t chunk = (key_sum * hkv + 255) / 256;
+  // keys per scoring item: about kTargetItems items over the whole call (one
+  // per CU and phase), 64-key granularity, 256 .. kMaxChunk keys: the
+  // shortest chunk with which the prompts longer than the window form at
+  // most kTargetItems (prompt, chunk, KV head) items, so that a ragged
+  // batch's items run in one round rather than spilling into a second
+  auto pairs_for = [&](int64_t c) {
+    int64_t n = 0;
+    for (int b = 0; b < batch; ++b)
+      if (seq_lens[b] > window) n += (seq_lens[b] + c - 1) / c;
+    return n;
+  };
+  int64_t chunk = (key_sum * hkv + snapkv::kTargetItems - 1) / snapkv::kTargetItems;
   chunk = (chunk + snapkv::kKeyTile - 1) / snapkv::kKeyTile * snapkv::kKeyTile;
   if (chunk < 256) chunk = 256;
+  while (chunk < snapkv::kMaxChunk && pairs_for(chunk) * hkv > snapkv::kTargetItems)
+    chunk += snapkv::kKeyTile;
   if (chunk > snapkv::kMaxChunk) chunk = snapkv::kMaxChunk;
   pl->chunk = (int)chunk;
   pl->nchunk = (int)((l_max + chunk - 1) / chunk);
+  pl->scored_pairs = (int)pairs_for(chunk);
+  // pair entries hold the chunk in 8 bits; an export adds one entry for each
+  // prompt not longer than the window (it zeroes that prompt's row)
+  pl->compact = pl->nchunk <= 256 && pl->scored_pairs + batch <= snapkv::kMaxPairs;
   pl->l_max = l_max;
   pl->p_max = l_max - window > 1 ? l_max - window : 1;
   pl->p_stride = (int)align_up((size_t)pl->p_max, 64);
@@ -202,6 +219,22 @@ snapkv::PathParams path_params(const Plan& pl, const void* q, const void* k, con
   p.score_all = score_all ? 1 : 0;
   p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)pl.d));
   p.tab = pl.tab;
+  // the compact scoring grid: every chunk of each prompt this call scores
+  // (with score_all, an export, also chunk 0 of the other prompts, whose
+  // rows the vote kernel zeroes)
+  p.npairs = 0;
+  if (pl.compact) {
+    int n = 0;
+    for (int b = 0; b < pl.batch; ++b) {
+      const int L = pl.tab.len[b];
+      if (L - pl.window >= 1 && (score_all || L > budget)) {
+        for (int c = 0; c * pl.chunk < L; ++c) p.pair[n++] = (uint16_t)(b << 8 | c);
+      } else if (score_all) {
+        p.pair[n++] = (uint16_t)(b << 8);
+      }
+    }
+    p.npairs = n;
+  }
   gather_plan(pl, budget, &p);
   return p;
 }
@@ -252,10 +285,16 @@ bool env_flag(const char* name) {
 // 16 keys) and streaming them twice otherwise.
 enum class Scoring { kTwoKernels, kFusedResident, kFusedStream };
 
+// Workgroups of the score kernels' grid (an upper bound for a call that
+// scores fewer prompts: the compact grid then has fewer pairs).
+int64_t score_items(const Plan& pl) {
+  return pl.compact ? (int64_t)pl.scored_pairs * pl.hkv : (int64_t)pl.nchunk * pl.hkv * pl.batch;
+}
+
 Scoring scoring_plan(const Plan& pl, int32_t kernel) {
   if (env_flag("SNAPKV_NO_FUSED_SCORE") || pl.nchunk > snapkv::kThreads)
     return Scoring::kTwoKernels;
-  const int64_t items = (int64_t)pl.nchunk * pl.hkv * pl.batch;
+  const int64_t items = score_items(pl);
   const int cus = device_cus();
   if (cus <= 0 || items > cus) return Scoring::kTwoKernels;
   if (pl.d == 128 && pl.rows_pad <= snapkv::kFusedMaxRows && pl.chunk <= snapkv::kFusedChunk &&
@@ -303,7 +342,7 @@ bool use_select_in_gather(const Plan& pl, snapkv::PathParams* p) {
 bool votes_resident(const Plan& pl) {
   if (env_flag("SNAPKV_NO_FUSED_SCORE") || pl.nchunk > snapkv::kThreads) return false;
   const int cus = device_cus();
-  return cus > 0 && (int64_t)pl.nchunk * pl.hkv * pl.batch <= cus;
+  return cus > 0 && score_items(pl) <= cus;
 }
 
 bool any_scored(const Plan& pl, int32_t budget, bool score_all) {

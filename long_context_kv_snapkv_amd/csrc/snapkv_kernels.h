@@ -12,7 +12,9 @@ constexpr int kMaxRows = 512;      // G * W scored rows per KV head
 constexpr int kMaxKernel = 2049;   // pooling kernel
 constexpr int kThreads = 512;      // workgroup size of every kernel
 constexpr int kKeyTile = 64;       // keys per LDS tile
-constexpr int kMaxChunk = 4096;    // keys per scoring work item
+constexpr int kMaxChunk = 8192;    // keys per scoring work item
+constexpr int kTargetItems = 256;  // scoring items per call the chunk length aims at
+constexpr int kMaxPairs = 512;     // (prompt, chunk) pairs of a compact scoring grid
 constexpr int kGatherRows = 64;    // compressed rows per gather work item (at most)
 constexpr int kTopHistBins = 2048; // bins of the selection's first radix digit
 constexpr int kSegment = 256;      // positions per selection count-table entry
@@ -98,8 +100,15 @@ struct PathParams {
   float* scores_out;       // snapkv_compress_with_scores: [batch, Hkv, scores_len] copy of
   int32_t scores_len;      // the pooled rows the selection read (0 where not compressed)
   float scale_log2;        // log2(e) / sqrt(D)
+  // Compact scoring grid (npairs > 0): the score kernels run over (pair,
+  // KV head), pair i being prompt pair[i] >> 8 and chunk pair[i] & 255, only
+  // for the prompts the call scores; otherwise over (chunk, KV head, prompt)
+  // with nchunk chunk slots for every prompt.
+  int32_t npairs;
+  uint16_t pair[kMaxPairs];
   PromptTable tab;
 };
+static_assert(sizeof(PathParams) <= 4096, "kernel arguments");
 
 // Optional events recorded by the dispatch itself at the kernel's start and
 // end (so they time the kernel alone, as a profiler's kernel trace does).

@@ -54,6 +54,24 @@ __device__ __forceinline__ void prefetch_gather_args(const PathParams& p, int b)
   asm volatile("" ::"s"(p.hist_bad), "s"(p.epoch));
 }
 
+// The (prompt, KV head, chunk) of a scoring workgroup, from the compact
+// grid's pair table or the full grid's coordinates.
+struct ScoreItem {
+  int b, h, c;
+};
+__device__ __forceinline__ ScoreItem score_item(const PathParams& p) {
+  if (p.npairs > 0) {
+    const uint32_t e = p.pair[blockIdx.x];
+    return ScoreItem{(int)(e >> 8), (int)blockIdx.y, (int)(e & 255u)};
+  }
+  return ScoreItem{(int)blockIdx.z, (int)blockIdx.y, (int)blockIdx.x};
+}
+
+// The grid of the score kernels.
+dim3 score_grid(const PathParams& p) {
+  return p.npairs > 0 ? dim3(p.npairs, p.hkv, 1) : dim3(p.nchunk, p.hkv, p.batch);
+}
+
 __device__ __forceinline__ bool is_scored(const PathParams& p, int b) {
   const int L = p.tab.len[b];
   return L - p.window >= 1 && (p.score_all || L > p.budget);
@@ -66,7 +84,8 @@ __device__ __forceinline__ int num_chunks(const PathParams& p, int b) {
 template <int D, int RTW>
 __global__ void __launch_bounds__(kThreads) snapkv_score_stats(const PathParams p) {
   __shared__ StatsSmem<D> sm;
-  const int b = blockIdx.z, h = blockIdx.y, c = blockIdx.x;
+  const ScoreItem it = score_item(p);
+  const int b = it.b, h = it.h, c = it.c;
   prefetch_score_args(p, b);
   if (!is_scored(p, b) || c >= num_chunks(p, b)) return;
   snapkv_score_stats_item<D, RTW>(p, sm, b, h, c);
@@ -75,7 +94,8 @@ __global__ void __launch_bounds__(kThreads) snapkv_score_stats(const PathParams 
 template <int D, int RTW, bool EXT_LSE, bool ZERO_FIRST = false>
 __global__ void __launch_bounds__(kThreads) snapkv_score_vote(const PathParams p) {
   __shared__ VoteSmem<D> sm;
-  const int b = blockIdx.z, h = blockIdx.y, c = blockIdx.x;
+  const ScoreItem it = score_item(p);
+  const int b = it.b, h = it.h, c = it.c;
   prefetch_score_args(p, b);
   const int P = p.tab.len[b] - p.window;
   const int nvote = P >= 1 ? (P + p.chunk - 1) / p.chunk : 0;
@@ -93,7 +113,8 @@ __global__ void __launch_bounds__(kThreads) snapkv_score_vote(const PathParams p
 template <int D>
 __global__ void __launch_bounds__(kThreads) snapkv_score_fused(const PathParams p) {
   __shared__ FusedSmem<D> sm;
-  const int b = blockIdx.z, h = blockIdx.y, c = blockIdx.x;
+  const ScoreItem it = score_item(p);
+  const int b = it.b, h = it.h, c = it.c;
   prefetch_score_args(p, b);
   if (!is_scored(p, b) || c >= num_chunks(p, b)) return;
   snapkv_score_fused_item<D>(p, sm, b, h, c);
@@ -104,7 +125,8 @@ __global__ void __launch_bounds__(kThreads) snapkv_score_fused(const PathParams 
 template <int D, int RTW>
 __global__ void __launch_bounds__(kThreads) snapkv_score_fused_stream(const PathParams p) {
   __shared__ FusedStreamSmem<D, RTW> sm;
-  const int b = blockIdx.z, h = blockIdx.y, c = blockIdx.x;
+  const ScoreItem it = score_item(p);
+  const int b = it.b, h = it.h, c = it.c;
   prefetch_score_args(p, b);
   if (!is_scored(p, b) || c >= num_chunks(p, b)) return;
   snapkv_score_fused_stream_item<D, RTW>(p, sm, b, h, c);
@@ -247,8 +269,8 @@ int row_tiles_per_wave(const PathParams& p) {
 hipError_t launch_score_stats(const PathParams& p, int head_dim, hipStream_t stream,
                               StageEvents ev) {
   return dispatch_dim_rtw(head_dim, row_tiles_per_wave(p), [&](auto d, auto rtw) {
-    return launch(snapkv_score_stats<decltype(d)::value, decltype(rtw)::value>,
-                  dim3(p.nchunk, p.hkv, p.batch), stream, ev, p);
+    return launch(snapkv_score_stats<decltype(d)::value, decltype(rtw)::value>, score_grid(p),
+                  stream, ev, p);
   });
 }
 
@@ -256,7 +278,7 @@ hipError_t launch_score_vote(const PathParams& p, int head_dim, hipStream_t stre
                              StageEvents ev, bool ext_lse, bool zero_first) {
   if (zero_first && (!ext_lse || p.nchunk > kThreads)) return hipErrorInvalidValue;
   return dispatch_dim_rtw(head_dim, row_tiles_per_wave(p), [&](auto d, auto rtw) {
-    const dim3 grid(p.nchunk, p.hkv, p.batch);
+    const dim3 grid = score_grid(p);
     if (zero_first)
       return launch(snapkv_score_vote<decltype(d)::value, decltype(rtw)::value, true, true>, grid,
                     stream, ev, p);
@@ -273,8 +295,7 @@ hipError_t launch_score_fused(const PathParams& p, int head_dim, hipStream_t str
   if (head_dim != 128 || p.rows_pad > kFusedMaxRows || p.chunk > kFusedChunk ||
       p.kernel / 2 > kFusedMaxHalo || p.nchunk > kThreads)
     return hipErrorInvalidValue;
-  return launch(snapkv_score_fused<128>, dim3(p.nchunk, p.hkv, p.batch), stream, ev, p,
-                p.cooperative != 0);
+  return launch(snapkv_score_fused<128>, score_grid(p), stream, ev, p, p.cooperative != 0);
 }
 
 hipError_t launch_score_fused_stream(const PathParams& p, int head_dim, hipStream_t stream,
@@ -282,7 +303,7 @@ hipError_t launch_score_fused_stream(const PathParams& p, int head_dim, hipStrea
   if (p.nchunk > kThreads) return hipErrorInvalidValue;
   return dispatch_dim_rtw(head_dim, row_tiles_per_wave(p), [&](auto d, auto rtw) {
     return launch(snapkv_score_fused_stream<decltype(d)::value, decltype(rtw)::value>,
-                  dim3(p.nchunk, p.hkv, p.batch), stream, ev, p, p.cooperative != 0);
+                  score_grid(p), stream, ev, p, p.cooperative != 0);
   });
 }
 

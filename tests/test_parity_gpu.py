@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import long_context_kv_snapkv_amd as skv
+from synth.device import layer_lengths
 from synth import WORKLOADS, make_custom, make_layer
 
 from parity import bits_from_device, full_check, run_gpu, upload
@@ -261,8 +262,16 @@ def test_score_kernel_count_by_shape():
     assert skv.snapkv_score_kernels(32, 8, 64, [16384], 32, 7) == (3 if one else 2)
     assert skv.snapkv_score_kernels(32, 8, 128, [16384], 32, 35) == (3 if one else 2)
     assert skv.snapkv_score_kernels(8, 8, 128, [1000], 32, 33) == 1
-    # more scoring items than compute units: two kernels
-    assert skv.snapkv_score_kernels(32, 8, 128, [20000] * 8, 64, 13) == 2
+    # a ragged batch: the chunk is lengthened until the (prompt, chunk, head)
+    # items fit one round, so the statistics and vote run in one launch
+    assert skv.snapkv_score_kernels(32, 8, 128, [20000] * 8, 64, 13) == (3 if one else 2)
+    r = WORKLOADS["llama3_8b_ragged8"]
+    lens = layer_lengths(r, 0)
+    assert skv.snapkv_score_kernels(r.h_q, r.h_kv, r.head_dim, lens, r.window,
+                                    r.kernel) == (3 if one else 2)
+    # more scoring items than compute units even with the longest chunks:
+    # two kernels
+    assert skv.snapkv_score_kernels(32, 8, 128, [100000] * 8, 64, 13) == 2
 
 
 @needs_gpu
