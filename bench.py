@@ -447,12 +447,15 @@ def measure_extras(w, args, dev, stream, sets, outs, ws, timed):
         for r in runs:
             r()
         torch.cuda.synchronize()
-        return sum(a.elapsed_time(b) for a, b in evs) / n
+        t = sorted(a.elapsed_time(b) for a, b in evs)
+        return sum(t) / n, t[n // 2]
 
     dec_steps = {"compressed": [make_comp(i) for i in range(ncomp)],
                  "full": [make_full(i) for i in range(nsets)]}
     dec_ms = {key: timed(lambda i, st=st: st[i % len(st)]()) for key, st in dec_steps.items()}
-    dec_dev_ms = {"compressed": device_ms(make_comp), "full": device_ms(make_full)}
+    dec_dev = {"compressed": device_ms(make_comp), "full": device_ms(make_full)}
+    dec_dev_ms = {k: v[0] for k, v in dec_dev.items()}
+    dec_dev_med = {k: v[1] for k, v in dec_dev.items()}
     dec_kernels = {"compressed": skv.snapkv_decode_kernels(w.h_q, hkv, d, n_kept,
                                                            skv.SNAPKV_CACHE_COMPRESSED, B),
                    "full": skv.snapkv_decode_kernels(w.h_q, hkv, d, lens,
@@ -509,13 +512,15 @@ def measure_extras(w, args, dev, stream, sets, outs, ws, timed):
                     "compressed cache (B rows per head) and over the full prefill cache; "
                     "*_us: host-driven loop of prepared steps (events around the loop), "
                     "*_device_us: the step's dispatch events (first kernel start to last "
-                    "kernel end), averaged",
+                    "kernel end), mean (and median) over the steps",
             "compressed_us": round(dec_ms["compressed"] * 1e3, 3),
             "full_us": round(dec_ms["full"] * 1e3, 3),
             "speedup": round(dec_ms["full"] / dec_ms["compressed"], 2),
             "compressed_device_us": round(dec_dev_ms["compressed"] * 1e3, 3),
             "full_device_us": round(dec_dev_ms["full"] * 1e3, 3),
             "device_speedup": round(dec_dev_ms["full"] / dec_dev_ms["compressed"], 2),
+            "compressed_device_median_us": round(dec_dev_med["compressed"] * 1e3, 3),
+            "full_device_median_us": round(dec_dev_med["full"] * 1e3, 3),
             "kernels": dec_kernels,
             "compressed_gbps": round(dec_bytes["compressed"] / (dec_dev_ms["compressed"] * 1e-3) /
                                      1e9, 1),
