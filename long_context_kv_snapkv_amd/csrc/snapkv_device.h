@@ -151,7 +151,7 @@ __device__ __forceinline__ void interleave_mfma_valu() {
 #pragma unroll
     for (int t = 0; t < RTW; ++t) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
     }
     if (s + kAhead < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // next read
   }
