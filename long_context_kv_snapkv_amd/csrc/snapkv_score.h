@@ -544,9 +544,16 @@ __device__ __forceinline__ void snapkv_score_vote_item(const PathParams& p, Vote
       for (int u = 0; u < kPartBatch; ++u)
         if (sub + u * tpr < nch) s += pe[u].y * exp2_fast(pe[u].x - m);
     }
-    for (int cc = sub + kPartBatch * tpr; cc < nch; cc += tpr) {  // long prompts only
-      const float2 e = load_part<COHERENT>(&part[(size_t)cc * p.rows_pad + row_c]);
-      lse_merge(m, s, e.x, e.y);
+    // more chunks (long prompts): merged one by one in chunk order, their
+    // loads issued kPartBatch at a time
+    for (int c0 = sub + kPartBatch * tpr; c0 < nch; c0 += kPartBatch * tpr) {
+      float2 e[kPartBatch];
+#pragma unroll
+      for (int u = 0; u < kPartBatch; ++u)
+        e[u] = load_part<COHERENT>(&part[(size_t)min(c0 + u * tpr, nch - 1) * p.rows_pad + row_c]);
+#pragma unroll
+      for (int u = 0; u < kPartBatch; ++u)
+        if (c0 + u * tpr < nch) lse_merge(m, s, e[u].x, e[u].y);
     }
     float2* scratch = reinterpret_cast<float2*>(&sm.vred[0][0][0]);  // kThreads float2
     scratch[tid] = row_ok ? make_float2(m, s) : make_float2(-kInf, 0.f);
