@@ -339,11 +339,15 @@ GIVE_UP = [
     "llama3_8b_32k_x32",
     ([40000], 8, 2, 128, 16, 7, "max", 2048),
     ([70000], 8, 2, 128, 16, 5, "avg", 1024),
+    # the ragged batch on the compact (prompt chunk, head) grid, one prompt
+    # kept whole (no items of its own)
+    "llama3_8b_ragged8",
 ]
 
 
 @needs_gpu
-@pytest.mark.parametrize("case", GIVE_UP, ids=["16k", "32k", "resident_sliced", "stream_sliced"])
+@pytest.mark.parametrize("case", GIVE_UP,
+                         ids=["16k", "32k", "resident_sliced", "stream_sliced", "ragged"])
 def test_fused_wait_gives_up_with_identical_results(case, monkeypatch):
     # the fused score kernels' wait for the other items of a head is bounded;
     # with the bound forced to zero polls from the host, an item gives up at
