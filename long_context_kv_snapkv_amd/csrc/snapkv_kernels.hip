@@ -188,7 +188,23 @@ struct alignas(16) GatherSelectSmem {
 template <int D, int FORM, int RW>
 __global__ void __launch_bounds__(kThreads) snapkv_gather_select(const PathParams p) {
   __shared__ GatherSelectSmem sm;
-  const int b = blockIdx.z, h = blockIdx.y, rb = blockIdx.x;
+  // Every item of a head on one XCD: workgroups are dealt to the 8 XCDs in
+  // turn, so workgroup w goes to XCD w mod 8, and item (head, rb) is given to
+  // w = 8 * ((head / 8) * nb + rb) + head mod 8. Each item reads its head's
+  // whole pooled row, which then comes into one L2 instead of eight (HBM
+  // traffic 1.50 -> 1.04x the algorithmic bytes on the 16K layer). Any other
+  // placement of workgroups still gives every item exactly once.
+  int b = blockIdx.z, h = blockIdx.y, rb = blockIdx.x;
+  {
+    const int nb = gridDim.x, heads = gridDim.y * gridDim.z;
+    if (heads % 8 == 0) {
+      const int w = blockIdx.x + nb * (blockIdx.y + gridDim.y * blockIdx.z);
+      const int slot = w / 8, head = (slot / nb) * 8 + w % 8;
+      rb = slot % nb;
+      h = head % gridDim.y;
+      b = head / gridDim.y;
+    }
+  }
   prefetch_gather_args(p, b);
   const int t0 = rb * RW;
   const int L = p.tab.len[b];
