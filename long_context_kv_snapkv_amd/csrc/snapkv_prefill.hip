@@ -35,6 +35,11 @@ namespace {
 constexpr int BM = kPrefillRows;
 constexpr int BN = kPrefillKeys;
 
+template <int N>
+struct VROW_EVEN {
+  static constexpr bool ok = N % 2 == 0;
+};
+
 template <int D>
 struct alignas(16) PrefillSmem {
   static constexpr int ROWB = D * 2 + 16;  // padded row (bytes): MFMA fragment reads hit distinct banks
@@ -90,30 +95,54 @@ __global__ void __launch_bounds__(kPrefillThreads, 2) snapkv_prefill(const Prefi
 
   const int kend = min(r0 + BM, L);  // keys up to the item's last row
   const int ntiles = (kend + BN - 1) / BN;
+  // a thread moves K pieces of single keys and V pieces of key pairs: the
+  // pair's two values of each column go to the transposed tile as one word
   constexpr int LOADS = BN * PIECES / kPrefillThreads;
-  for (int it = 0; it < ntiles; ++it) {
-    const int k0 = it * BN;
-    u32x4 kx[LOADS], vx[LOADS];
+  constexpr int VPAIRS = LOADS / 2;
+  static_assert(LOADS % 2 == 0 && VROW_EVEN<S::VROW>::ok, "pairs of keys per transposed word");
+  u32x4 kx[LOADS], va[VPAIRS], vb[VPAIRS];
+  // tile k0's loads into the registers (rows past the prompt: a valid row,
+  // masked in the logits)
+  auto load_tile = [&](int k0) {
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
       const int pc = tid + u * kPrefillThreads;
-      const int key = pc / PIECES, col = pc % PIECES;
-      const int j = min(k0 + key, L - 1);  // past the prompt: a valid row, masked below
-      kx[u] = *reinterpret_cast<const u32x4*>(kbase + (size_t)j * kstride + col * 8);
-      vx[u] = *reinterpret_cast<const u32x4*>(vbase + (size_t)j * kstride + col * 8);
+      const int j = min(k0 + pc / PIECES, L - 1);
+      kx[u] = *reinterpret_cast<const u32x4*>(kbase + (size_t)j * kstride + (pc % PIECES) * 8);
     }
+#pragma unroll
+    for (int u = 0; u < VPAIRS; ++u) {
+      const int pc = tid + u * kPrefillThreads;  // key pair pc / PIECES
+      const int j0 = min(k0 + 2 * (pc / PIECES), L - 1), j1 = min(k0 + 2 * (pc / PIECES) + 1, L - 1);
+      va[u] = *reinterpret_cast<const u32x4*>(vbase + (size_t)j0 * kstride + (pc % PIECES) * 8);
+      vb[u] = *reinterpret_cast<const u32x4*>(vbase + (size_t)j1 * kstride + (pc % PIECES) * 8);
+    }
+  };
+  load_tile(0);
+  for (int it = 0; it < ntiles; ++it) {
+    const int k0 = it * BN;
     __syncthreads();  // every wave is done with the previous tile
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
       const int pc = tid + u * kPrefillThreads;
-      const int key = pc / PIECES, col = pc % PIECES;
-      *reinterpret_cast<u32x4*>(sm.kt + key * ROWB + col * 16) = kx[u];
+      *reinterpret_cast<u32x4*>(sm.kt + (pc / PIECES) * ROWB + (pc % PIECES) * 16) = kx[u];
+    }
+#pragma unroll
+    for (int u = 0; u < VPAIRS; ++u) {
+      const int pc = tid + u * kPrefillThreads;
+      const int key = 2 * (pc / PIECES), col = pc % PIECES;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        sm.vt[(col * 8 + 2 * e) * S::VROW + key] = (uint16_t)(vx[u][e] & 0xFFFFu);
-        sm.vt[(col * 8 + 2 * e + 1) * S::VROW + key] = (uint16_t)(vx[u][e] >> 16);
+        // columns 8 col + 2e and + 2e + 1: (key, key + 1) as one 32-bit word each
+        const uint32_t x = va[u][e], y = vb[u][e];
+        *reinterpret_cast<uint32_t*>(&sm.vt[(col * 8 + 2 * e) * S::VROW + key]) =
+            (x & 0xFFFFu) | (y << 16);
+        *reinterpret_cast<uint32_t*>(&sm.vt[(col * 8 + 2 * e + 1) * S::VROW + key]) =
+            (x >> 16) | (y & 0xFFFF0000u);
       }
     }
+    // the next tile's loads fly while this one is computed
+    if (it + 1 < ntiles) load_tile(k0 + BN);
     __syncthreads();
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
