@@ -87,7 +87,7 @@ __global__ void __launch_bounds__(kPrefillThreads, 2) snapkv_prefill(const Prefi
   const int wr0 = r0 + 32 * wave;          // first row of this wave
   const int my_row = wr0 + (lane & 31);    // the row of this lane's S^T column
   const float scale = p.scale_log2;
-  float m = -kInf;  // running maximum of the row (scaled log2 units), same in lanes l and l^32
+  float m = -kInf;  // the row's reference (scaled log2 units, within 8 of its maximum so far), same in lanes l and l^32
   float lsum = 0.f; // this lane's part of the row's sum of 2^(x - m)
   f32x16 o[NDS];
 #pragma unroll
@@ -172,7 +172,11 @@ __global__ void __launch_bounds__(kPrefillThreads, 2) snapkv_prefill(const Prefi
 #pragma unroll
       for (int v = 1; v < 16; ++v) bm = fmaxf(bm, x[v]);
       bm = fmaxf(bm, __shfl_xor(bm, 32));
-      const float mn = fmaxf(m, bm);  // finite: every row sees key 0 in the first block
+      // the row's reference moves only when the block's maximum exceeds it
+      // by more than 8 (log2 units): the terms 2^(x - m) then stay below 2^8,
+      // and the output rows are rescaled rarely (m + log2(sum) is the row's
+      // normaliser whichever reference m holds)
+      const float mn = bm > m + 8.f ? bm : m;  // finite: every row sees key 0 in the first block
       const float alpha = exp2_fast(m - mn);
       float pv[16];
       float ps = 0.f;
