@@ -282,7 +282,9 @@ bool env_flag(const char* name) {
 // items exchange the statistics (every item of the grid resident at once,
 // one workgroup per CU), keeping a chunk's keys in LDS when they fit
 // (head_dim 128, one row tile per wave, at most 512 keys, a halo of at most
-// 16 keys) and streaming them twice otherwise.
+// 16 keys) and streaming them twice otherwise. One row tile per wave needs
+// the window rows to form a power-of-two number of row tiles (at most 8):
+// 3, 5, 6 or 7 tiles give some waves two, which the streaming form handles.
 enum class Scoring { kTwoKernels, kFusedResident, kFusedStream };
 
 // Workgroups of the score kernels' grid (an upper bound for a call that
@@ -297,8 +299,8 @@ Scoring scoring_plan(const Plan& pl, int32_t kernel) {
   const int64_t items = score_items(pl);
   const int cus = device_cus();
   if (cus <= 0 || items > cus) return Scoring::kTwoKernels;
-  if (pl.d == 128 && pl.rows_pad <= snapkv::kFusedMaxRows && pl.chunk <= snapkv::kFusedChunk &&
-      kernel / 2 <= snapkv::kFusedMaxHalo)
+  if (pl.d == 128 && pl.rows_pad <= snapkv::kFusedMaxRows && pl.nrt == pl.nwr &&
+      pl.chunk <= snapkv::kFusedChunk && kernel / 2 <= snapkv::kFusedMaxHalo)
     return Scoring::kFusedResident;
   return Scoring::kFusedStream;
 }

@@ -308,8 +308,8 @@ hipError_t launch_score_vote(const PathParams& p, int head_dim, hipStream_t stre
 
 hipError_t launch_score_fused(const PathParams& p, int head_dim, hipStream_t stream,
                               StageEvents ev) {
-  if (head_dim != 128 || p.rows_pad > kFusedMaxRows || p.chunk > kFusedChunk ||
-      p.kernel / 2 > kFusedMaxHalo || p.nchunk > kThreads)
+  if (head_dim != 128 || p.rows_pad > kFusedMaxRows || row_tiles_per_wave(p) != 1 ||
+      p.chunk > kFusedChunk || p.kernel / 2 > kFusedMaxHalo || p.nchunk > kThreads)
     return hipErrorInvalidValue;
   return launch(snapkv_score_fused<128>, score_grid(p), stream, ev, p, p.cooperative != 0);
 }

@@ -83,6 +83,10 @@ EDGE = [
     # the sliced selection: short, kept-whole and one-slice prompts beside it
     ([40000, 3000, 400, 35000, 4100], 8, 2, 128, 16, 5, "avg", 512),
     ([3000, 2500], 16, 4, 128, 64, 5, "avg", 1024),
+    # window rows forming 3 and 5 row tiles (G = 3 and 5, W = 32): some
+    # waves hold two row tiles, so short prompts take the streaming form
+    ([300], 12, 4, 128, 32, 5, "avg", 64),         # R = 96
+    ([700, 90], 20, 4, 128, 32, 7, "max", 128),    # R = 160, ragged
 ]
 
 
@@ -262,6 +266,11 @@ def test_score_kernel_count_by_shape():
     assert skv.snapkv_score_kernels(32, 8, 64, [16384], 32, 7) == (3 if one else 2)
     assert skv.snapkv_score_kernels(32, 8, 128, [16384], 32, 35) == (3 if one else 2)
     assert skv.snapkv_score_kernels(8, 8, 128, [1000], 32, 33) == 1
+    # short prompts keep their keys in LDS only with one row tile per wave:
+    # 128 window rows (4 row tiles) do, 96 and 160 (3 and 5) stream instead
+    assert skv.snapkv_score_kernels(8, 2, 128, [300], 32, 5) == (1 if one else 2)
+    assert skv.snapkv_score_kernels(12, 4, 128, [300], 32, 5) == (3 if one else 2)
+    assert skv.snapkv_score_kernels(20, 4, 128, [700, 90], 32, 7) == (3 if one else 2)
     # a ragged batch: the chunk is lengthened until the (prompt, chunk, head)
     # items fit one round, so the statistics and vote run in one launch
     assert skv.snapkv_score_kernels(32, 8, 128, [20000] * 8, 64, 13) == (3 if one else 2)
@@ -377,9 +386,10 @@ def test_fused_wait_gives_up_with_identical_results(case, monkeypatch):
 
 
 @needs_gpu
-@pytest.mark.parametrize("case", [EDGE[12], EDGE[9], EDGE[8], EDGE[13], EDGE[16], EDGE[10]],
+@pytest.mark.parametrize("case", [EDGE[12], EDGE[9], EDGE[8], EDGE[13], EDGE[16], EDGE[10],
+                                  EDGE[17], EDGE[18]],
                          ids=["ragged_mixed", "rows512", "d64_rows72", "one_token", "batch2_w64",
-                              "wide_kernel"])
+                              "wide_kernel", "rows96", "rows160"])
 def test_fused_paths_identical_on_edge_shapes(case, monkeypatch):
     # small ragged, row-padded, head_dim-64 and one-token batches take the
     # fused forms (one-launch scoring, selection inside the gather) by
