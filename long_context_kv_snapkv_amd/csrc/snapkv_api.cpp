@@ -49,17 +49,19 @@ int largest_pow2_at_most(int x) {
 //   sel_meta  uint32[batch * H_kv, 4]               threshold of each head
 //   part      float2[batch, H_kv, nchunk, rows_pad]  per-chunk row statistics
 //   flags     uint64[batch, H_kv, nchunk]       fused score kernel: published items
+//   sflags    uint64[batch * H_kv, 2, slices]   one-launch sliced selection: published
+//                                                digit counts (slices = 0 for short prefixes)
 //   hist_bad  uint64[batch * H_kv]               call whose first-digit counts are untrusted
 //   pooled    float [batch, H_kv, p_stride]      pooled scores, p_stride =
 //                                                max P rounded up to 64
-// Every word is written by a call before that call reads it, except flags
-// and hist_bad, which only count when they hold the call's own epoch.
+// Every word is written by a call before that call reads it, except flags,
+// sflags and hist_bad, which only count when they hold the call's own epoch.
 struct Plan {
   int batch, hq, hkv, d, window, group, rows, rows_pad, nrt, nwr;
   int chunk, nchunk, l_max, p_max, p_stride;
   int scored_pairs;  // (prompt, chunk) pairs of the prompts longer than the window
   bool compact;      // the score kernels can run over a compact (pair, head) grid
-  size_t off_top, off_table, off_meta, off_part, off_flags, off_bad, off_pooled, bytes;
+  size_t off_top, off_table, off_meta, off_part, off_flags, off_sflags, off_bad, off_pooled, bytes;
   int t_stride;
   snapkv::PromptTable tab;
 };
@@ -148,6 +150,11 @@ int32_t make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const int32
   off = align_up(off + heads * pl->nchunk * pl->rows_pad * sizeof(float2), 256);
   pl->off_flags = off;
   off = align_up(off + heads * pl->nchunk * sizeof(uint64_t), 256);
+  pl->off_sflags = off;
+  const int64_t slices = pl->p_max > snapkv::kSelectHeldKeys
+                             ? (pl->p_max + snapkv::kSliceKeys - 1) / snapkv::kSliceKeys
+                             : 0;
+  off = align_up(off + heads * 2 * slices * sizeof(uint64_t), 256);
   pl->off_bad = off;
   off = align_up(off + heads * sizeof(uint64_t), 256);
   pl->off_pooled = off;
@@ -200,6 +207,7 @@ snapkv::PathParams path_params(const Plan& pl, const void* q, const void* k, con
   p.table_stride = pl.t_stride;
   p.part = reinterpret_cast<float2*>(w + pl.off_part);
   p.flags = reinterpret_cast<uint64_t*>(w + pl.off_flags);
+  p.sel_flags = reinterpret_cast<uint64_t*>(w + pl.off_sflags);
   p.hist_bad = reinterpret_cast<uint64_t*>(w + pl.off_bad);
   p.pooled = reinterpret_cast<float*>(w + pl.off_pooled);
   p.pooled_stride = pl.p_stride;
@@ -320,6 +328,17 @@ int32_t spin_limit() {
   const long v = std::strtol(e, &end, 10);
   if (end == e || v < 0 || v > snapkv::kSpinLimit) return snapkv::kSpinLimit;
   return (int32_t)v;
+}
+
+// The sliced selection in one launch (its slice workgroups exchange the
+// digit histograms through flags, with a bounded wait): when every slice
+// workgroup of the call fits the device at once. SNAPKV_NO_FUSED_SELECT
+// turns it off too (three kernels).
+bool use_one_launch_slices(const Plan& pl, const snapkv::PathParams& p) {
+  if (p.sel_slices == 0 || p.sel_slices > snapkv::kThreads || env_flag("SNAPKV_NO_FUSED_SELECT"))
+    return false;
+  const int cus = device_cus();
+  return cus > 0 && (int64_t)p.sel_slices * pl.hkv * pl.batch <= cus;
 }
 
 bool use_select_in_gather(const Plan& pl, snapkv::PathParams* p) {
@@ -485,6 +504,7 @@ int32_t compress_impl(int32_t batch, int32_t hq, int32_t hkv, int32_t d, const v
   // kernel before the gather
   const bool sel_in_gather = scored && use_select_in_gather(pl, &p);
   if (scored && !sel_in_gather) {
+    p.sel_one_launch = use_one_launch_slices(pl, p) ? 1 : 0;
     if ((e = snapkv::launch_select(p, s, events(2))) != hipSuccess)
       return hip_fail(e, "snapkv_select launch");
   } else if (scored) {

@@ -166,6 +166,53 @@ __device__ __forceinline__ void pin_here(f32x16 (&a)[N]) {
   for (int t = 0; t < N; ++t) asm volatile("" : "+v"(a[t]));
 }
 
+// ------------------------------------------------------------- exchange ---
+// Publish what this workgroup wrote for other workgroups of the same launch
+// (device-coherent stores or atomics already issued by every thread): each
+// thread's writes complete, then flags[c] = the call's epoch.
+__device__ __forceinline__ void publish_item(const PathParams& p, uint64_t* flags, int c) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&flags[c], p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until the flags of chunks 0 .. nch-1 of a head carry this call's
+// epoch, at most p.spin_limit polls each; returns non-zero (in every thread)
+// if any poll gave up, and with `missing` (LDS, nch entries) records which
+// chunks' flags were still unset. Ends with a workgroup barrier.
+//
+// Ordering: the publishing item writes its words with device-coherent stores
+// (agent-scope relaxed atomics: performed at the device's coherence point,
+// not held in one XCD's L2), waits until every one of its threads has had
+// them acknowledged (s_waitcnt vmcnt(0), then a workgroup barrier), and only
+// then stores its flag the same way. A waiting thread polls the flag with
+// device-coherent loads and issues the loads of the published words only
+// after it has seen the flag (the loop exit depends on the loaded value),
+// again device-coherent, so they are served from the coherence point, which
+// already holds the words. No cache write-back or invalidation is needed
+// for these words. The same holds for counts added with agent-scope atomics
+// (the one-launch sliced selection's histograms): those are performed at the
+// coherence point too. Requires nch <= kThreads.
+__device__ __forceinline__ int wait_head(const PathParams& p, const uint64_t* flags, int nch,
+                                         uint8_t* missing = nullptr) {
+  int timed_out = 0;
+  if ((int)threadIdx.x < nch) {
+    int spins = 0;
+    uint64_t* f = const_cast<uint64_t*>(&flags[threadIdx.x]);
+    while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != p.epoch) {
+      if (++spins > p.spin_limit) {
+        timed_out = 1;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (missing != nullptr) missing[threadIdx.x] = (uint8_t)timed_out;
+  }
+  // the same in every thread; returned as a scalar
+  return __builtin_amdgcn_readfirstlane(__syncthreads_or(timed_out));
+}
+
 // ------------------------------------------------------------ key tiles ---
 // A tile is 128 keys x D bf16 of one KV head. Threads load it from global
 // memory into registers (16-byte pieces, consecutive threads on consecutive

@@ -97,6 +97,9 @@ struct PathParams {
                            // there are few items (D = 128 only)
   int32_t sel_slices;      // 0: one selection workgroup per head; else kSliceKeys-position
                            // slices per head of the sliced selection
+  int32_t sel_one_launch;  // sliced selection as one launch exchanging its histograms
+  uint64_t* sel_flags;     // [batch * Hkv, 2, sel_slices] that launch: `epoch` once a slice's
+                           // digit-2 (then digit-3) counts are added
   float* scores_out;       // snapkv_compress_with_scores: [batch, Hkv, scores_len] copy of
   int32_t scores_len;      // the pooled rows the selection read (0 where not compressed)
   float scale_log2;        // log2(e) / sqrt(D)
@@ -135,7 +138,9 @@ hipError_t launch_score_fused(const PathParams& p, int head_dim, hipStream_t str
 // head_dim and row tiling; every item of the grid resident at once)
 hipError_t launch_score_fused_stream(const PathParams& p, int head_dim, hipStream_t stream,
                                      StageEvents ev = {});
-// one workgroup per head, or (sel_slices > 0) three sliced kernels
+// one workgroup per head, or (sel_slices > 0) the sliced selection: one
+// launch when every slice workgroup fits the device at once
+// (sel_one_launch), else three kernels
 hipError_t launch_select(const PathParams& p, hipStream_t stream, StageEvents ev = {});
 // form 0: bf16 rows; 1: 4-bit, 2: FP8 E4M3 codes with per-row scales, through
 // out_kq/out_ks/out_vq/out_vs

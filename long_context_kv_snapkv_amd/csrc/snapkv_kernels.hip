@@ -164,6 +164,15 @@ __global__ void __launch_bounds__(kThreads) snapkv_select_count(const PathParams
   select_count_slice(p, sm, b, h, sl);
 }
 
+// the sliced selection as one launch: grid (slice, head, prompt), every
+// workgroup resident at once
+__global__ void __launch_bounds__(kThreads) snapkv_select_slices(const PathParams p) {
+  __shared__ SliceOneSmem sm;
+  const int sl = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  if (p.tab.len[b] <= p.budget) return;
+  select_slices_one_launch(p, sm, b, h, sl);
+}
+
 template <int D, int FORM, int RW>
 __global__ void __launch_bounds__(kThreads) snapkv_gather(const PathParams p) {
   __shared__ GatherSmem sm;
@@ -333,8 +342,12 @@ hipError_t launch_clear_hist(const PathParams& p, hipStream_t stream, StageEvent
 
 hipError_t launch_select(const PathParams& p, hipStream_t stream, StageEvents ev) {
   if (p.sel_slices == 0) return launch(snapkv_select, dim3(p.hkv, p.batch), stream, ev, p);
-  // the stage's events bracket the three kernels
   const dim3 grid(p.sel_slices, p.hkv, p.batch);
+  if (p.sel_one_launch) {
+    if (p.sel_slices > kThreads) return hipErrorInvalidValue;  // one flag poll per thread
+    return launch(snapkv_select_slices, grid, stream, ev, p);
+  }
+  // the stage's events bracket the three kernels
   StageEvents first, last;
   first.start = ev.start;
   last.stop = ev.stop;

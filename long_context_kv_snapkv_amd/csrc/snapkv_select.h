@@ -34,8 +34,9 @@
 //     of which some are kept are the lowest-positioned ones of them taken.
 //
 // Long prefixes (sel_slices > 0) spread each head over workgroups of
-// kSliceKeys positions instead, in three kernels: digit 2's histogram,
-// digit 3's histogram and the count table. Each workgroup re-derives the
+// kSliceKeys positions instead, in three kernels (digit 2's histogram,
+// digit 3's histogram and the count table) or in one launch that passes
+// the histograms between its workgroups (below). Each workgroup re-derives the
 // threshold digits known so far from the head's global histograms (the same
 // integer search in every workgroup, so all agree), counts its slice into
 // LDS and adds the non-zero bins to the head's next histogram with global
@@ -443,6 +444,171 @@ __device__ __forceinline__ void select_count_slice(const PathParams& p, SliceSme
   if (tid == 0) sm.sh_lost = 0u;
   const Threshold t = resolve_digits(hist, hist + (recount ? kHistFix : kHistD1), 3,
                                      (uint32_t)(p.budget - p.window), sm);
+  const uint32_t tau = t.prefix;  // settled: keep keys >= prefix; else > tau, and `need` == tau
+  const int nseg = (P + kSegment - 1) / kSegment;
+  uint32_t* table = p.sel_table + head * (size_t)p.table_stride * 2;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t u = key[g][e];
+      c += (t.settled ? u >= tau : u > tau) ? 1u : 0u;
+      c += (!t.settled && u == tau) ? 0x10000u : 0u;
+    }
+    const uint32_t tot = wave_total(wave_incl_scan(c));
+    const int seg = (s0 + g * kSlab) / kSegment + wave;
+    if (lane == 0 && seg < nseg) {
+      table[2 * seg] = tot & 0xFFFFu;
+      table[2 * seg + 1] = tot >> 16;
+    }
+  }
+  if (sl == 0 && tid == 0) {
+    uint32_t* meta = p.sel_meta + head * 4;
+    meta[0] = tau;
+    meta[1] = t.need;
+    meta[2] = t.settled ? 1u : 0u;
+    meta[3] = sm.sh_lost;
+  }
+}
+
+// ---------------------------------------------- one-launch sliced selection ---
+// The three sliced passes as one launch (sel_one_launch, when every slice
+// workgroup of the call fits the device at once). Each slice workgroup loads
+// its keys once and keeps them in registers for every pass. A pass's digit
+// histogram is complete once every slice of the head has added its counts
+// (agent-scope atomics, performed at the device's coherence point) and
+// published that with its flag (publish_item: its atomics acknowledged, a
+// barrier, then the flag = the call's epoch). The workgroup then waits for
+// the flags of the head's slices (wait_head: bounded) and reads the
+// histogram with device-coherent loads. If the wait gives up, the workgroup
+// counts that digit over the head's whole prefix itself, in LDS: integer
+// counts, so the same histogram and the same threshold. The threshold
+// search, the counting and the count table are those of the three kernels.
+struct alignas(16) SliceOneSmem {
+  uint32_t rep[kRepStride];  // this slice's counts of the digit being counted
+  uint32_t own[kRepStride];  // a digit counted over the whole prefix here
+  uint32_t rowtot[kWaves];
+  uint32_t sh_bin, sh_need, sh_count;
+  uint32_t sh_lost;
+};
+
+// Four histogram words with device-coherent loads (16-byte aligned).
+__device__ __forceinline__ u32x4 load_coherent4(const uint32_t* a) {
+  uint64_t* w = const_cast<uint64_t*>(reinterpret_cast<const uint64_t*>(a));
+  const uint64_t lo = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t hi = __hip_atomic_load(w + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+}
+
+// One more radix digit (bits shift .. of nbins bins) of threshold t from
+// that digit's histogram, row(i) giving bins i .. i + 3: the step
+// resolve_digits takes for each digit.
+template <typename Row, typename Smem>
+__device__ __forceinline__ void next_digit(Threshold& t, int shift, int nbins, Row&& row,
+                                           Smem& sm) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  find_bin(
+      [&] {
+        const int i = 256 * wave + 4 * lane;
+        return i < nbins ? row(i) : u32x4{0u, 0u, 0u, 0u};
+      },
+      t.need, sm);
+  t.prefix |= sm.sh_bin << shift;
+  t.need = sm.sh_need;
+  t.settled = t.need == sm.sh_count;
+  t.low = shift;
+}
+
+__device__ __forceinline__ void select_slices_one_launch(const PathParams& p, SliceOneSmem& sm,
+                                                         int b, int h, int sl) {
+  const int P = p.tab.len[b] - p.window;
+  const int s0 = sl * kSliceKeys;
+  if (s0 >= P) return;
+  const int nsl = (P + kSliceKeys - 1) / kSliceKeys;  // slices of this head that publish
+  const size_t head = (size_t)(b * p.hkv + h);
+  uint32_t* hist = p.top_hist + head * kSelHistWords;
+  const float* src = p.pooled + head * p.pooled_stride;
+  uint64_t* flags = p.sel_flags + head * 2 * (size_t)p.sel_slices;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool recount = p.hist_bad[head] == p.epoch;
+  uint32_t key[2][4];
+  load_slice_keys(key, src, P, s0);
+  if (tid == 0) sm.sh_lost = 0u;
+  auto clear = [&](uint32_t* h4) {
+    for (int i = tid; i < kRepStride / 4; i += kThreads)
+      reinterpret_cast<u32x4*>(h4)[i] = u32x4{0u, 0u, 0u, 0u};
+  };
+  Threshold t{0u, (uint32_t)(p.budget - p.window), 32, false};
+
+  // digit 1: the score kernel's histogram (complete before this launch), or
+  // recounted here when that kernel marked it untrustworthy for this call
+  if (recount) {
+    clear(sm.own);
+    __syncthreads();
+    for (int a = 0; a < P; a += kSliceKeys) {
+      uint32_t k2[2][4];
+      load_slice_keys(k2, src, P, a);
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (a + g * kSlab + 4 * tid + e < P) lds_count(sm.own, k2[g][e] >> kTopShift);
+    }
+    __syncthreads();
+    next_digit(t, kTopShift, kBins,
+               [&](int i) { return *reinterpret_cast<const u32x4*>(sm.own + i); }, sm);
+  } else {
+    next_digit(t, kTopShift, kBins,
+               [&](int i) { return *reinterpret_cast<const u32x4*>(hist + kHistD1 + i); }, sm);
+  }
+
+  // digits 2 and 3 (every workgroup of the head reaches the same `settled`)
+#pragma unroll
+  for (int d = 2; d <= 3; ++d) {
+    if (t.settled) break;
+    const int shift = d == 2 ? 10 : 0;
+    const int nbins = d == 2 ? 2048 : 1024;
+    const uint32_t mask = (uint32_t)nbins - 1u;
+    uint32_t* dst = hist + (d == 2 ? kHistD2 : kHistD3);
+    clear(sm.rep);
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((key[g][e] >> t.low) == (t.prefix >> t.low))
+          atomicAdd(&sm.rep[(key[g][e] >> shift) & mask], 1u);
+    __syncthreads();
+    for (int i = tid; i < nbins; i += kThreads) {
+      const uint32_t n = sm.rep[i];
+      if (n != 0u) atomicAdd(&dst[i], n);
+    }
+    uint64_t* pass_flags = flags + (d - 2) * (size_t)p.sel_slices;
+    publish_item(p, pass_flags, sl);
+    if (wait_head(p, pass_flags, nsl)) {
+      // not every slice has published: this digit over the whole prefix here
+      clear(sm.own);
+      __syncthreads();
+      for (int a = 0; a < P; a += kSliceKeys) {
+        uint32_t k2[2][4];
+        load_slice_keys(k2, src, P, a);
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if ((k2[g][e] >> t.low) == (t.prefix >> t.low))
+              atomicAdd(&sm.own[(k2[g][e] >> shift) & mask], 1u);
+      }
+      __syncthreads();
+      next_digit(t, shift, nbins,
+                 [&](int i) { return *reinterpret_cast<const u32x4*>(sm.own + i); }, sm);
+    } else {
+      next_digit(t, shift, nbins, [&](int i) { return load_coherent4(dst + i); }, sm);
+    }
+  }
+
+  // count table of this slice's segments, as select_count_slice writes it
   const uint32_t tau = t.prefix;  // settled: keep keys >= prefix; else > tau, and `need` == tau
   const int nseg = (P + kSegment - 1) / kSegment;
   uint32_t* table = p.sel_table + head * (size_t)p.table_stride * 2;

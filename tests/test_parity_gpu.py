@@ -387,13 +387,14 @@ def test_fused_wait_gives_up_with_identical_results(case, monkeypatch):
 
 @needs_gpu
 @pytest.mark.parametrize("case", [EDGE[12], EDGE[9], EDGE[8], EDGE[13], EDGE[16], EDGE[10],
-                                  EDGE[17], EDGE[18]],
+                                  EDGE[17], EDGE[18], EDGE[14], EDGE[15]],
                          ids=["ragged_mixed", "rows512", "d64_rows72", "one_token", "batch2_w64",
-                              "wide_kernel", "rows96", "rows160"])
+                              "wide_kernel", "rows96", "rows160", "sliced", "sliced_mixed"])
 def test_fused_paths_identical_on_edge_shapes(case, monkeypatch):
     # small ragged, row-padded, head_dim-64 and one-token batches take the
-    # fused forms (one-launch scoring, selection inside the gather) by
-    # default; with both switched off every output bit is the same
+    # fused forms (one-launch scoring, selection inside the gather, the
+    # sliced selection of long prefixes in one launch) by default; with them
+    # switched off every output bit is the same
     lens, hq, hkv, d, window, kernel, pool, budget = case
     x = make_custom(lens, hq, hkv, d, window, seed=sum(lens) % 89)
     q, k, v = upload(x)
