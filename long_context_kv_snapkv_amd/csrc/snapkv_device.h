@@ -165,6 +165,11 @@ __device__ __forceinline__ void pin_here(f32x16 (&a)[N]) {
 #pragma unroll
   for (int t = 0; t < N; ++t) asm volatile("" : "+v"(a[t]));
 }
+template <int N>
+__device__ __forceinline__ void pin_here(float (&a)[N]) {
+#pragma unroll
+  for (int t = 0; t < N; ++t) asm volatile("" : "+v"(a[t]));
+}
 
 // ------------------------------------------------------------- exchange ---
 // Publish what this workgroup wrote for other workgroups of the same launch

@@ -293,6 +293,7 @@ __device__ __forceinline__ void score_stats_body(const PathParams& p, unsigned c
 #pragma unroll
           for (int t = 0; t < RTW; ++t) sb[t] = direct_sum(pacc[t], t);
           interleave_mfma_valu<D / 16, RTW>();
+          pin_here(sb);
         }
 #pragma unroll
         for (int t = 0; t < RTW; ++t) retire(pacc[t], t, sb[t]);
@@ -304,6 +305,7 @@ __device__ __forceinline__ void score_stats_body(const PathParams& p, unsigned c
 #pragma unroll
           for (int t = 0; t < RTW; ++t) sb[t] = direct_sum(acc[t], t);
           interleave_mfma_valu<D / 16, RTW>();
+          pin_here(sb);
         }
 #pragma unroll
         for (int t = 0; t < RTW; ++t) retire(acc[t], t, sb[t]);
