@@ -953,8 +953,16 @@ __device__ __forceinline__ void snapkv_score_fused_item(const PathParams& p, Fus
     for (int q = 0; q < 4; q += 2) {
       const int kb0 = role.wk + q * role.nwk, kb1 = kb0 + role.nwk;
       if (has(tt, q + 1)) {  // two chains in flight before either column sum
-        const f32x16 a0 = chain(tile, kb0);
-        const f32x16 a1 = chain(tile, kb1);
+        bf16x8 k0[D / 16], k1[D / 16];
+        read_key_frags<D, false>(k0, tile, kb0, lane);
+        read_key_frags<D, true>(k1, tile, kb1, lane);
+        f32x16 a0 = {}, a1 = {};
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s)
+          a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][s], k0[s], a0, 0, 0, 0);
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s)
+          a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][s], k1[s], a1, 0, 0, 0);
         pv[tt][q] = colsum(a0);
         pv[tt][q + 1] = colsum(a1);
       } else if (has(tt, q)) {
