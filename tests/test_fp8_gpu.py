@@ -61,6 +61,10 @@ CASES = [
     ([1000], 8, 8, 64, 32, 5, "avg", 256),
     ([3000, 2500], 16, 4, 128, 64, 5, "avg", 1024),
     ([64, 300, 65, 5, 1000], 8, 2, 128, 32, 5, "avg", 96),
+    # prefixes past the register-resident selection, one prompt kept whole:
+    # the sliced selection and the gather in one launch
+    ([40000, 3000, 400, 35000, 4100], 8, 2, 128, 16, 5, "avg", 512),
+    ([36000], 4, 4, 64, 16, 7, "max", 1500),            # D = 64
 ]
 
 

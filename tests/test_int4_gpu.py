@@ -29,6 +29,10 @@ CASES = [
     ([64, 300, 65, 5, 1000], 8, 2, 128, 32, 5, "avg", 96),  # ragged, kept whole, L < W
     ([700], 6, 2, 64, 24, 9, "max", 80),
     ([257], 4, 2, 128, 16, 5, "max", 256),              # L = B + 1
+    # prefixes past the register-resident selection, one prompt kept whole:
+    # the sliced selection and the gather in one launch
+    ([40000, 3000, 400, 35000, 4100], 8, 2, 128, 16, 5, "avg", 512),
+    ([36000], 4, 4, 64, 16, 7, "max", 1500),            # D = 64
 ]
 
 
