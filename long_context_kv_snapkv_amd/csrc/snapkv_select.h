@@ -264,22 +264,22 @@ __device__ __forceinline__ void select_head(const PathParams& p, SelectSmem& sm,
     if (!RESIDENT) load_keys<NS>(key, src, P, bt * NS);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      uint32_t c = 0;  // above | equal << 16 (a wave sums at most 256 of each)
+      // the wave's counts from ballots of its 64 lanes (scalar popcounts)
+      uint32_t above = 0, equal = 0;
       if (settled_s) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) c += key[s][e] >= tau ? 1u : 0u;
+        for (int e = 0; e < 4; ++e) above += (uint32_t)__popcll(__ballot(key[s][e] >= tau));
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          c += key[s][e] > tau ? 1u : 0u;
-          c += key[s][e] == tau ? 0x10000u : 0u;
+          above += (uint32_t)__popcll(__ballot(key[s][e] > tau));
+          equal += (uint32_t)__popcll(__ballot(key[s][e] == tau));
         }
       }
-      const uint32_t tot = wave_sum(c);
       const int g = (bt * NS + s) * kWaves + wave;  // segment index in the prefix
       if (lane == 0 && g < nseg) {
-        table[2 * g] = tot & 0xFFFFu;
-        table[2 * g + 1] = tot >> 16;
+        table[2 * g] = above;
+        table[2 * g + 1] = equal;
       }
     }
   }
@@ -449,18 +449,18 @@ __device__ __forceinline__ void select_count_slice(const PathParams& p, SliceSme
   uint32_t* table = p.sel_table + head * (size_t)p.table_stride * 2;
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    uint32_t c = 0;
+    // the wave's counts from ballots of its 64 lanes (scalar popcounts)
+    uint32_t above = 0, equal = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t u = key[g][e];
-      c += (t.settled ? u >= tau : u > tau) ? 1u : 0u;
-      c += (!t.settled && u == tau) ? 0x10000u : 0u;
+      above += (uint32_t)__popcll(__ballot(t.settled ? u >= tau : u > tau));
+      equal += (uint32_t)__popcll(__ballot(!t.settled && u == tau));
     }
-    const uint32_t tot = wave_total(wave_incl_scan(c));
     const int seg = (s0 + g * kSlab) / kSegment + wave;
     if (lane == 0 && seg < nseg) {
-      table[2 * seg] = tot & 0xFFFFu;
-      table[2 * seg + 1] = tot >> 16;
+      table[2 * seg] = above;
+      table[2 * seg + 1] = equal;
     }
   }
   if (sl == 0 && tid == 0) {
@@ -614,18 +614,18 @@ __device__ __forceinline__ void select_slices_one_launch(const PathParams& p, Sl
   uint32_t* table = p.sel_table + head * (size_t)p.table_stride * 2;
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    uint32_t c = 0;
+    // the wave's counts from ballots of its 64 lanes (scalar popcounts)
+    uint32_t above = 0, equal = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t u = key[g][e];
-      c += (t.settled ? u >= tau : u > tau) ? 1u : 0u;
-      c += (!t.settled && u == tau) ? 0x10000u : 0u;
+      above += (uint32_t)__popcll(__ballot(t.settled ? u >= tau : u > tau));
+      equal += (uint32_t)__popcll(__ballot(!t.settled && u == tau));
     }
-    const uint32_t tot = wave_total(wave_incl_scan(c));
     const int seg = (s0 + g * kSlab) / kSegment + wave;
     if (lane == 0 && seg < nseg) {
-      table[2 * seg] = tot & 0xFFFFu;
-      table[2 * seg + 1] = tot >> 16;
+      table[2 * seg] = above;
+      table[2 * seg + 1] = equal;
     }
   }
   if (sl == 0 && tid == 0) {
