@@ -69,8 +69,8 @@ def stage_bytes(w, seq_lens):
     d, q_bytes = w.head_dim, w.h_q * w.window * w.head_dim * 2
     gather = algorithmic_bytes(w, seq_lens)[1]
     out = {"snapkv_score_stats": 0, "snapkv_score_vote": 0, "snapkv_score_fused": 0,
-           "snapkv_score_fused_stream": 0, "snapkv_select": 0, "snapkv_gather": gather,
-           "snapkv_gather_select": gather}
+           "snapkv_score_fused_stream": 0, "snapkv_select": 0, "snapkv_select_slices": 0,
+           "snapkv_select_sliced": 0, "snapkv_gather": gather, "snapkv_gather_select": gather}
     for L in seq_lens:
         if L > w.budget:
             P = L - w.window
@@ -79,6 +79,8 @@ def stage_bytes(w, seq_lens):
             out["snapkv_score_fused_stream"] += q_bytes + w.h_kv * L * d * 2
             out["snapkv_score_vote"] += q_bytes + w.h_kv * P * d * 2
             out["snapkv_select"] += w.h_kv * (P * 4 + w.budget * 4)
+            out["snapkv_select_slices"] += w.h_kv * (P * 4 + w.budget * 4)
+            out["snapkv_select_sliced"] += w.h_kv * (P * 4 + w.budget * 4)
             out["snapkv_gather_select"] += w.h_kv * P * 4  # the pooled scores, read once
     return out
 
@@ -263,6 +265,7 @@ def measure(w, args, dev, stream, extras=False):
     fused = score_kernels != 2
     fused_name = "snapkv_score_fused" if score_kernels == 1 else "snapkv_score_fused_stream"
     sel_in_gather = skv.snapkv_gather_selects(w.h_q, hkv, d, lens0, w.window, B) == 1
+    select_kernels = skv.snapkv_select_kernels(w.h_q, hkv, d, lens0, w.window, B)
     stage_ms = {}
     for s_ in range(nst):
         if (fused and s_ == 1) or (sel_in_gather and s_ == 2):
@@ -273,6 +276,8 @@ def measure(w, args, dev, stream, extras=False):
             name = fused_name
         if sel_in_gather and s_ == 3:
             name = "snapkv_gather_select"
+        if s_ == 2:  # the selection stage's own kernel(s)
+            name = {2: "snapkv_select_slices", 3: "snapkv_select_sliced"}.get(select_kernels, name)
         stage_ms[name] = float(np.mean(vals))
 
     sbytes = stage_bytes(w, lens0)

@@ -191,6 +191,31 @@ int32_t snapkv_gather_selects(int32_t batch, int32_t num_q_heads,
                               int32_t budget, int32_t* fused);
 
 /*
+ * Which kernels snapkv_compress's selection stage (stage 2 of
+ * snapkv_compress_staged) launches on this shape, on the current device
+ * (the per-head selection of the pages' step 3: glossary page
+ * "SnapKV(スナップケーブイ)", section "SnapKVの仕組み"):
+ *   0  none: no prompt is compressed, or the selection runs inside the
+ *      gather (snapkv_gather_selects = 1);
+ *   1  snapkv_select, one workgroup per (prompt, KV head), every prefix
+ *      L - W at most 32768 positions;
+ *   2  snapkv_select_slices, the sliced selection of longer prefixes as one
+ *      launch whose 4096-position slice workgroups exchange the digit
+ *      histograms through flags (every slice workgroup of the call fits the
+ *      device one per compute unit);
+ *   3  the sliced selection as three kernels (snapkv_select_digit<2>,
+ *      snapkv_select_digit<3>, snapkv_select_count), otherwise, or while
+ *      SNAPKV_NO_FUSED_SELECT is set to a non-empty value other than "0".
+ * Results are identical in every case. Writes *kernels and returns
+ * SNAPKV_OK, or an error status under the shape rules of snapkv_compress
+ * (SNAPKV_ERR_INVALID_ARGUMENT also for a NULL `kernels` or budget <= window).
+ */
+int32_t snapkv_select_kernels(int32_t batch, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim,
+                              const int32_t* seq_lens, int32_t window,
+                              int32_t budget, int32_t* kernels);
+
+/*
  * snapkv_compress for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid allocation):
  * no workspace argument; the intermediates go to a fixed scratch area of
@@ -260,7 +285,8 @@ int32_t snapkv_compress_with_scores(int32_t batch, int32_t num_q_heads,
  * score kernel (snapkv_score_kernels = 1 or 3) stage 0 times that kernel
  * and stage 1 has no work; with the selection inside the gather
  * (snapkv_gather_selects = 1) stage 3 times snapkv_gather_select and stage 2
- * has no work.
+ * has no work; otherwise stage 2 spans the selection kernel(s) that
+ * snapkv_select_kernels names.
  * Errors as for snapkv_compress.
  */
 int32_t snapkv_compress_staged(int32_t batch, int32_t num_q_heads,

@@ -39,6 +39,7 @@ from .snapkv import (  # noqa: F401
     snapkv_last_error,
     snapkv_prefill_attention,
     snapkv_gather_selects,
+    snapkv_select_kernels,
     snapkv_score_kernels,
     snapkv_stage_name,
     snapkv_status_string,

@@ -632,6 +632,26 @@ int32_t snapkv_gather_selects(int32_t batch, int32_t num_q_heads, int32_t num_kv
   return SNAPKV_OK;
 }
 
+int32_t snapkv_select_kernels(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, const int32_t* seq_lens, int32_t window,
+                              int32_t budget, int32_t* kernels) {
+  if (kernels == nullptr) return fail(SNAPKV_ERR_INVALID_ARGUMENT, "kernels is NULL");
+  Plan pl;
+  const int32_t st = make_plan(batch, num_q_heads, num_kv_heads, head_dim, seq_lens, window, &pl);
+  if (st != SNAPKV_OK) return st;
+  if (budget <= window)
+    return fail(SNAPKV_ERR_INVALID_ARGUMENT, "budget must exceed window (it includes the window)");
+  snapkv::PathParams p{};
+  gather_plan(pl, budget, &p);
+  if (!any_scored(pl, budget, false) || use_select_in_gather(pl, &p))
+    *kernels = 0;
+  else if (p.sel_slices == 0)
+    *kernels = 1;
+  else
+    *kernels = use_one_launch_slices(pl, p) ? 2 : 3;
+  return SNAPKV_OK;
+}
+
 int32_t snapkv_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t head_dim, const int32_t* seq_lens, int32_t window,
                               size_t* bytes) {

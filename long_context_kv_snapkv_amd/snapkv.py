@@ -115,6 +115,8 @@ def load_library():
     lib.snapkv_score_kernels.restype = _i32
     lib.snapkv_gather_selects.argtypes = [_i32, _i32, _i32, _i32, _pi32, _i32, _i32, _pi32]
     lib.snapkv_gather_selects.restype = _i32
+    lib.snapkv_select_kernels.argtypes = [_i32, _i32, _i32, _i32, _pi32, _i32, _i32, _pi32]
+    lib.snapkv_select_kernels.restype = _i32
     lib.snapkv_stage_name.argtypes = [_i32]
     lib.snapkv_stage_name.restype = ctypes.c_char_p
     _lib = lib
@@ -635,6 +637,18 @@ def snapkv_gather_selects(num_q_heads: int, num_kv_heads: int, head_dim: int,
     arr, vals = _lens(seq_lens)
     n = ctypes.c_int32(0)
     _check(load_library().snapkv_gather_selects(len(vals), num_q_heads, num_kv_heads, head_dim,
+                                                arr, window, budget, ctypes.byref(n)))
+    return n.value
+
+def snapkv_select_kernels(num_q_heads: int, num_kv_heads: int, head_dim: int,
+                          seq_lens: Iterable[int], window: int, budget: int) -> int:
+    """Which kernels snapkv_compress's selection stage launches for this
+    shape on the current device: 0 none (inside the gather, or nothing to
+    select), 1 snapkv_select, 2 snapkv_select_slices (the sliced selection
+    as one launch), 3 the sliced selection as three kernels."""
+    arr, vals = _lens(seq_lens)
+    n = ctypes.c_int32(0)
+    _check(load_library().snapkv_select_kernels(len(vals), num_q_heads, num_kv_heads, head_dim,
                                                 arr, window, budget, ctypes.byref(n)))
     return n.value
 

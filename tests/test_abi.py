@@ -22,7 +22,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = skv.header_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     assert "snapkv_compress_staged" in names
     assert "snapkv_compress_with_scores" in names
     assert "snapkv_compress_static" in names
@@ -250,6 +250,27 @@ def test_decode_kernel_count(lib):
     assert skv.snapkv_decode_kernels(8, 8, 64, [2049], packed) == 2   # 17
     with pytest.raises(skv.SnapKVError):
         skv.snapkv_decode_kernels(32, 8, 96, [10], comp, 16)
+
+
+def test_select_kernels_host_logic(lib):
+    # no device here (no CU count): nothing runs inside the gather and the
+    # sliced selection takes its three kernels; a prefix of up to 32768
+    # positions is one workgroup per head, a longer one is sliced, and a
+    # call that compresses nothing selects nothing
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host logic without a device")
+    assert skv.snapkv_select_kernels(32, 8, 128, [16384], 32, 1024) == 1
+    assert skv.snapkv_select_kernels(32, 8, 128, [32768 + 32], 32, 1024) == 1
+    assert skv.snapkv_select_kernels(32, 8, 128, [32768 + 33], 32, 1024) == 3
+    assert skv.snapkv_select_kernels(64, 8, 128, [131072], 64, 1024) == 3
+    assert skv.snapkv_select_kernels(32, 8, 128, [1000, 500], 32, 1024) == 0
+    with pytest.raises(skv.SnapKVError):
+        skv.snapkv_select_kernels(32, 8, 128, [16384], 32, 32)  # budget <= window
+    n = ctypes.c_int32(0)
+    lens = (ctypes.c_int32 * 1)(16384)
+    assert (lib.snapkv_select_kernels(1, 32, 8, 128, lens, 32, 1024, None)
+            == skv.SNAPKV_ERR_INVALID_ARGUMENT)
 
 
 def test_score_kernels_host_logic(lib):

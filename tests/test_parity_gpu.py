@@ -295,6 +295,22 @@ def test_selection_inside_gather_by_shape():
     assert skv.snapkv_gather_selects(64, 8, 128, [131072], 64, 1024) == 0
     # too many gather items for the device at once
     assert skv.snapkv_gather_selects(32, 8, 128, [20000] * 8, 64, 4096) == 0
+    # the selection stage's own kernels: none (inside the gather), one
+    # workgroup per head, the sliced selection in one launch
+    assert skv.snapkv_select_kernels(w.h_q, w.h_kv, w.head_dim, [16384], w.window,
+                                     w.budget) == (0 if cus >= 256 else 1)
+    assert skv.snapkv_select_kernels(32, 8, 128, [20000] * 8, 64, 4096) == 1
+    assert skv.snapkv_select_kernels(64, 8, 128, [131072], 64, 1024) == (2 if cus >= 256 else 3)
+    assert skv.snapkv_select_kernels(8, 2, 128, [40000], 16, 2048) == (2 if cus >= 20 else 3)
+
+
+@needs_gpu
+def test_select_kernels_switch_off(monkeypatch):
+    # with the fused forms switched off the sliced selection takes its three
+    # kernels (bit-identity of the two forms: test_fused_paths_identical_on_edge_shapes)
+    monkeypatch.setenv("SNAPKV_NO_FUSED_SELECT", "1")
+    assert skv.snapkv_select_kernels(64, 8, 128, [131072], 64, 1024) == 3
+    assert skv.snapkv_select_kernels(32, 8, 128, [16384], 32, 1024) == 1
 
 
 @needs_gpu
