@@ -37,6 +37,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+# VALU issue floor of the score passes: every logit takes an fma, an exp2
+# and an add in each pass, and a SIMD issues a wave64 fp32 instruction every
+# 4 cycles (16 lanes), an exp2 every 16 (a quarter of the rate), so 24
+# cycles per 64 logit updates; 256 CUs x 4 SIMDs at 2.4 GHz
+VALU_LOGIT_PEAK = 256 * 4 * 2.4e9 * 64 / 24  # logit updates per second
 METRIC = "prompt tokens compressed/sec per layer; achieved HBM GB/s vs MI355X peak"
 CACHE_BYTES = 256 << 20       # Infinity Cache
 HEADLINE = "llama3_70b_128k_x80"
@@ -83,6 +88,13 @@ def stage_bytes(w, seq_lens):
             out["snapkv_select_sliced"] += w.h_kv * (P * 4 + w.budget * 4)
             out["snapkv_gather_select"] += w.h_kv * P * 4  # the pooled scores, read once
     return out
+
+
+def score_logit_updates(w, seq_lens):
+    """Logit updates of the two score passes: every window row against all
+    L keys (statistics) and against the P = L - W prefix keys (vote)."""
+    rows = w.h_q * w.window
+    return sum(rows * (2 * L - w.window) for L in seq_lens if L > w.budget)
 
 
 def score_flops(w, seq_lens):
@@ -321,6 +333,13 @@ def measure(w, args, dev, stream, extras=False):
                                                        BF16_PEAK_TFLOPS, 4),
                             "issued_2pass": round(2 * flops / (score_ms * 1e-3) / 1e12 /
                                                   BF16_PEAK_TFLOPS, 4)},
+        # the score kernels against their VALU issue floor (fma, exp2 at a
+        # quarter rate, add per logit and pass), the bound they meet first
+        "valu_floor_score": {"logit_updates": score_logit_updates(w, lens0),
+                             "floor_us": round(score_logit_updates(w, lens0) / VALU_LOGIT_PEAK
+                                               * 1e6, 1),
+                             "frac": round(score_logit_updates(w, lens0) / VALU_LOGIT_PEAK /
+                                           (score_ms * 1e-3), 4)},
         "score_kernels": score_kernels,
         "score_kernel": fused_name if fused else "snapkv_score_stats + snapkv_score_vote",
         "selection_in_gather": sel_in_gather,
