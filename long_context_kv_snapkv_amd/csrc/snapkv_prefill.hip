@@ -160,18 +160,22 @@ __global__ void __launch_bounds__(kPrefillThreads, 2) snapkv_prefill(const Prefi
           s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[st], s, 0, 0, 0);
       }
       // s[v]: logit of row my_row with key bk0 + acc_row(v, lane)
-      float x[16];
+      // masked keys get -inf logits; the scale enters each term's exponent
+      // through an fma, and the block maximum is scaled once (scale > 0 and
+      // rounding is monotonic, so that is the maximum of the scaled logits)
+      f32x16 x = s;
       const bool edge = bk0 + 31 > wr0 || bk0 + 31 >= L;  // the diagonal or the prompt's end
+      if (edge) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        x[v] = s[v] * scale;
-        const int key = bk0 + acc_row(v, lane);
-        if (edge && (key > my_row || key >= L)) x[v] = -kInf;
+        for (int v = 0; v < 16; ++v) {
+          const int key = bk0 + acc_row(v, lane);
+          if (key > my_row || key >= L) x[v] = -kInf;
+        }
       }
       float bm = x[0];
 #pragma unroll
       for (int v = 1; v < 16; ++v) bm = fmaxf(bm, x[v]);
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      bm = fmaxf(bm, __shfl_xor(bm, 32)) * scale;
       // the row's reference moves only when the block's maximum exceeds it
       // by more than 8 (log2 units): the terms 2^(x - m) then stay below 2^8,
       // and the output rows are rescaled rarely (m + log2(sum) is the row's
@@ -182,7 +186,7 @@ __global__ void __launch_bounds__(kPrefillThreads, 2) snapkv_prefill(const Prefi
       float ps = 0.f;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        pv[v] = exp2_fast(x[v] - mn);
+        pv[v] = exp2_fast(fmaf(x[v], scale, -mn));
         ps += pv[v];
       }
       lsum = lsum * alpha + ps;
