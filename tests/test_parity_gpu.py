@@ -62,6 +62,25 @@ def test_llama3_70b_128k_layer0():
     full_check(x, w.window, w.kernel, w.pool, w.budget)
 
 
+@needs_gpu
+def test_longest_context_of_the_pages():
+    # One 380,000-token prompt, the longest context the paper page reports on
+    # a single 80 GB device (paper page "SnapKV: LLM Knows What You are
+    # Looking for Before Generation", sections "핵심 기여도" and "주요 결과"),
+    # on a Llama-3-8B-shaped layer. 47 chunks of 8192 keys per head are more
+    # items than CUs (two score kernels), and the 379,968-position prefix
+    # takes 93 selection slices per head (the three-kernel sliced form); the
+    # last chunk, tile and slice are ragged.
+    lens, hq, hkv, d, window, kernel, pool, budget = [380000], 32, 8, 128, 32, 7, "max", 4096
+    print(f"[parity] longest context lens={lens}", flush=True)
+    if torch.cuda.get_device_properties(0).multi_processor_count < 376:
+        assert skv.snapkv_score_kernels(hq, hkv, d, lens, window, kernel) == 2
+    if torch.cuda.get_device_properties(0).multi_processor_count < 744:
+        assert skv.snapkv_select_kernels(hq, hkv, d, lens, window, budget) == 3
+    x = make_custom(lens, hq, hkv, d, window, seed=5, planting="spans64")
+    full_check(x, window, kernel, pool, budget)
+
+
 EDGE = [
     # lens, h_q, h_kv, d, window, kernel, pool, budget
     ([256], 4, 2, 128, 16, 5, "avg", 256),        # L == B: kept whole
