@@ -10,7 +10,7 @@
 //
 // Work item: 128 query rows of one (prompt, query head), four waves of 32
 // rows. Keys and values go through LDS 64 at a time (K row-major, V
-// transposed); the item visits the keys up to its last row. Per 32-key block
+// row-major); the item visits the keys up to its last row. Per 32-key block
 // a wave computes S^T = K . Q^T with bf16 MFMAs (v_mfma_f32_32x32x16_bf16),
 // so a lane holds 16 keys of one row: the running maximum and sum of that
 // row are in-lane (plus the other lane half). P = 2^(s - m) goes, rounded to
@@ -18,7 +18,10 @@
 // are taken as the k-slots in the order the S^T layout holds them, and the V
 // operand is read from the transposed tile in the same key order. The
 // output accumulates in float32 and is rescaled only when some row's maximum
-// moved. At the end each row is divided by its sum and written as bf16; the
+// moved. V stays row-major in LDS, as K does; the P . V operand (four keys
+// of one column per lane and step half) comes from the transposing LDS read
+// of gfx950 (ds_read_b64_tr_b16). At the end each row is divided by its sum
+// and written as bf16; the
 // rows of each prompt's observation window also report their natural-log
 // normaliser and a copy of their query, in the layouts snapkv_compress_from_lse
 // reads.
@@ -32,21 +35,27 @@
 namespace snapkv {
 namespace {
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// ds_read_b64_tr_b16 at an 8-byte aligned LDS address (a generic pointer
+// into a __shared__ array)
+__device__ __forceinline__ uint2 read_tr16(const unsigned char* a) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(a)));
+}
+
 constexpr int BM = kPrefillRows;
 constexpr int BN = kPrefillKeys;
 
-template <int N>
-struct VROW_EVEN {
-  static constexpr bool ok = N % 2 == 0;
-};
-
 template <int D>
 struct alignas(16) PrefillSmem {
-  static constexpr int ROWB = D * 2 + 16;  // padded row (bytes): MFMA fragment reads hit distinct banks
-  static constexpr int VROW = BN + 4;      // transposed V row (bf16 elements), padded likewise
-  unsigned char qo[BM * ROWB];             // the item's query rows, later its output rows
-  unsigned char kt[BN * ROWB];             // K tile [key][d]
-  uint16_t vt[D * VROW];                   // V tile transposed [d][key]
+  static constexpr int ROWB = D * 2 + 16;   // padded row (bytes): MFMA fragment reads hit distinct banks
+  // V row (bytes): a transposing read takes 8 bytes from each of 4
+  // consecutive rows; a stride of 8 banks puts them on distinct banks
+  static constexpr int VROWB = D * 2 + 32;
+  unsigned char qo[BM * ROWB];              // the item's query rows, later its output rows
+  unsigned char kt[BN * ROWB];              // K tile [key][d]
+  unsigned char vt[BN * VROWB];             // V tile [key][d]
 };
 
 template <int D>
@@ -95,12 +104,10 @@ __global__ void __launch_bounds__(kPrefillThreads, 2) snapkv_prefill(const Prefi
 
   const int kend = min(r0 + BM, L);  // keys up to the item's last row
   const int ntiles = (kend + BN - 1) / BN;
-  // a thread moves K pieces of single keys and V pieces of key pairs: the
-  // pair's two values of each column go to the transposed tile as one word
+  // a thread moves the same 16-byte pieces of K and of V
   constexpr int LOADS = BN * PIECES / kPrefillThreads;
-  constexpr int VPAIRS = LOADS / 2;
-  static_assert(LOADS % 2 == 0 && VROW_EVEN<S::VROW>::ok, "pairs of keys per transposed word");
-  u32x4 kx[LOADS], va[VPAIRS], vb[VPAIRS];
+  static_assert(LOADS >= 1 && BN * PIECES % kPrefillThreads == 0, "tile split");
+  u32x4 kx[LOADS], vx[LOADS];
   // tile k0's loads into the registers (rows past the prompt: a valid row,
   // masked in the logits)
   auto load_tile = [&](int k0) {
@@ -109,13 +116,7 @@ __global__ void __launch_bounds__(kPrefillThreads, 2) snapkv_prefill(const Prefi
       const int pc = tid + u * kPrefillThreads;
       const int j = min(k0 + pc / PIECES, L - 1);
       kx[u] = *reinterpret_cast<const u32x4*>(kbase + (size_t)j * kstride + (pc % PIECES) * 8);
-    }
-#pragma unroll
-    for (int u = 0; u < VPAIRS; ++u) {
-      const int pc = tid + u * kPrefillThreads;  // key pair pc / PIECES
-      const int j0 = min(k0 + 2 * (pc / PIECES), L - 1), j1 = min(k0 + 2 * (pc / PIECES) + 1, L - 1);
-      va[u] = *reinterpret_cast<const u32x4*>(vbase + (size_t)j0 * kstride + (pc % PIECES) * 8);
-      vb[u] = *reinterpret_cast<const u32x4*>(vbase + (size_t)j1 * kstride + (pc % PIECES) * 8);
+      vx[u] = *reinterpret_cast<const u32x4*>(vbase + (size_t)j * kstride + (pc % PIECES) * 8);
     }
   };
   load_tile(0);
@@ -126,20 +127,7 @@ __global__ void __launch_bounds__(kPrefillThreads, 2) snapkv_prefill(const Prefi
     for (int u = 0; u < LOADS; ++u) {
       const int pc = tid + u * kPrefillThreads;
       *reinterpret_cast<u32x4*>(sm.kt + (pc / PIECES) * ROWB + (pc % PIECES) * 16) = kx[u];
-    }
-#pragma unroll
-    for (int u = 0; u < VPAIRS; ++u) {
-      const int pc = tid + u * kPrefillThreads;
-      const int key = 2 * (pc / PIECES), col = pc % PIECES;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // columns 8 col + 2e and + 2e + 1: (key, key + 1) as one 32-bit word each
-        const uint32_t x = va[u][e], y = vb[u][e];
-        *reinterpret_cast<uint32_t*>(&sm.vt[(col * 8 + 2 * e) * S::VROW + key]) =
-            (x & 0xFFFFu) | (y << 16);
-        *reinterpret_cast<uint32_t*>(&sm.vt[(col * 8 + 2 * e + 1) * S::VROW + key]) =
-            (x >> 16) | (y & 0xFFFF0000u);
-      }
+      *reinterpret_cast<u32x4*>(sm.vt + (pc / PIECES) * S::VROWB + (pc % PIECES) * 16) = vx[u];
     }
     // the next tile's loads fly while this one is computed
     if (it + 1 < ntiles) load_tile(k0 + BN);
@@ -206,17 +194,22 @@ __global__ void __launch_bounds__(kPrefillThreads, 2) snapkv_prefill(const Prefi
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 8; ++i) pa[t][i] = (__bf16)pv[8 * t + i];
-      // the V operand in the same key order: step t, lane half hh holds keys
-      // 16t + 4hh + {0..3} and 16t + 8 + 4hh + {0..3} of column 32ds + lane%32
+      // The V operand in the same key order: step t, lane half hh holds keys
+      // 16t + 4hh + {0..3} and 16t + 8 + 4hh + {0..3} of column 32ds + lane%32.
+      // Within each 16-lane group the transposing read hands lane j, slot c,
+      // bytes 2j % 8 .. +1 of the 8 that lane 4c + j/4 points at; so lane
+      // i = 4c + q of a group points at key (base + c), columns n0 + 4q .. +3,
+      // and lane j receives column n0 + j of keys base .. base + 3.
+      const int gi = lane & 15;
+      const unsigned char* vgrp = sm.vt + (32 * kb + 4 * (lane >> 5) + (gi >> 2)) * S::VROWB +
+                                  (16 * ((lane >> 4) & 1) + 4 * (gi & 3)) * 2;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
         for (int ds = 0; ds < NDS; ++ds) {
-          const uint16_t* vrow =
-              sm.vt + (32 * ds + (lane & 31)) * S::VROW + 32 * kb + 16 * t + 4 * (lane >> 5);
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-          const bf16x8 vb = as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
+          const unsigned char* a = vgrp + 16 * t * S::VROWB + 32 * ds * 2;
+          const uint2 l2 = read_tr16(a), h2 = read_tr16(a + 8 * S::VROWB);
+          const bf16x8 vb = as_bf16x8(u32x4{l2.x, l2.y, h2.x, h2.y});
           o[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[t], vb, o[ds], 0, 0, 0);
         }
       }
