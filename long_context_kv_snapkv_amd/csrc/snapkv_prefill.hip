@@ -51,8 +51,10 @@ template <int D>
 struct alignas(16) PrefillSmem {
   static constexpr int ROWB = D * 2 + 16;   // padded row (bytes): MFMA fragment reads hit distinct banks
   // V row (bytes): a transposing read takes 8 bytes from each of 4
-  // consecutive rows; a stride of 8 banks puts them on distinct banks
-  static constexpr int VROWB = D * 2 + 32;
+  // consecutive rows per 16-lane group, and the two groups of a lane half
+  // read columns 16 apart; a row stride of 16 banks (mod 64) keeps all 32
+  // lanes on distinct banks
+  static constexpr int VROWB = D * 2 + 64;
   unsigned char qo[BM * ROWB];              // the item's query rows, later its output rows
   unsigned char kt[BN * ROWB];              // K tile [key][d]
   unsigned char vt[BN * VROWB];             // V tile [key][d]
