@@ -265,8 +265,9 @@ __global__ void __launch_bounds__(kDecodeThreads) snapkv_decode_partial(const De
 #pragma unroll
     for (int r = 0; r < 4; ++r) x[r] = t0 + 4 * mk + r < r1 ? sc[r] * p.scale_log2 : -kInf;
     float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float2 t16 = rows16(tmax);
+    const float2 t32 = halves32(fmaxf(t16.x, t16.y));
+    tmax = fmaxf(t32.x, t32.y);
     const float mnew = fmaxf(m_run, tmax);
     float cs = 1.f, pr[4] = {0.f, 0.f, 0.f, 0.f};
     if (mnew != -kInf) {  // some row of the wave seen so far
@@ -330,8 +331,9 @@ __global__ void __launch_bounds__(kDecodeThreads) snapkv_decode_partial(const De
   // lanes, and each output element as a fixed-order sum over the groups
   // the wave's sum of weights per query (fixed-order butterfly over mk); its
   // lane groups share the wave's max, and the sum is carried by group 0
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  const float2 l16 = rows16(l_run);
+  const float2 l32 = halves32(l16.x + l16.y);
+  l_run = l32.x + l32.y;
   if (mk == 0 && mrow < GM) {
 #pragma unroll
     for (int j = 0; j < RPI; ++j) {

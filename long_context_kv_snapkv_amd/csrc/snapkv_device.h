@@ -36,6 +36,23 @@ __device__ __forceinline__ int acc_row(int v, int lane) {
   return ((v >> 2) << 3) + ((lane >> 5) << 2) + (v & 3);
 }
 
+// The values x of lanes l & ~32 and l | 32 (the wave's two halves), in every
+// lane, from one v_permlane32_swap: a VALU exchange, in place of an LDS
+// crossbar round trip. A commutative combine of .x and .y gives every lane
+// the same bits as combining its own x with lane l ^ 32's.
+__device__ __forceinline__ float2 halves32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                   false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// Likewise lanes l & ~16 and l | 16 (the even and odd 16-lane rows of each
+// pair), from one v_permlane16_swap.
+__device__ __forceinline__ float2 rows16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                   false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Merge two (reference m, sum of 2^(x - m)) pairs (the reference need not be
 // the maximum; the result takes the larger one).
 __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {

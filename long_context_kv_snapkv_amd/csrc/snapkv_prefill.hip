@@ -165,7 +165,8 @@ __global__ void __launch_bounds__(kPrefillThreads, 2) snapkv_prefill(const Prefi
       float bm = x[0];
 #pragma unroll
       for (int v = 1; v < 16; ++v) bm = fmaxf(bm, x[v]);
-      bm = fmaxf(bm, __shfl_xor(bm, 32)) * scale;
+      const float2 bh = halves32(bm);
+      bm = fmaxf(bh.x, bh.y) * scale;
       // the row's reference moves only when the block's maximum exceeds it
       // by more than 8 (log2 units): the terms 2^(x - m) then stay below 2^8,
       // and the output rows are rescaled rarely (m + log2(sum) is the row's
@@ -219,7 +220,8 @@ __global__ void __launch_bounds__(kPrefillThreads, 2) snapkv_prefill(const Prefi
   }
 
   // the row's sum (both lane halves), its normaliser, and the output rows
-  const float ltot = lsum + __shfl_xor(lsum, 32);
+  const float2 lh = halves32(lsum);
+  const float ltot = lh.x + lh.y;
   const float inv = 1.f / ltot;
   __syncthreads();  // every wave is done with the query rows in LDS
 #pragma unroll

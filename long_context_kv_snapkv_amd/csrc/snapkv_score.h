@@ -358,13 +358,14 @@ __device__ __forceinline__ void score_stats_body(const PathParams& p, unsigned c
 #pragma unroll
   for (int t = 0; t < RTW; ++t) update_full(pacc[t], t);
 
-  // lanes l and l^32 hold the same row over different keys
+  // lanes l and l^32 hold the same row over different keys: the lower
+  // half's pair merged with the upper half's
 #pragma unroll
   for (int t = 0; t < RTW; ++t) {
-    const float mo = __shfl_xor(mrun[t], 32);
-    const float so = __shfl_xor(srun[t], 32);
-    lse_merge(mrun[t], srun[t], mo, so);
-    if (lane < 32 && t < role.my_nrt) wstats[wave][t * 32 + lane] = make_float2(mrun[t], srun[t]);
+    const float2 mh = halves32(mrun[t]), sh = halves32(srun[t]);
+    float mm = mh.x, ss = sh.x;
+    lse_merge(mm, ss, mh.y, sh.y);
+    if (lane < 32 && t < role.my_nrt) wstats[wave][t * 32 + lane] = make_float2(mm, ss);
   }
   __syncthreads();
   float2* dst = p.part + ((size_t)(b * p.hkv + h) * p.nchunk + c) * p.rows_pad;
