@@ -52,7 +52,7 @@ __device__ __forceinline__ float bf16_elem(const u32x4& w, int e) {
 
 // Sum over aligned groups of W = 8, 16 or 32 lanes, left in every lane of
 // the group: DPP exchanges within quads (lane ^ 1, lane ^ 2), then across
-// the halves of 8 (half mirror) and of 16 (mirror), then one lane shuffle
+// the halves of 8 (half mirror) and of 16 (mirror), then a permlane swap
 // across two rows. Each step adds a value and its partner's, so all lanes of
 // a group hold the same bits.
 template <int W>
@@ -62,12 +62,15 @@ __device__ __forceinline__ float group_sum(float x) {
   x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xf, 0xf, false));
   if (W >= 16)
     x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xf, 0xf, false));
-  if (W == 32) x += __shfl_xor(x, 16);
+  if (W == 32) {
+    const float2 r = rows16(x);
+    x = r.x + r.y;
+  }
   return x;
 }
 
 // Maximum over aligned groups of W = 16 or 32 lanes, in every lane (DPP
-// within rows of 16, one lane shuffle across two rows).
+// within rows of 16, a permlane swap across two rows).
 template <int W>
 __device__ __forceinline__ float group_max(float x) {
   x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf,
@@ -78,7 +81,10 @@ __device__ __forceinline__ float group_max(float x) {
                                                           false)));
   x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xf, 0xf,
                                                           false)));
-  if (W == 32) x = fmaxf(x, __shfl_xor(x, 16));
+  if (W == 32) {
+    const float2 r = rows16(x);
+    x = fmaxf(r.x, r.y);
+  }
   return x;
 }
 
